@@ -1,0 +1,175 @@
+// C ABI of the LAGA per-rank attention path: argument checks, workspace
+// carving and kernel sequencing.  Declarations and contracts: include/laga.h.
+#include "../../include/laga.h"
+
+#include "launch.hpp"
+
+namespace {
+
+using laga::Shape;
+
+constexpr int64_t kMaxTokens = int64_t(1) << 22;
+
+bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Fills `s` from `d`; returns LAGA_OK or the reason the dims are rejected.
+laga_status check_dims(const laga_dims* d, Shape* s) {
+  if (d == nullptr) return LAGA_ERR_INVALID;
+  if (d->B < 1 || d->S < 1 || d->n_h < 1 || d->sp_size < 1) return LAGA_ERR_INVALID;
+  if (d->n_h % d->sp_size != 0 || d->sp_rank < 0 || d->sp_rank >= d->sp_size) return LAGA_ERR_INVALID;
+  if (!(d->eps > 0.f) || !(d->eps < 1.f)) return LAGA_ERR_INVALID;
+  if (d->dtype != LAGA_F32 && d->dtype != LAGA_BF16) return LAGA_ERR_INVALID;
+  if (d->precision != LAGA_OPERANDS_FP16 && d->precision != LAGA_OPERANDS_SPLIT) return LAGA_ERR_INVALID;
+  if (d->B > kMaxTokens || d->S > kMaxTokens || d->B * d->S > kMaxTokens) return LAGA_ERR_UNSUPPORTED;
+  const bool v3 = d->d_kv == 512 && d->d_nope == 128 && d->d_rope == 64 && d->d_v == 128;
+  const bool tiny = d->d_kv == 64 && d->d_nope == 32 && d->d_rope == 16 && d->d_v == 32;
+  if (!((d->dtype == LAGA_BF16 && v3) || (d->dtype == LAGA_F32 && tiny))) return LAGA_ERR_UNSUPPORTED;
+  s->B = d->B;
+  s->S = d->S;
+  s->T = d->B * d->S;
+  s->n_h = d->n_h;
+  s->h = d->n_h / d->sp_size;
+  s->head_lo = d->sp_rank * s->h;
+  s->d_kv = d->d_kv;
+  s->d_nope = d->d_nope;
+  s->d_rope = d->d_rope;
+  s->d_v = d->d_v;
+  s->eps = d->eps;
+  s->bf16 = d->dtype == LAGA_BF16;
+  s->split = s->bf16 && d->precision == LAGA_OPERANDS_SPLIT;
+  if (static_cast<int64_t>(s->h) * ((s->S + 127) / 128) * s->B > (int64_t(1) << 31)) return LAGA_ERR_UNSUPPORTED;
+  return LAGA_OK;
+}
+
+laga_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return LAGA_OK;
+  if (e == hipErrorNotSupported) return LAGA_ERR_UNSUPPORTED;
+  return LAGA_ERR_HIP;
+}
+
+// Backward workspace regions, each 256-byte aligned, in float32 elements.
+struct BwdLayout {
+  size_t delta, dkv, dkpe, dL, dw, dg, total;  // byte offsets, total bytes
+};
+
+size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
+
+BwdLayout bwd_layout(const Shape& s) {
+  BwdLayout L;
+  size_t off = 0;
+  auto take = [&](size_t floats) {
+    const size_t at = off;
+    off += round256(floats * sizeof(float));
+    return at;
+  };
+  L.delta = take(static_cast<size_t>(s.B) * s.h * s.S);
+  L.dkv = take(static_cast<size_t>(s.T) * s.h * s.C());
+  L.dkpe = take(static_cast<size_t>(s.h) * s.T * s.d_rope);
+  L.dL = take(static_cast<size_t>(s.T) * s.d_kv);
+  L.dw = take(laga::fold_dw_partial_floats(s));
+  L.dg = take(laga::norm_bwd_partial_floats(s));
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t laga_kv_elem_bytes(const laga_dims* dims) {
+  Shape s;
+  if (check_dims(dims, &s) != LAGA_OK) return 0;
+  return (s.bf16 && !s.split) ? 2 : 4;
+}
+
+laga_status laga_latent_norm(const laga_dims* dims, const void* latent, const void* gamma,
+                             float* latent_n, float* rstd, void* stream) {
+  Shape s;
+  laga_status st = check_dims(dims, &s);
+  if (st != LAGA_OK) return st;
+  if (!latent || !gamma || !latent_n || !rstd) return LAGA_ERR_INVALID;
+  if (!aligned16(latent) || !aligned16(gamma) || !aligned16(latent_n) || !aligned16(rstd)) return LAGA_ERR_ALIGN;
+  return from_hip(laga::launch_norm_fwd(s, latent, gamma, latent_n, rstd, static_cast<hipStream_t>(stream)));
+}
+
+laga_status laga_kv_up(const laga_dims* dims, const float* latent_n, const void* w_kv_b, void* k_nope,
+                       void* v, void* stream) {
+  Shape s;
+  laga_status st = check_dims(dims, &s);
+  if (st != LAGA_OK) return st;
+  if (!latent_n || !w_kv_b || !k_nope || !v) return LAGA_ERR_INVALID;
+  if (!aligned16(latent_n) || !aligned16(w_kv_b) || !aligned16(k_nope) || !aligned16(v)) return LAGA_ERR_ALIGN;
+  return from_hip(laga::launch_kv_up(s, latent_n, w_kv_b, k_nope, v, static_cast<hipStream_t>(stream)));
+}
+
+laga_status laga_attn_fwd(const laga_dims* dims, const void* q, const void* k_nope, const void* k_pe,
+                          const void* v, float* o, float* lse, void* stream) {
+  Shape s;
+  laga_status st = check_dims(dims, &s);
+  if (st != LAGA_OK) return st;
+  if (!q || !k_nope || !k_pe || !v || !o || !lse) return LAGA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k_nope) || !aligned16(k_pe) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return LAGA_ERR_ALIGN;
+  return from_hip(laga::launch_attn_fwd(s, q, k_nope, k_pe, v, o, lse, static_cast<hipStream_t>(stream)));
+}
+
+size_t laga_attn_bwd_workspace_bytes(const laga_dims* dims) {
+  Shape s;
+  if (check_dims(dims, &s) != LAGA_OK) return 0;
+  return bwd_layout(s).total;
+}
+
+laga_status laga_attn_bwd(const laga_dims* dims, const void* q, const void* latent, const void* gamma,
+                          const float* rstd, const void* k_nope, const void* k_pe, const void* v,
+                          const void* w_kv_b, const float* o, const float* lse, const void* d_o,
+                          float* dq, float* d_latent, float* d_k_pe, float* d_w_kv_b, float* d_gamma,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  Shape s;
+  laga_status st = check_dims(dims, &s);
+  if (st != LAGA_OK) return st;
+  if (s.bf16 && !s.split) return LAGA_ERR_UNSUPPORTED;  // the backward needs fp32-class K/V
+  const void* ptrs[] = {q, latent, gamma, rstd, k_nope, k_pe, v, w_kv_b, o, lse, d_o,
+                        dq, d_latent, d_k_pe, d_w_kv_b, d_gamma};
+  for (const void* p : ptrs)
+    if (p == nullptr) return LAGA_ERR_INVALID;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return LAGA_ERR_ALIGN;
+  const BwdLayout L = bwd_layout(s);
+  if (workspace == nullptr || workspace_bytes < L.total) return LAGA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LAGA_ERR_ALIGN;
+  char* ws = static_cast<char*>(workspace);
+  float* delta = reinterpret_cast<float*>(ws + L.delta);
+  float* dkv = reinterpret_cast<float*>(ws + L.dkv);
+  float* dkpe = reinterpret_cast<float*>(ws + L.dkpe);
+  float* dL = reinterpret_cast<float*>(ws + L.dL);
+  float* dw = reinterpret_cast<float*>(ws + L.dw);
+  float* dg = reinterpret_cast<float*>(ws + L.dg);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+
+  hipError_t e;
+  if ((e = laga::launch_bwd_dot(s, o, d_o, delta, hs)) != hipSuccess) return from_hip(e);
+  if ((e = laga::launch_attn_bwd_dkdv(s, q, k_nope, k_pe, v, lse, delta, d_o, dkv, dkpe, hs)) != hipSuccess)
+    return from_hip(e);
+  if ((e = laga::launch_attn_bwd_dq(s, q, k_nope, k_pe, v, lse, delta, d_o, dq, hs)) != hipSuccess)
+    return from_hip(e);
+  if ((e = laga::launch_head_sum(s, dkpe, d_k_pe, hs)) != hipSuccess) return from_hip(e);
+  if ((e = laga::launch_fold_dl(s, dkv, w_kv_b, dL, hs)) != hipSuccess) return from_hip(e);
+  if ((e = laga::launch_fold_dw(s, dkv, latent, gamma, rstd, dw, d_w_kv_b, hs)) != hipSuccess) return from_hip(e);
+  if ((e = laga::launch_norm_bwd(s, dL, latent, gamma, rstd, d_latent, dg, d_gamma, hs)) != hipSuccess)
+    return from_hip(e);
+  return LAGA_OK;
+}
+
+const char* laga_status_string(laga_status status) {
+  switch (status) {
+    case LAGA_OK: return "LAGA_OK";
+    case LAGA_ERR_INVALID: return "LAGA_ERR_INVALID: invalid argument";
+    case LAGA_ERR_UNSUPPORTED: return "LAGA_ERR_UNSUPPORTED: dims/dtype/precision not supported";
+    case LAGA_ERR_ALIGN: return "LAGA_ERR_ALIGN: pointer not 16-byte aligned";
+    case LAGA_ERR_HIP: return "LAGA_ERR_HIP: HIP launch error";
+    case LAGA_ERR_WORKSPACE: return "LAGA_ERR_WORKSPACE: workspace missing or too small";
+  }
+  return "unknown laga_status";
+}
+
+}  // extern "C"

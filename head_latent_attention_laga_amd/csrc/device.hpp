@@ -1,0 +1,129 @@
+// Device-side building blocks shared by the LAGA kernels (gfx950 / CDNA4).
+//
+// Matrix-core atoms: every contraction in this library is expressed with the
+// 32x32 MFMA family.  For an atom with KPL elements per lane, lane l of a
+// 64-wide wavefront supplies
+//   A operand: row (l % 32), k = (l / 32) * KPL + [0, KPL)
+//   B operand: col (l % 32), k = (l / 32) * KPL + [0, KPL)
+// and receives 16 fp32 results at
+//   C[r]: row 8 * (r / 4) + 4 * (l / 32) + (r % 4), col (l % 32),  r in [0, 16).
+// One instruction covers K = 2 * KPL.  Because A and B use the same k
+// assignment, any consistent permutation of k between the two operands gives
+// the same dot products; the attention kernels use that to feed accumulator
+// registers straight back in as the next contraction's operand.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace laga {
+
+typedef _Float16 half_t;
+typedef uint16_t bf16_t;  // raw bfloat16 bit pattern
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bfx8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- conversions
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even float -> bfloat16 bits (inputs are finite).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+// Element tags for templated code: what a value is stored as in memory.
+struct Bf16In {};  // raw bfloat16 bits
+struct F32In {};   // float32
+
+template <class Tag> struct InType;
+template <> struct InType<Bf16In> { typedef bf16_t type; static constexpr int bytes = 2; };
+template <> struct InType<F32In> { typedef float type; static constexpr int bytes = 4; };
+
+__device__ __forceinline__ float to_f32(bf16_t v) { return bf16_to_f32(v); }
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(half_t v) { return static_cast<float>(v); }
+
+// ------------------------------------------------------------ MFMA element types
+// Matrix-core operand types: fp16, bf16 (stored as raw bits in LDS) and fp32.
+struct MmaF16 {
+  typedef half_t elem;
+  typedef half8 frag;
+  static constexpr int KPL = 8;
+  static constexpr int K = 16;
+  __device__ static __forceinline__ elem from_f32(float f) { return static_cast<half_t>(f); }
+  __device__ static __forceinline__ float to_f32(elem e) { return static_cast<float>(e); }
+  __device__ static __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+struct MmaBf16 {
+  typedef bf16_t elem;
+  typedef u16x8 frag;
+  static constexpr int KPL = 8;
+  static constexpr int K = 16;
+  __device__ static __forceinline__ elem from_f32(float f) { return f32_to_bf16(f); }
+  __device__ static __forceinline__ float to_f32(elem e) { return bf16_to_f32(e); }
+  __device__ static __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bfx8, a),
+                                                   __builtin_bit_cast(bfx8, b), c, 0, 0, 0);
+  }
+};
+
+struct MmaF32 {
+  typedef float elem;
+  typedef float frag;
+  static constexpr int KPL = 1;
+  static constexpr int K = 2;
+  __device__ static __forceinline__ elem from_f32(float f) { return f; }
+  __device__ static __forceinline__ float to_f32(elem e) { return e; }
+  __device__ static __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// Split a float into NS terms of the MMA element type: x ~= sum_s part[s].
+template <class M, int NS>
+__device__ __forceinline__ void split_to(float x, typename M::elem* part) {
+  float r = x;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    part[s] = M::from_f32(r);
+    r -= M::to_f32(part[s]);
+  }
+}
+
+// Load a KPL-element fragment from LDS (contiguous, aligned to KPL elements).
+template <class M>
+__device__ __forceinline__ typename M::frag lds_frag(const typename M::elem* p) {
+  return *reinterpret_cast<const typename M::frag*>(p);
+}
+
+// ------------------------------------------------------------ wave reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Exchange with the lane 32 positions away (the other half of the wavefront).
+__device__ __forceinline__ float swap_halves(float v) { return __shfl_xor(v, 32, kWave); }
+
+// Position of key `k` (0..BN-1) inside an LDS row that a 32x32 atom reads as a
+// K-operand fed from accumulator registers: bits 2 and 3 of the key index are
+// swapped, so that the KPL keys one lane needs for one MFMA step are contiguous.
+__device__ __forceinline__ int acc_key_col(int k) {
+  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
+
+}  // namespace laga

@@ -1,0 +1,50 @@
+// Host-side launchers of the LAGA kernels (internal; the public ABI is laga.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace laga {
+
+// Validated sizes of one call.  h local heads start at global head `head_lo`.
+struct Shape {
+  int64_t B, S, T;  // T = B * S tokens
+  int n_h, h, head_lo;
+  int d_kv, d_nope, d_rope, d_v;
+  float eps;
+  bool bf16;   // inputs are bfloat16 (else float32)
+  bool split;  // hi/lo split operands, float32 K/V (bf16 inputs only)
+  int C() const { return d_nope + d_v; }
+  int d_qk() const { return d_nope + d_rope; }
+};
+
+hipError_t launch_norm_fwd(const Shape& s, const void* latent, const void* gamma, float* L,
+                           float* rstd, hipStream_t st);
+hipError_t launch_kv_up(const Shape& s, const float* L, const void* w, void* k_nope, void* v,
+                        hipStream_t st);
+hipError_t launch_attn_fwd(const Shape& s, const void* q, const void* k_nope, const void* k_pe,
+                           const void* v, float* o, float* lse, hipStream_t st);
+
+// Backward pieces.  Workspace carving lives in the API layer.
+hipError_t launch_bwd_dot(const Shape& s, const float* o, const void* d_o, float* delta,
+                          hipStream_t st);
+hipError_t launch_attn_bwd_dkdv(const Shape& s, const void* q, const void* k_nope,
+                                const void* k_pe, const void* v, const float* lse,
+                                const float* delta, const void* d_o, float* dkv,
+                                float* dk_pe_part, hipStream_t st);
+hipError_t launch_attn_bwd_dq(const Shape& s, const void* q, const void* k_nope, const void* k_pe,
+                              const void* v, const float* lse, const float* delta,
+                              const void* d_o, float* dq, hipStream_t st);
+hipError_t launch_head_sum(const Shape& s, const float* part, float* out, hipStream_t st);
+hipError_t launch_fold_dl(const Shape& s, const float* dkv, const void* w, float* dL,
+                          hipStream_t st);
+size_t fold_dw_partial_floats(const Shape& s);
+hipError_t launch_fold_dw(const Shape& s, const float* dkv, const void* latent, const void* gamma,
+                          const float* rstd, float* partial, float* d_w, hipStream_t st);
+size_t norm_bwd_partial_floats(const Shape& s);
+hipError_t launch_norm_bwd(const Shape& s, const float* dL, const void* latent, const void* gamma,
+                           const float* rstd, float* d_latent, float* dgamma_part, float* d_gamma,
+                           hipStream_t st);
+
+}  // namespace laga

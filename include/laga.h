@@ -1,0 +1,161 @@
+/*
+ * laga.h -- C ABI of the LAGA per-rank attention path on one MI355X (gfx950).
+ *
+ * The operations follow "A Training-Memory Regression in MLA Sequence
+ * Parallelism: Why Megatron-Core Forbids Absorption, and LAGA -- a
+ * Communication-Efficient Fix" (arXiv 2607.17644v1), cited as [LAGA §...].
+ * A rank r of an SP group of size P owns the head shard
+ * H_r = [r*h, (r+1)*h) with h = n_h / P [LAGA §3.3, Algorithm 1 input] and,
+ * after the latent all-gather, holds the full-sequence latent and k_pe.  This
+ * library runs everything that rank computes locally: the latent norm, the
+ * head-shard up-projection, causal attention, and the backward of all three
+ * [LAGA §3.3 Algorithm 1; §5.1; §5.2].  Collectives are not part of it.
+ *
+ * Conventions shared by every entry point
+ *  - All arrays are dense, row-major, contiguous device memory owned by the
+ *    caller.  The library allocates nothing, keeps no state between calls and
+ *    is reentrant; calls on one stream are ordered by that stream.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
+ *    enqueued asynchronously; device faults surface at the caller's next
+ *    synchronisation.  Argument checks run on the host before any launch and
+ *    enqueue nothing when they fail.
+ *  - Every pointer must be non-NULL and 16-byte aligned (LAGA_ERR_ALIGN).
+ *  - Outputs are overwritten, never accumulated into.
+ *  - "in" dtype is dims->dtype: bfloat16 (raw 16-bit patterns) or float32.
+ *    Every output that is compared with an fp64 reference is float32.
+ *  - The attention mask is causal over global positions (key u <= query t),
+ *    with no dropout, bias, softcap or window.
+ *
+ * Layouts (T = B*S tokens, h local heads, d_qk = d_nope + d_rope, C = d_nope + d_v)
+ *   latent   [B, S, d_kv]  in        gathered latent (pre-norm)
+ *   gamma    [d_kv]        in        RMSNorm weight
+ *   latent_n [B, S, d_kv]  float32   L = gamma * latent * rstd
+ *   rstd     [B, S]        float32   1 / sqrt(mean(latent^2) + eps)
+ *   w_kv_b   [n_h, C, d_kv] in       full tensor; per head the d_nope K rows
+ *                                    then the d_v V rows; rows of H_r are read
+ *   q        [B, S, h, d_qk] in      nope part first, rope part already rotated
+ *   k_pe     [B, S, d_rope] in       one band shared by every head
+ *   k_nope   [B, S, h, d_nope] kv    kv element type, see laga_kv_elem_bytes
+ *   v        [B, S, h, d_v]    kv
+ *   o        [B, S, h, d_v]  float32
+ *   lse      [B, h, S]       float32 natural-log sum of exp(scores) per query
+ */
+#ifndef LAGA_H
+#define LAGA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LAGA_OK = 0,
+  LAGA_ERR_INVALID = 1,     /* NULL dims/pointer, B or S < 1, bad head split, eps <= 0 */
+  LAGA_ERR_UNSUPPORTED = 2, /* head dims / dtype / precision combination not built */
+  LAGA_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
+  LAGA_ERR_HIP = 4,         /* the HIP runtime reported an error at launch */
+  LAGA_ERR_WORKSPACE = 5    /* backward workspace missing or smaller than required */
+} laga_status;
+
+typedef enum { LAGA_F32 = 0, LAGA_BF16 = 1 } laga_dtype;
+
+/*
+ * Operand precision of the matrix-core contractions for LAGA_BF16 inputs.
+ *  LAGA_OPERANDS_FP16:  K/V are stored as fp16; scores, probabilities and V
+ *                       enter the MFMAs as single fp16 values (fp32 accumulate).
+ *  LAGA_OPERANDS_SPLIT: K/V are stored as float32 and every computed operand
+ *                       (L, K, V, P, dS, and the fold operands) enters the
+ *                       MFMAs as a hi+lo pair of fp16/bf16 values, giving
+ *                       fp32-class results at 2-3x the matrix-core work.
+ * LAGA_F32 inputs always use float32 MFMAs and float32 K/V (field ignored).
+ * The backward needs the K/V, o and lse of a LAGA_OPERANDS_SPLIT forward.
+ */
+typedef enum { LAGA_OPERANDS_FP16 = 0, LAGA_OPERANDS_SPLIT = 1 } laga_precision;
+
+/* Sizes in the paper's notation [LAGA §2.1, §3.3]. */
+typedef struct {
+  int64_t B;         /* batch */
+  int64_t S;         /* full (gathered) sequence length */
+  int32_t n_h;       /* total heads */
+  int32_t sp_size;   /* P, SP degree; n_h % P == 0 */
+  int32_t sp_rank;   /* r, 0 <= r < P */
+  int32_t d_kv;      /* latent width */
+  int32_t d_nope;    /* per-head non-positional q/k width */
+  int32_t d_rope;    /* decoupled RoPE band width */
+  int32_t d_v;       /* per-head value width */
+  float eps;         /* RMSNorm epsilon (1e-6) */
+  int32_t dtype;     /* laga_dtype of every "in" array */
+  int32_t precision; /* laga_precision */
+} laga_dims;
+
+/*
+ * Supported shapes: (d_kv, d_nope, d_rope, d_v) = (512, 128, 64, 128) with
+ * LAGA_BF16 (DeepSeek-V3 head dims [LAGA §4.1]) and (64, 32, 16, 32) with
+ * LAGA_F32.  Anything else returns LAGA_ERR_UNSUPPORTED.  Inputs must be
+ * finite; bf16 inputs converted to fp16 operands must stay below 65504 in
+ * magnitude.
+ */
+
+/* Bytes per element of k_nope / v for these dims: 2 (fp16) or 4 (float32).
+ * Returns 0 when the dims are invalid or unsupported. */
+size_t laga_kv_elem_bytes(const laga_dims* dims);
+
+/*
+ * Latent RMSNorm [LAGA §2.1 "kv = W_kv_b LN(latent)"; §3.3 Algorithm 1 norm
+ * of the latent].  Per token t: rstd[t] = 1/sqrt(mean_j latent[t,j]^2 + eps),
+ * latent_n[t,j] = gamma[j] * latent[t,j] * rstd[t].
+ */
+laga_status laga_latent_norm(const laga_dims* dims, const void* latent, const void* gamma,
+                             float* latent_n, float* rstd, void* stream);
+
+/*
+ * Head-shard up-projection [LAGA §3.3 Algorithm 1 local up-projection; §5.1]:
+ * for i in [0, h): k_nope[t,i,:] = W_kv_b[r*h+i, 0:d_nope, :] . latent_n[t,:]
+ * and v[t,i,:] = W_kv_b[r*h+i, d_nope:C, :] . latent_n[t,:].  Output element
+ * type is given by laga_kv_elem_bytes.
+ */
+laga_status laga_kv_up(const laga_dims* dims, const float* latent_n, const void* w_kv_b,
+                       void* k_nope, void* v, void* stream);
+
+/*
+ * Causal attention forward of the h local heads [LAGA §3.3 Algorithm 1 scores,
+ * softmax and output; §5.3 the k_pe band is shared by all heads]:
+ * s[t,u] = (q_nope[t,i] || q_rope[t,i]) . (k_nope[u,i] || k_pe[u]) / sqrt(d_nope + d_rope)
+ * for u <= t; o[t,i] = sum_u softmax_u(s) v[u,i]; lse[i,t] = ln sum_u exp(s[t,u]).
+ */
+laga_status laga_attn_fwd(const laga_dims* dims, const void* q, const void* k_nope,
+                          const void* k_pe, const void* v, float* o, float* lse, void* stream);
+
+/* Workspace bytes laga_attn_bwd needs for these dims (0 if invalid). */
+size_t laga_attn_bwd_workspace_bytes(const laga_dims* dims);
+
+/*
+ * Backward of the rank-local path for the loss sum(d_o * o) [LAGA §5.2]:
+ *   dq        [B,S,h,d_qk] float32
+ *   d_latent  [B,S,d_kv]   float32  gradient w.r.t. the pre-norm gathered latent
+ *                                   (this rank's partial; the cross-rank sum is a
+ *                                   reduce-scatter outside this library)
+ *   d_k_pe    [B,S,d_rope] float32  sum over the local heads (this rank's partial)
+ *   d_w_kv_b  [n_h,C,d_kv] float32  rows of H_r written; other rows untouched
+ *   d_gamma   [d_kv]       float32  this rank's partial
+ * Inputs are those of the forward plus its o and lse (LAGA_OPERANDS_SPLIT for
+ * LAGA_BF16), rstd from laga_latent_norm, and d_o [B,S,h,d_v] in the input
+ * dtype.  workspace: device memory of at least laga_attn_bwd_workspace_bytes.
+ */
+laga_status laga_attn_bwd(const laga_dims* dims, const void* q, const void* latent,
+                          const void* gamma, const float* rstd, const void* k_nope,
+                          const void* k_pe, const void* v, const void* w_kv_b,
+                          const float* o, const float* lse, const void* d_o, float* dq,
+                          float* d_latent, float* d_k_pe, float* d_w_kv_b, float* d_gamma,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, human-readable text of a status code. */
+const char* laga_status_string(laga_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LAGA_H */

@@ -130,3 +130,13 @@ def make_inputs(dims: Dims, seed: int = 0, backward: bool = False) -> dict[str, 
 def workload(name: str) -> tuple[Dims, bool]:
     w = WORKLOADS[name]
     return w["dims"], w["backward"]
+
+
+def to_torch(t: Tensor, device="cuda"):
+    """Copy one input to a torch tensor on `device` in its storage dtype (bf16 or float32)."""
+    import torch
+    if t.dtype == BF16:
+        host = torch.from_numpy(t.raw.view(np.int16)).view(torch.bfloat16)
+    else:
+        host = torch.from_numpy(t.raw)
+    return host.to(device).contiguous()

@@ -1,0 +1,118 @@
+"""The C ABI loads and rejects bad arguments on the host (CPU only, no launches).
+
+Every case here returns from the library's argument checks before any HIP
+call, so it runs without a GPU.
+"""
+import ctypes
+import subprocess
+
+import pytest
+
+from head_latent_attention_laga_amd import _lib
+from head_latent_attention_laga_amd.build import LIB
+
+OK, INVALID, UNSUPPORTED, ALIGN, HIP, WORKSPACE = range(6)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def v3(**kw):
+    d = dict(B=1, S=512, n_h=128, sp_size=8, sp_rank=0, d_kv=512, d_nope=128, d_rope=64, d_v=128,
+             dtype=_lib.LAGA_BF16, precision=_lib.LAGA_OPERANDS_SPLIT)
+    d.update(kw)
+    return _lib.make_dims(**d)
+
+
+def tiny(**kw):
+    d = dict(B=1, S=256, n_h=2, sp_size=1, sp_rank=0, d_kv=64, d_nope=32, d_rope=16, d_v=32,
+             dtype=_lib.LAGA_F32, precision=0)
+    d.update(kw)
+    return _lib.make_dims(**d)
+
+
+FAKE = ctypes.c_void_p(1 << 20)     # 16-byte aligned, never dereferenced
+MISALIGNED = ctypes.c_void_p((1 << 20) + 4)
+
+
+def test_exports_every_header_function(lib):
+    names = _lib.header_functions()
+    assert set(names) >= {"laga_latent_norm", "laga_kv_up", "laga_attn_fwd", "laga_attn_bwd",
+                          "laga_attn_bwd_workspace_bytes", "laga_status_string", "laga_kv_elem_bytes"}
+    syms = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    for n in names:
+        assert getattr(lib, n) is not None
+        assert f" T {n}\n" in syms, n
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert lib.laga_status_string(s).decode().startswith(_lib.STATUS[s])
+
+
+def test_kv_elem_bytes():
+    assert _lib.kv_elem_bytes(tiny()) == 4
+    assert _lib.kv_elem_bytes(v3(precision=_lib.LAGA_OPERANDS_FP16)) == 2
+    assert _lib.kv_elem_bytes(v3(precision=_lib.LAGA_OPERANDS_SPLIT)) == 4
+    assert _lib.kv_elem_bytes(v3(d_kv=256)) == 0
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(B=0), INVALID), (dict(S=0), INVALID), (dict(n_h=0), INVALID), (dict(sp_size=0), INVALID),
+    (dict(n_h=12, sp_size=8), INVALID), (dict(sp_rank=8), INVALID), (dict(sp_rank=-1), INVALID),
+    (dict(eps=0.0), INVALID), (dict(dtype=7), INVALID), (dict(precision=3), INVALID),
+    (dict(d_kv=256), UNSUPPORTED), (dict(d_rope=32), UNSUPPORTED), (dict(d_v=64), UNSUPPORTED),
+    (dict(dtype=_lib.LAGA_F32), UNSUPPORTED), (dict(S=1 << 23), UNSUPPORTED),
+])
+def test_dims_rejected_before_launch(lib, bad, code):
+    d = v3(**bad)
+    assert lib.laga_latent_norm(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None) == code
+    assert lib.laga_kv_up(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None) == code
+    assert lib.laga_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == code
+    assert lib.laga_attn_bwd_workspace_bytes(ctypes.byref(d)) == 0
+    args = [FAKE] * 17 + [ctypes.c_size_t(1 << 40), None]
+    assert lib.laga_attn_bwd(ctypes.byref(d), *args) == code
+
+
+def test_null_dims(lib):
+    assert lib.laga_attn_fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == INVALID
+    assert lib.laga_attn_bwd_workspace_bytes(None) == 0
+
+
+@pytest.mark.parametrize("slot", range(6))
+def test_null_and_misaligned_pointers(lib, slot):
+    d = v3()
+    args = [FAKE] * 6
+    args[slot] = None
+    assert lib.laga_attn_fwd(ctypes.byref(d), *args, None) == INVALID
+    args[slot] = MISALIGNED
+    assert lib.laga_attn_fwd(ctypes.byref(d), *args, None) == ALIGN
+
+
+def test_backward_argument_checks(lib):
+    d = v3()
+    need = lib.laga_attn_bwd_workspace_bytes(ctypes.byref(d))
+    assert need > 0
+    args = [FAKE] * 17
+    assert lib.laga_attn_bwd(ctypes.byref(d), *args, ctypes.c_size_t(need - 1), None) == WORKSPACE
+    a2 = list(args)
+    a2[16] = None  # workspace pointer
+    assert lib.laga_attn_bwd(ctypes.byref(d), *a2, ctypes.c_size_t(need), None) == WORKSPACE
+    a3 = list(args)
+    a3[4] = None
+    assert lib.laga_attn_bwd(ctypes.byref(d), *a3, ctypes.c_size_t(need), None) == INVALID
+    a4 = list(args)
+    a4[10] = MISALIGNED
+    assert lib.laga_attn_bwd(ctypes.byref(d), *a4, ctypes.c_size_t(need), None) == ALIGN
+    # the backward needs the fp32-class K/V of a split-operand forward
+    d16 = v3(precision=_lib.LAGA_OPERANDS_FP16)
+    assert lib.laga_attn_bwd(ctypes.byref(d16), *args, ctypes.c_size_t(1 << 40), None) == UNSUPPORTED
+
+
+def test_workspace_grows_with_sequence(lib):
+    a = lib.laga_attn_bwd_workspace_bytes(ctypes.byref(v3(S=1024)))
+    b = lib.laga_attn_bwd_workspace_bytes(ctypes.byref(v3(S=2048)))
+    assert b > a > 0
+    assert lib.laga_attn_bwd_workspace_bytes(ctypes.byref(tiny())) > 0
