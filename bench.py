@@ -1,0 +1,225 @@
+"""Benchmark of the LAGA per-rank attention block on one MI355X.
+
+One step = the whole per-rank hot path on one batch of seeded synthetic input
+already resident in HBM: latent RMSNorm -> head-shard up-projection -> causal
+attention forward -> attention backward folded into dLatent / dW_kv_b / dgamma.
+Workload: B=1, S=16384, 16 local heads (n_h=128 at SP=8, rank 0), DeepSeek-V3
+head dims (d_kv=512, d_nope=d_v=128, d_rope=64), bf16 inputs, causal, with the
+split-operand precision the training step needs for its parity bars.  The
+forward alone is also timed with single fp16 operands (the forward-only
+workload's setting).
+
+Prints one JSON line with tokens/s, algorithmic TFLOP/s, per-kernel times
+(HIP events on the launch stream), the roofline of the dominant kernel, the
+fp64 oracle timed on a bounded sample on the host cores, and activation
+memory of LAGA against the explicit and absorbed forms.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+WORKLOAD = "v3_sp8_s16384_h16_train"
+METRIC = "MLA attention-block tokens/s and TFLOP/s (fwd, fwd+bwd) vs bf16 MFMA peak, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+FP16, SPLIT = 0, 1
+
+
+def alg_flops(d) -> dict:
+    """Algorithmic FLOPs: causal pairs only, no recompute, no hi/lo extra passes."""
+    pairs = d.S * (d.S + 1) / 2
+    attn_fwd = 2 * pairs * (d.d_qk + d.d_v) * d.h * d.B
+    kv_up = 2 * d.B * d.S * d.d_kv * d.h * (d.d_nope + d.d_v)
+    return dict(attn_fwd=attn_fwd, attn_bwd=2 * attn_fwd, kv_up=kv_up, fold=2 * kv_up,
+                fwd=attn_fwd + kv_up, step=3 * attn_fwd + 3 * kv_up)
+
+
+def activation_bytes(d, kv_bytes: int) -> dict:
+    """Bytes one rank keeps for the backward: LAGA vs the explicit (B1) and absorbed (B2) forms."""
+    T, h = d.B * d.S, d.h
+    common = T * h * d.d_qk * 2 + T * h * d.d_v * 4 + T * h * 4        # q (bf16), o (fp32), lse
+    laga = common + T * d.d_kv * 2 + T * d.d_rope * 2 + T * 4 + T * h * (d.d_nope + d.d_v) * kv_bytes
+    explicit = common + T * h * (d.d_qk + d.d_v) * kv_bytes             # per-head K (incl. rope band) and V
+    absorbed = common + T * d.d_kv * 2 + T * d.d_rope * 2 + T * 4 + 2 * T * h * d.d_kv * kv_bytes
+    return dict(laga=laga, explicit=explicit, absorbed=absorbed)
+
+
+def kernel_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter summary."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return {}
+    with open(path) as f:
+        return json.load(f)
+
+
+def cpu_baseline(d) -> dict:
+    """The fp64 oracle, untuned, on 4 of the workload's heads (n_h=128 at SP=32, rank 0):
+    norm, up-projection of those heads, causal attention forward and backward, and the
+    folds, at the full S.  Tokens/s is scaled to the workload's head count."""
+    import laga_inputs as li
+    import oracle
+    from threadpoolctl import threadpool_info
+    sample_heads = 4
+    one = li.Dims(B=d.B, S=d.S, n_h=d.n_h, sp_size=d.n_h // sample_heads, sp_rank=0, d_kv=d.d_kv, d_nope=d.d_nope,
+                  d_rope=d.d_rope, d_v=d.d_v, dtype=d.dtype)
+    inp = li.make_inputs(one, 0, backward=True)
+    v = {k: t.value for k, t in inp.items()}
+    kw = dict(n_h=one.n_h, sp_size=one.sp_size, sp_rank=0, d_nope=one.d_nope, eps=one.eps)
+    t0 = time.perf_counter()
+    f = oracle.forward(v["q"], v["latent"], v["k_pe"], v["w_kv_b"], v["gamma"], **kw)
+    oracle.backward(v["q"], v["latent"], v["k_pe"], v["w_kv_b"], v["gamma"], v["d_o"], fwd=f, **kw)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": d.B * d.S * sample_heads / (dt * d.h), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"fp64 oracle fwd+bwd of {sample_heads} of the {d.h} heads at full S={d.S} "
+                      f"({dt:.1f} s), scaled by {sample_heads}/{d.h}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU's share of the SP group; runs on more than one GPU "
+              "are not part of this path (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import laga_inputs as li
+    from head_latent_attention_laga_amd import LagaPath, _lib
+
+    d, _ = li.workload(WORKLOAD)
+    inp = li.make_inputs(d, 0, backward=True)
+    x = {k: li.to_torch(t) for k, t in inp.items()}
+    dev = torch.device("cuda")
+    path = LagaPath(d.B, d.S, d.n_h, d.sp_size, d.sp_rank, d.d_kv, d.d_nope, d.d_rope, d.d_v, d.dtype, SPLIT,
+                    d.eps)
+    fwd = path.alloc_forward()
+    grads = path.alloc_backward()
+    fast = LagaPath(d.B, d.S, d.n_h, d.sp_size, d.sp_rank, d.d_kv, d.d_nope, d.d_rope, d.d_v, d.dtype, FP16,
+                    d.eps)
+    ffwd = fast.alloc_forward()
+    torch.cuda.synchronize()
+
+    names = ["rmsnorm_fwd", "kv_up", "attn_fwd"] + list(_lib.BWD_STAGE_NAMES)
+    nev = 3 + _lib.LAGA_BWD_STAGES + 1
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+
+    def step(e=None):
+        dims = path.dims
+        if e is not None:
+            e[0].record()
+        _lib.latent_norm(dims, x["latent"], x["gamma"], fwd["latent_n"], fwd["rstd"])
+        if e is not None:
+            e[1].record()
+        _lib.kv_up(dims, fwd["latent_n"], x["w_kv_b"], fwd["k_nope"], fwd["v"])
+        if e is not None:
+            e[2].record()
+        _lib.attn_fwd(dims, x["q"], fwd["k_nope"], x["k_pe"], fwd["v"], fwd["o"], fwd["lse"])
+        g = grads
+        bargs = (dims, x["q"], x["latent"], x["gamma"], fwd["rstd"], fwd["k_nope"], x["k_pe"], fwd["v"],
+                 x["w_kv_b"], fwd["o"], fwd["lse"], x["d_o"], g["dq"], g["d_latent"], g["d_k_pe"],
+                 g["d_w_kv_b"], g["d_gamma"], g["workspace"])
+        if e is not None:
+            _lib.attn_bwd_traced(*bargs, events=e[3:])
+        else:
+            _lib.attn_bwd(*bargs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {n: statistics.mean(ev[i][k].elapsed_time(ev[i][k + 1]) for i in range(args.steps))
+           for k, n in enumerate(names)}
+    ms_step = wall * 1e3 / args.steps
+    fl = alg_flops(d)
+    tok_s = d.B * d.S / (ms_step / 1e3)
+
+    # Forward alone with single fp16 operands (the forward-only workload's precision).
+    fe = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for _ in range(args.warmup):
+        fast.forward(x, ffwd)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(args.steps):
+        e = fe[i]
+        e[0].record()
+        _lib.latent_norm(fast.dims, x["latent"], x["gamma"], ffwd["latent_n"], ffwd["rstd"])
+        e[1].record()
+        _lib.kv_up(fast.dims, ffwd["latent_n"], x["w_kv_b"], ffwd["k_nope"], ffwd["v"])
+        e[2].record()
+        _lib.attn_fwd(fast.dims, x["q"], ffwd["k_nope"], x["k_pe"], ffwd["v"], ffwd["o"], ffwd["lse"])
+        e[3].record()
+    torch.cuda.synchronize()
+    fwall = (time.perf_counter() - t1) * 1e3 / args.steps
+    fper = {n: statistics.mean(fe[i][k].elapsed_time(fe[i][k + 1]) for i in range(args.steps))
+            for k, n in enumerate(["rmsnorm_fwd", "kv_up", "attn_fwd"])}
+
+    # Roofline of the dominant kernel of the step.
+    work = {"rmsnorm_fwd": ("hbm", d.B * d.S * d.d_kv * (2 + 4) + 4 * d.B * d.S + 2 * d.d_kv),
+            "kv_up": ("mfma", fl["kv_up"]), "attn_fwd": ("mfma", fl["attn_fwd"]),
+            "attn_bwd_dkdv": ("mfma", fl["attn_bwd"] * 3 / 5), "attn_bwd_dq": ("mfma", fl["attn_bwd"] * 2 / 5),
+            "fold_dL": ("mfma", fl["kv_up"]), "fold_dW": ("mfma", fl["kv_up"])}
+    dom = max((n for n in per if n in work), key=lambda n: per[n])
+    bound, units = work[dom]
+    ach = units / (per[dom] / 1e3) / (1e12 if bound == "mfma" else 1e9)
+    peak = PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_HBM_GBS
+    tr = kernel_traffic().get(dom)
+    roofline = {"kernel": dom, "bound": bound, "achieved": round(ach, 2), "peak": peak,
+                "unit": "TFLOP/s" if bound == "mfma" else "GB/s", "frac": round(ach / peak, 4),
+                "traffic": tr}
+
+    fwd_ms = fper["rmsnorm_fwd"] + fper["kv_up"] + fper["attn_fwd"]
+    kvb = _lib.kv_elem_bytes(path.dims)
+    act = {k: round(v / 2**20, 1) for k, v in activation_bytes(d, kvb).items()}
+    line = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "LAGA per-rank MLA attention block fwd+bwd, causal, one rank's head shard",
+                   "B": d.B, "S": d.S, "local_heads": d.h, "n_h": d.n_h, "sp_size": d.sp_size,
+                   "d_kv": d.d_kv, "d_nope": d.d_nope, "d_rope": d.d_rope, "d_v": d.d_v,
+                   "operands": "fp16/bf16 hi+lo split, fp32 accumulate", "parallelism": "one GPU (one SP rank)"},
+        "tflops_step": round(fl["step"] / (ms_step / 1e3) / 1e12, 2),
+        "frac_peak_step": round(fl["step"] / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "forward_fp16_operands": {
+            "ms": round(fwd_ms, 4), "wall_ms": round(fwall, 4), "tokens_s": round(d.B * d.S / (fwd_ms / 1e3), 1),
+            "tflops": round(fl["fwd"] / (fwd_ms / 1e3) / 1e12, 2),
+            "frac_peak": round(fl["fwd"] / (fwd_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "attn_tflops": round(fl["attn_fwd"] / (fper["attn_fwd"] / 1e3) / 1e12, 2),
+            "kernels_ms": {k: round(v, 4) for k, v in fper.items()}},
+        "kernels_ms": {k: round(v, 4) for k, v in per.items()},
+        "roofline": roofline,
+        "activation_mb": act,
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        del x, fwd, grads, ffwd
+        torch.cuda.empty_cache()
+        line["cpu_baseline"] = cpu_baseline(d)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

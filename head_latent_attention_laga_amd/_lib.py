@@ -17,6 +17,9 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "laga.h")
 
 LAGA_F32, LAGA_BF16 = 0, 1
 LAGA_OPERANDS_FP16, LAGA_OPERANDS_SPLIT = 0, 1
+LAGA_BWD_STAGES = 7
+BWD_STAGE_NAMES = ("bwd_delta", "attn_bwd_dkdv", "attn_bwd_dq", "dk_pe_head_sum", "fold_dL", "fold_dW",
+                   "rmsnorm_bwd")
 STATUS = {0: "LAGA_OK", 1: "LAGA_ERR_INVALID", 2: "LAGA_ERR_UNSUPPORTED", 3: "LAGA_ERR_ALIGN",
           4: "LAGA_ERR_HIP", 5: "LAGA_ERR_WORKSPACE"}
 
@@ -46,6 +49,8 @@ _SIGS = {
     "laga_attn_fwd": (ctypes.c_int, [ctypes.POINTER(laga_dims), _P, _P, _P, _P, _P, _P, _P]),
     "laga_attn_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(laga_dims)]),
     "laga_attn_bwd": (ctypes.c_int, [ctypes.POINTER(laga_dims)] + [_P] * 17 + [ctypes.c_size_t, _P]),
+    "laga_attn_bwd_traced": (ctypes.c_int, [ctypes.POINTER(laga_dims)] + [_P] * 17
+                             + [ctypes.c_size_t, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, _P]),
     "laga_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -129,3 +134,19 @@ def attn_bwd(dims, q, latent, gamma, rstd, k_nope, k_pe, v, w_kv_b, o, lse, d_o,
         _ptr(v), _ptr(w_kv_b), _ptr(o), _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(d_latent), _ptr(d_k_pe),
         _ptr(d_w_kv_b), _ptr(d_gamma), _ptr(workspace), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
         _stream(stream)))
+
+
+def attn_bwd_traced(dims, q, latent, gamma, rstd, k_nope, k_pe, v, w_kv_b, o, lse, d_o, dq, d_latent,
+                    d_k_pe, d_w_kv_b, d_gamma, workspace, events, stream=None):
+    """laga_attn_bwd recording `events` (LAGA_BWD_STAGES + 1 torch.cuda.Event with timing) around its stages."""
+    if len(events) != LAGA_BWD_STAGES + 1:
+        raise ValueError(f"need {LAGA_BWD_STAGES + 1} events")
+    for e in events:
+        if e.cuda_event == 0:  # torch creates the HIP event lazily
+            e.record()
+    arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+    _check("laga_attn_bwd_traced", load().laga_attn_bwd_traced(
+        ctypes.byref(dims), _ptr(q), _ptr(latent), _ptr(gamma), _ptr(rstd), _ptr(k_nope), _ptr(k_pe),
+        _ptr(v), _ptr(w_kv_b), _ptr(o), _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(d_latent), _ptr(d_k_pe),
+        _ptr(d_w_kv_b), _ptr(d_gamma), _ptr(workspace), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+        arr, len(events), _stream(stream)))

@@ -119,14 +119,18 @@ size_t laga_attn_bwd_workspace_bytes(const laga_dims* dims) {
   return bwd_layout(s).total;
 }
 
-laga_status laga_attn_bwd(const laga_dims* dims, const void* q, const void* latent, const void* gamma,
-                          const float* rstd, const void* k_nope, const void* k_pe, const void* v,
-                          const void* w_kv_b, const float* o, const float* lse, const void* d_o,
-                          float* dq, float* d_latent, float* d_k_pe, float* d_w_kv_b, float* d_gamma,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+laga_status laga_attn_bwd_traced(const laga_dims* dims, const void* q, const void* latent, const void* gamma,
+                                 const float* rstd, const void* k_nope, const void* k_pe, const void* v,
+                                 const void* w_kv_b, const float* o, const float* lse, const void* d_o, float* dq,
+                                 float* d_latent, float* d_k_pe, float* d_w_kv_b, float* d_gamma, void* workspace,
+                                 size_t workspace_bytes, void* const* events, int n_events, void* stream) {
   Shape s;
   laga_status st = check_dims(dims, &s);
   if (st != LAGA_OK) return st;
+  if (n_events != 0 && (n_events != LAGA_BWD_STAGES + 1 || events == nullptr)) return LAGA_ERR_INVALID;
+  if (n_events != 0)
+    for (int i = 0; i < n_events; ++i)
+      if (events[i] == nullptr) return LAGA_ERR_INVALID;
   if (s.bf16 && !s.split) return LAGA_ERR_UNSUPPORTED;  // the backward needs fp32-class K/V
   const void* ptrs[] = {q, latent, gamma, rstd, k_nope, k_pe, v, w_kv_b, o, lse, d_o,
                         dq, d_latent, d_k_pe, d_w_kv_b, d_gamma};
@@ -145,19 +149,39 @@ laga_status laga_attn_bwd(const laga_dims* dims, const void* q, const void* late
   float* dw = reinterpret_cast<float*>(ws + L.dw);
   float* dg = reinterpret_cast<float*>(ws + L.dg);
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  auto mark = [&](int i) -> hipError_t {
+    return n_events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), hs) : hipSuccess;
+  };
 
   hipError_t e;
+  if ((e = mark(0)) != hipSuccess) return from_hip(e);
   if ((e = laga::launch_bwd_dot(s, o, d_o, delta, hs)) != hipSuccess) return from_hip(e);
+  if ((e = mark(1)) != hipSuccess) return from_hip(e);
   if ((e = laga::launch_attn_bwd_dkdv(s, q, k_nope, k_pe, v, lse, delta, d_o, dkv, dkpe, hs)) != hipSuccess)
     return from_hip(e);
+  if ((e = mark(2)) != hipSuccess) return from_hip(e);
   if ((e = laga::launch_attn_bwd_dq(s, q, k_nope, k_pe, v, lse, delta, d_o, dq, hs)) != hipSuccess)
     return from_hip(e);
+  if ((e = mark(3)) != hipSuccess) return from_hip(e);
   if ((e = laga::launch_head_sum(s, dkpe, d_k_pe, hs)) != hipSuccess) return from_hip(e);
+  if ((e = mark(4)) != hipSuccess) return from_hip(e);
   if ((e = laga::launch_fold_dl(s, dkv, w_kv_b, dL, hs)) != hipSuccess) return from_hip(e);
+  if ((e = mark(5)) != hipSuccess) return from_hip(e);
   if ((e = laga::launch_fold_dw(s, dkv, latent, gamma, rstd, dw, d_w_kv_b, hs)) != hipSuccess) return from_hip(e);
+  if ((e = mark(6)) != hipSuccess) return from_hip(e);
   if ((e = laga::launch_norm_bwd(s, dL, latent, gamma, rstd, d_latent, dg, d_gamma, hs)) != hipSuccess)
     return from_hip(e);
+  if ((e = mark(7)) != hipSuccess) return from_hip(e);
   return LAGA_OK;
+}
+
+laga_status laga_attn_bwd(const laga_dims* dims, const void* q, const void* latent, const void* gamma,
+                          const float* rstd, const void* k_nope, const void* k_pe, const void* v,
+                          const void* w_kv_b, const float* o, const float* lse, const void* d_o,
+                          float* dq, float* d_latent, float* d_k_pe, float* d_w_kv_b, float* d_gamma,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return laga_attn_bwd_traced(dims, q, latent, gamma, rstd, k_nope, k_pe, v, w_kv_b, o, lse, d_o, dq, d_latent,
+                              d_k_pe, d_w_kv_b, d_gamma, workspace, workspace_bytes, nullptr, 0, stream);
 }
 
 const char* laga_status_string(laga_status status) {

@@ -151,6 +151,27 @@ laga_status laga_attn_bwd(const laga_dims* dims, const void* q, const void* late
                           float* d_latent, float* d_k_pe, float* d_w_kv_b, float* d_gamma,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * laga_attn_bwd with stage timing, for tracing tools.  `events` holds
+ * n_events hipEvent_t handles created by the caller; with n_events ==
+ * LAGA_BWD_STAGES + 1 the library records events[i] on `stream` right before
+ * stage i and events[LAGA_BWD_STAGES] after the last, so that
+ * hipEventElapsedTime(events[i], events[i+1]) is the duration of stage i:
+ *   0 delta = rowsum(d_o * o)     1 dK/dV attention kernel   2 dq attention kernel
+ *   3 dk_pe head sum              4 fold into dL             5 fold into dW_kv_b (+ chunk sum)
+ *   6 RMSNorm backward (+ dgamma reduction)
+ * n_events == 0 behaves exactly like laga_attn_bwd; any other count returns
+ * LAGA_ERR_INVALID.  Recording failures return LAGA_ERR_HIP.
+ */
+#define LAGA_BWD_STAGES 7
+laga_status laga_attn_bwd_traced(const laga_dims* dims, const void* q, const void* latent,
+                                 const void* gamma, const float* rstd, const void* k_nope,
+                                 const void* k_pe, const void* v, const void* w_kv_b,
+                                 const float* o, const float* lse, const void* d_o, float* dq,
+                                 float* d_latent, float* d_k_pe, float* d_w_kv_b, float* d_gamma,
+                                 void* workspace, size_t workspace_bytes, void* const* events,
+                                 int n_events, void* stream);
+
 /* Static, human-readable text of a status code. */
 const char* laga_status_string(laga_status status);
 
