@@ -94,7 +94,7 @@ struct BwdArgs {
   const void* q; const void* k_nope; const void* k_pe; const void* v;
   const float* lse; const float* delta; const void* d_o;
   float* dkv; float* dk_pe_part; float* dq;
-  int64_t S; int B, h; float scale_log2, scale;
+  int64_t S, plane_k, plane_v; int B, h; float scale_log2, scale;
 };
 
 // ============================================================ dK / dV kernel
@@ -141,7 +141,8 @@ struct DkdvKernel {
       const int d0 = s * M::K + hf * M::KPL;
       F tmp[SPLIT];
       if (d0 < DN) {
-        load_frag_split<M, SPLIT>(kn + krow * DN + d0, kvalid, tmp);
+#pragma unroll
+        for (int p = 0; p < SPLIT; ++p) load_frag_split<M, 1>(kn + p * a.plane_k + krow * DN + d0, kvalid, &tmp[p]);
       } else {
         load_frag_split<M, 1>(kp + (b * a.S + (kvalid ? key : 0)) * DR + (d0 - DN), kvalid, tmp);
         if constexpr (SPLIT == 2) tmp[1] = F{};
@@ -152,7 +153,9 @@ struct DkdvKernel {
 #pragma unroll
     for (int s = 0; s < KS_V; ++s) {
       F tmp[SPLIT];
-      load_frag_split<M, SPLIT>(vg + krow * DV + s * M::K + hf * M::KPL, kvalid, tmp);
+#pragma unroll
+      for (int p = 0; p < SPLIT; ++p)
+        load_frag_split<M, 1>(vg + p * a.plane_v + krow * DV + s * M::K + hf * M::KPL, kvalid, &tmp[p]);
 #pragma unroll
       for (int p = 0; p < SPLIT; ++p) vf[p][s] = tmp[p];
     }
@@ -329,11 +332,16 @@ struct DqKernel {
     for (int64_t key0 = 0; key0 < kend; key0 += BN) {
       const int nk = static_cast<int>(a.S - key0 < BN ? a.S - key0 : BN);
       __syncthreads();
-      stage<M, KvT, BN, DN, SPLIT, true, true>(kn + ((b * a.S + key0) * a.h + head) * DN, int64_t(a.h) * DN, nk,
-                                               Ks, LDK, OFF_KL, Kt, LDT);
+      stage<M, KvT, BN, DN, 1, true, true>(kn + ((b * a.S + key0) * a.h + head) * DN, int64_t(a.h) * DN, nk,
+                                           Ks, LDK, 0, Kt, LDT);
+      if constexpr (SPLIT == 2)
+        stage<M, KvT, BN, DN, 1, true, false>(kn + a.plane_k + ((b * a.S + key0) * a.h + head) * DN,
+                                              int64_t(a.h) * DN, nk, Kl, LDK, 0, nullptr, 0);
       stage<M, InT, BN, DR, 1, true, true>(kp + (b * a.S + key0) * DR, DR, nk, Ks + DN, LDK, 0, Kt + DN * LDT, LDT);
-      stage<M, KvT, BN, DV, SPLIT, true, false>(vg + ((b * a.S + key0) * a.h + head) * DV, int64_t(a.h) * DV, nk,
-                                                Vs, LDV, BN * LDV, nullptr, 0);
+#pragma unroll
+      for (int p = 0; p < SPLIT; ++p)
+        stage<M, KvT, BN, DV, 1, true, false>(vg + p * a.plane_v + ((b * a.S + key0) * a.h + head) * DV,
+                                              int64_t(a.h) * DV, nk, Vs + p * BN * LDV, LDV, 0, nullptr, 0);
       __syncthreads();
       if (key0 > qw + 31) continue;
 
@@ -417,6 +425,8 @@ BwdArgs make_args(const Shape& s, const void* q, const void* kn, const void* kp,
   a.q = q; a.k_nope = kn; a.k_pe = kp; a.v = v; a.lse = lse; a.delta = delta; a.d_o = d_o;
   a.dkv = nullptr; a.dk_pe_part = nullptr; a.dq = nullptr;
   a.S = s.S; a.B = static_cast<int>(s.B); a.h = s.h;
+  a.plane_k = s.T * s.h * s.d_nope;
+  a.plane_v = s.T * s.h * s.d_v;
   a.scale = 1.0f / sqrtf(static_cast<float>(s.d_qk()));
   a.scale_log2 = 1.4426950408889634f * a.scale;
   return a;
@@ -481,7 +491,7 @@ hipError_t launch_attn_bwd_dkdv(const Shape& s, const void* q, const void* kn, c
   a.dk_pe_part = dk_pe_part;
   const unsigned grid = static_cast<unsigned>(((s.S + 127) / 128) * s.B * s.h);
   if (s.bf16 && s.split && s.d_nope == 128 && s.d_rope == 64 && s.d_v == 128)
-    hipLaunchKernelGGL((dkdv_kernel<bf16_t, float, MmaF16, 2, 128, 64, 128>), dim3(grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((dkdv_kernel<bf16_t, half_t, MmaF16, 2, 128, 64, 128>), dim3(grid), dim3(kThreads), 0, st, a);
   else if (!s.bf16 && s.d_nope == 32 && s.d_rope == 16 && s.d_v == 32)
     hipLaunchKernelGGL((dkdv_kernel<float, float, MmaF32, 1, 32, 16, 32>), dim3(grid), dim3(kThreads), 0, st, a);
   else
@@ -495,7 +505,7 @@ hipError_t launch_attn_bwd_dq(const Shape& s, const void* q, const void* kn, con
   a.dq = dq;
   const unsigned grid = static_cast<unsigned>(((s.S + 127) / 128) * s.B * s.h);
   if (s.bf16 && s.split && s.d_nope == 128 && s.d_rope == 64 && s.d_v == 128)
-    hipLaunchKernelGGL((dq_kernel<bf16_t, float, MmaF16, 2, 128, 64, 128>), dim3(grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((dq_kernel<bf16_t, half_t, MmaF16, 2, 128, 64, 128>), dim3(grid), dim3(kThreads), 0, st, a);
   else if (!s.bf16 && s.d_nope == 32 && s.d_rope == 16 && s.d_v == 32)
     hipLaunchKernelGGL((dq_kernel<float, float, MmaF32, 1, 32, 16, 32>), dim3(grid), dim3(kThreads), 0, st, a);
   else

@@ -1,0 +1,74 @@
+// Pieces shared by the attention kernels: LDS tile staging with 16-byte
+// copies and the transposing LDS read that turns a row-major [k][n] tile
+// into 32x32 MFMA operand fragments.
+#pragma once
+
+#include "device.hpp"
+
+namespace laga {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// gfx950 transposing LDS read of 16-bit elements.  Within each group of 16
+// lanes, lane i receives element (i % 4) of the 8-byte words that lanes
+// 4j + i/4 (j = 0..3) addressed.  If lane s of the group addresses row
+// k0 + s/4, columns c0 + 4(s%4) .. +3 of a row-major tile, lane i therefore
+// gets column c0 + i, rows k0 .. k0+3.
+__device__ __forceinline__ s16x4 ds_read_tr16(const void* lds_ptr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(reinterpret_cast<uintptr_t>(lds_ptr)));
+}
+
+// Fragment of an operand whose k index runs down the rows of a row-major
+// 16-bit tile (k = row, n = column; row pitch `ld` elements), for a 32x32x16
+// atom: lane l gets column n0 + l%32 and the 8 rows
+//   k0 + 4*hf + [0,4)  and  k0 + 8 + 4*hf + [0,4)      (hf = l / 32)
+// which is the key order that 32x32 accumulator registers r = 8*st .. 8*st+7
+// hold (see acc_key_col), so probabilities and score gradients can be fed
+// straight from accumulators against this operand.
+template <class E>
+__device__ __forceinline__ half8 tr_frag_acc(const E* tile, int ld, int k0, int n0) {
+  static_assert(sizeof(E) == 2, "16-bit tiles only");
+  const int lane = threadIdx.x % kWave;
+  const int g = lane / 16, s = lane % 16, hf = lane / 32;
+  const int col = n0 + 16 * (g % 2) + 4 * (s % 4);
+  const int row = k0 + 4 * hf + s / 4;
+  s16x4 a = ds_read_tr16(tile + row * ld + col);
+  s16x4 b = ds_read_tr16(tile + (row + 8) * ld + col);
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(half8, r);
+}
+
+// Same, with the natural k order of the atom: lane l gets rows k0 + 8*hf + [0,8).
+template <class E>
+__device__ __forceinline__ half8 tr_frag(const E* tile, int ld, int k0, int n0) {
+  static_assert(sizeof(E) == 2, "16-bit tiles only");
+  const int lane = threadIdx.x % kWave;
+  const int g = lane / 16, s = lane % 16, hf = lane / 32;
+  const int col = n0 + 16 * (g % 2) + 4 * (s % 4);
+  const int row = k0 + 8 * hf + s / 4;
+  s16x4 a = ds_read_tr16(tile + row * ld + col);
+  s16x4 b = ds_read_tr16(tile + (row + 4) * ld + col);
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(half8, r);
+}
+
+// One 16-byte chunk of a [rows x cols] tile copied from global memory:
+// row r of the source starts at src + r*ld (elements), rows >= nrows read as 0.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <class T>
+__device__ __forceinline__ u32x4 load_chunk(const T* src, int64_t ld, int r, int c, int nrows) {
+  if (r < nrows) return *reinterpret_cast<const u32x4*>(src + r * ld + c);
+  return u32x4{0u, 0u, 0u, 0u};
+}
+
+template <class T>
+__device__ __forceinline__ void store_chunk(T* dst, int ld, int r, int c, u32x4 v) {
+  *reinterpret_cast<u32x4*>(dst + r * ld + c) = v;
+}
+
+}  // namespace laga

@@ -4,174 +4,142 @@
 //   s[t,u] = (q_nope || q_rope)[t,i] . (k_nope[u,i] || k_pe[u]) / sqrt(d_nope + d_rope), u <= t
 //   o[t,i] = sum_u softmax_u(s) v[u,i],   lse[i,t] = ln sum_u exp(s[t,u])
 //
-// Flash-style: one 256-thread workgroup owns BM = 128 queries of one head and
-// streams the keys 0 .. (last query of the tile) in blocks of BN = 64 through
-// LDS, with an online softmax, so no S x S score matrix ever exists.  Each
-// wavefront owns 32 queries and keeps them in registers as the B operand of
-//     S^T[key, query] = K . Q^T          (A = K rows from LDS)
-// so that the 32x32 accumulator layout puts one query per lane column: the row
-// statistics (running max, running sum) are lane-local up to one exchange with
-// the other half of the wavefront, and the probabilities already sit in the
-// layout of the B operand of
-//     O^T[dv, query] += V^T . P^T        (A = V^T from LDS, key-permuted)
-// The k_pe band is staged once per key block and serves every query of the
-// tile; it is never expanded per head.  Blocks that lie entirely above a
-// wavefront's diagonal are skipped; only blocks crossing it are masked.
+// Flash-style: a workgroup of NW wavefronts owns BM = 32*NW queries of one
+// head and streams keys 0 .. (last query of the tile) in blocks of BN = 64
+// through double-buffered LDS (the next block's global loads are in flight in
+// registers while the current one is computed), with an online softmax, so no
+// S x S matrix ever exists.  Each wavefront keeps its 32 queries in registers
+// as the B operand of
+//     S^T[key, query] = K . Q^T          (A = K rows, 16-byte LDS reads)
+// so that the 32x32 accumulators hold one query per lane column: the running
+// max / sum are lane-local up to one exchange between wavefront halves, and
+// the probabilities already sit in the B-operand layout of
+//     O^T[dv, query] += V^T . P^T        (A = V^T via transposing LDS reads)
+// K, k_pe and V are staged as plain 16-byte copies in their storage layout:
+// the rope band stays bf16 and meets q_rope in bf16 MFMAs (both exact), the
+// nope part meets q_nope (converted once to fp16, exactly) in fp16 MFMAs.
+// The k_pe band is staged once per key block for all queries of the tile and
+// never expanded per head.  Blocks above a wavefront's diagonal are skipped;
+// only blocks crossing it are masked.
 //
-// Precision: SPLIT == 1 feeds fp16 operands (bf16 q / k_pe convert exactly);
-// SPLIT == 2 stores K/V as float32 and feeds K, V and P as fp16 hi + lo pairs
-// (S = Q.K_hi + Q.K_lo, O = P_hi V_hi + P_hi V_lo + P_lo V_hi), fp32-class.
+// Precision: NS == 1 uses single fp16 K, V and P.  NS == 2 reads K and V as
+// fp16 hi/lo planes (as laga_kv_up writes them) and splits P:
+// S = Q.K_hi + Q.K_lo, O = P_hi V_hi + P_hi V_lo + P_lo V_hi (fp32-class).
 // The float32 instantiation uses fp32 MFMAs throughout.
-#include "device.hpp"
+#include "attn_common.hpp"
 #include "launch.hpp"
 
 namespace laga {
 namespace {
 
-constexpr int BM = 128;  // queries per workgroup (4 wavefronts x 32)
-constexpr int BN = 64;   // keys per block
-constexpr int kThreads = 256;
-
-template <class M> struct AttnPad { static constexpr int v = 8; };
-template <> struct AttnPad<MmaF32> { static constexpr int v = 1; };
+constexpr int BN = 64;  // keys per block
 
 struct FwdArgs {
   const void* q; const void* k_nope; const void* k_pe; const void* v;
   float* o; float* lse;
-  int64_t S; int B, h, n_qt; float scale_log2;
+  int64_t S, plane_k, plane_v; int B, h, n_qt; float scale_log2;
 };
 
-template <class InT, class KvT, class M, int SPLIT, int DN, int DR, int DV>
-struct FwdKernel {
+template <class M> struct Pads { static constexpr int k = 8, r = 8, v = 16; };
+template <> struct Pads<MmaF32> { static constexpr int k = 4, r = 4, v = 4; };
+
+// M: K/V/P operand type (fp16 or fp32); MR: rope operand type (bf16 or fp32);
+// InT: storage type of q and k_pe.
+template <class InT, class M, class MR, int NS, int DN, int DR, int DV, int NW>
+struct Fwd {
   typedef typename M::elem E;
-  static constexpr int DQK = DN + DR;
-  static constexpr int PAD = AttnPad<M>::v;
-  static constexpr int LDK = DQK + PAD;   // hi plane: nope + rope
-  static constexpr int LDKL = DN + PAD;   // lo plane: nope only
-  static constexpr int LDV = BN + PAD;    // V^T rows (one per dv)
-  static constexpr int NT = BN / 32;      // S^T atoms per wavefront per block
-  static constexpr int NO = DV / 32;      // O^T atoms
-  static constexpr int KS_QK = DQK / M::K;
-  static constexpr int KS_NOPE = DN / M::K;
-  static constexpr int PV_STEPS = 32 / M::K;  // MFMA steps per 32-key atom
-  static constexpr int LDS_K = BN * LDK;
-  static constexpr int LDS_KL = (SPLIT == 2) ? BN * LDKL : 0;
-  static constexpr int LDS_V = SPLIT * DV * LDV;
-  static constexpr int LDS_ELEMS = LDS_K + LDS_KL + LDS_V;
+  typedef typename MR::elem ER;
+  typedef typename M::frag F;
+  typedef typename MR::frag FR;
+  static constexpr int NT = NW * kWave;
+  static constexpr int BM = 32 * NW;
+  static constexpr int LDK = DN + Pads<M>::k, LDR = DR + Pads<M>::r, LDV = DV + Pads<M>::v;
+  // LDS buffer: NS K planes | rope band | NS V planes (element offsets of E; rope in ER).
+  static constexpr int K_ELEMS = NS * BN * LDK;
+  static constexpr int R_BYTES = BN * LDR * sizeof(ER);
+  static constexpr int V_ELEMS = NS * BN * LDV;
+  static constexpr int BUF_BYTES = (K_ELEMS + V_ELEMS) * sizeof(E) + R_BYTES;
+  static constexpr int LDS_BYTES = 2 * BUF_BYTES;
+  // 16-byte chunks per block.
+  static constexpr int EPC = 16 / sizeof(E), RPC = 16 / sizeof(ER);
+  static constexpr int K_CH = NS * BN * DN / EPC, R_CH = BN * DR / RPC, V_CH = NS * BN * DV / EPC;
+  static constexpr int ALL_CH = K_CH + R_CH + V_CH;
+  static constexpr int CH = (ALL_CH + NT - 1) / NT;
+  static constexpr int KS_N = DN / M::K, KS_R = DR / MR::K, NO = DV / 32, PV_STEPS = 32 / M::K;
+  static_assert(DN % M::K == 0 && DR % MR::K == 0 && DV % 32 == 0, "head dims");
 
-  // Staging of one key block: global -> registers (prefetch) -> LDS.
-  static constexpr int KVEC = 16 / sizeof(KvT);                 // KvT per 16-byte load
-  static constexpr int PVEC = 16 / sizeof(InT);                 // k_pe per 16-byte load
-  static constexpr int K_ITEMS = BN * DN / KVEC;
-  static constexpr int P_ITEMS = BN * DR / PVEC;
-  static constexpr int V_ITEMS = (BN / 4) * (DV / KVEC);        // 4 keys x KVEC dv each
-  static constexpr int K_PER = (K_ITEMS + kThreads - 1) / kThreads;
-  static constexpr int P_PER = (P_ITEMS + kThreads - 1) / kThreads;
-  static constexpr int V_PER = (V_ITEMS + kThreads - 1) / kThreads;
-  typedef KvT kvec __attribute__((ext_vector_type(KVEC)));
-  typedef InT pvec __attribute__((ext_vector_type(PVEC)));
-
-  struct Regs {
-    kvec k[K_PER];
-    pvec p[P_PER];
-    kvec v[V_PER][4];
-  };
+  struct Regs { u32x4 c[CH]; };
 
   __device__ static void load_block(const FwdArgs& a, int b, int head, int64_t key0, Regs& R) {
-    const KvT* kn = static_cast<const KvT*>(a.k_nope);
-    const InT* kp = static_cast<const InT*>(a.k_pe);
-    const KvT* vv = static_cast<const KvT*>(a.v);
-    const int tid = threadIdx.x;
+    const E* kn = static_cast<const E*>(a.k_nope);
+    const ER* kp = static_cast<const ER*>(a.k_pe);
+    const E* vg = static_cast<const E*>(a.v);
+    const int nk = static_cast<int>(a.S - key0 < BN ? a.S - key0 : BN);
 #pragma unroll
-    for (int j = 0; j < K_PER; ++j) {
-      const int it = j * kThreads + tid;
-      const int key = it / (DN / KVEC), c = (it % (DN / KVEC)) * KVEC;
-      const int64_t u = key0 + key;
-      if (it < K_ITEMS && u < a.S)
-        R.k[j] = *reinterpret_cast<const kvec*>(kn + ((b * a.S + u) * a.h + head) * DN + c);
-      else
-        R.k[j] = kvec{};
+    for (int i = 0; i < CH; ++i) {
+      int c = i * NT + static_cast<int>(threadIdx.x);
+      u32x4 val{0u, 0u, 0u, 0u};
+      if (c < K_CH) {
+        const int p = c / (BN * DN / EPC), rem = c % (BN * DN / EPC);
+        const int r = rem / (DN / EPC), j = rem % (DN / EPC);
+        val = load_chunk(kn + p * a.plane_k + ((b * a.S + key0) * a.h + head) * DN, int64_t(a.h) * DN, r, j * EPC, nk);
+      } else if (c < K_CH + R_CH) {
+        c -= K_CH;
+        const int r = c / (DR / RPC), j = c % (DR / RPC);
+        val = load_chunk(kp + (b * a.S + key0) * DR, DR, r, j * RPC, nk);
+      } else if (c < ALL_CH) {
+        c -= K_CH + R_CH;
+        const int p = c / (BN * DV / EPC), rem = c % (BN * DV / EPC);
+        const int r = rem / (DV / EPC), j = rem % (DV / EPC);
+        val = load_chunk(vg + p * a.plane_v + ((b * a.S + key0) * a.h + head) * DV, int64_t(a.h) * DV, r, j * EPC, nk);
+      }
+      R.c[i] = val;
     }
+  }
+
+  __device__ static void store_block(const Regs& R, char* buf) {
+    E* Ks = reinterpret_cast<E*>(buf);
+    ER* Kr = reinterpret_cast<ER*>(buf + K_ELEMS * sizeof(E));
+    E* Vs = reinterpret_cast<E*>(buf + K_ELEMS * sizeof(E) + R_BYTES);
 #pragma unroll
-    for (int j = 0; j < P_PER; ++j) {
-      const int it = j * kThreads + tid;
-      const int key = it / (DR / PVEC), c = (it % (DR / PVEC)) * PVEC;
-      const int64_t u = key0 + key;
-      if (it < P_ITEMS && u < a.S)
-        R.p[j] = *reinterpret_cast<const pvec*>(kp + (b * a.S + u) * DR + c);
-      else
-        R.p[j] = pvec{};
-    }
-#pragma unroll
-    for (int j = 0; j < V_PER; ++j) {
-      const int it = j * kThreads + tid;
-      const int kg = it / (DV / KVEC), c = (it % (DV / KVEC)) * KVEC;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t u = key0 + kg * 4 + r;
-        if (it < V_ITEMS && u < a.S)
-          R.v[j][r] = *reinterpret_cast<const kvec*>(vv + ((b * a.S + u) * a.h + head) * DV + c);
-        else
-          R.v[j][r] = kvec{};
+    for (int i = 0; i < CH; ++i) {
+      int c = i * NT + static_cast<int>(threadIdx.x);
+      if (c < K_CH) {
+        const int p = c / (BN * DN / EPC), rem = c % (BN * DN / EPC);
+        store_chunk(Ks + p * BN * LDK, LDK, rem / (DN / EPC), (rem % (DN / EPC)) * EPC, R.c[i]);
+      } else if (c < K_CH + R_CH) {
+        c -= K_CH;
+        store_chunk(Kr, LDR, c / (DR / RPC), (c % (DR / RPC)) * RPC, R.c[i]);
+      } else if (c < ALL_CH) {
+        c -= K_CH + R_CH;
+        const int p = c / (BN * DV / EPC), rem = c % (BN * DV / EPC);
+        store_chunk(Vs + p * BN * LDV, LDV, rem / (DV / EPC), (rem % (DV / EPC)) * EPC, R.c[i]);
       }
     }
   }
 
-  __device__ static void store_block(const Regs& R, E* lds) {
-    E* Ks = lds;
-    E* Kl = lds + LDS_K;
-    E* Vt = lds + LDS_K + LDS_KL;
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int j = 0; j < K_PER; ++j) {
-      const int it = j * kThreads + tid;
-      if (it >= K_ITEMS) continue;
-      const int key = it / (DN / KVEC), c = (it % (DN / KVEC)) * KVEC;
-#pragma unroll
-      for (int e = 0; e < KVEC; ++e) {
-        E part[SPLIT];
-        split_to<M, SPLIT>(to_f32(R.k[j][e]), part);
-        Ks[key * LDK + c + e] = part[0];
-        if constexpr (SPLIT == 2) Kl[key * LDKL + c + e] = part[1];
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < P_PER; ++j) {
-      const int it = j * kThreads + tid;
-      if (it >= P_ITEMS) continue;
-      const int key = it / (DR / PVEC), c = (it % (DR / PVEC)) * PVEC;
-#pragma unroll
-      for (int e = 0; e < PVEC; ++e) Ks[key * LDK + DN + c + e] = M::from_f32(to_f32(R.p[j][e]));
-    }
-#pragma unroll
-    for (int j = 0; j < V_PER; ++j) {
-      const int it = j * kThreads + tid;
-      if (it >= V_ITEMS) continue;
-      const int kg = it / (DV / KVEC), c = (it % (DV / KVEC)) * KVEC;
-      const int col = acc_key_col(kg * 4);  // 4 consecutive keys stay contiguous
-#pragma unroll
-      for (int e = 0; e < KVEC; ++e) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          E part[SPLIT];
-          split_to<M, SPLIT>(to_f32(R.v[j][r][e]), part);
-#pragma unroll
-          for (int s = 0; s < SPLIT; ++s) Vt[s * DV * LDV + (c + e) * LDV + col + r] = part[s];
-        }
-      }
+  // A operand of O^T += V^T P^T for one MFMA step: rows dv n0 + lane%32, keys of
+  // accumulator registers st*KPL .. of 32-key atom t (see acc_key_col).
+  __device__ static F v_frag(const E* Vp, int t, int st, int n0) {
+    if constexpr (M::KPL == 8) {
+      return tr_frag_acc(Vp, LDV, t * 32 + st * 16, n0);
+    } else {
+      const int lane = threadIdx.x % kWave;
+      const int key = t * 32 + 8 * (st / 4) + 4 * (lane / 32) + (st % 4);
+      return Vp[key * LDV + n0 + lane % 32];
     }
   }
 
-  __device__ static void run(const FwdArgs& a, E* lds) {
+  __device__ static void run(const FwdArgs& a, char* lds) {
     const int lane = threadIdx.x % kWave;
     const int wv = threadIdx.x / kWave;
     const int hf = lane / 32;
     const int col = lane % 32;
 
-    // Workgroup -> (batch*head, query tile).  Heads are grouped per XCD
-    // (workgroup ids are dealt round-robin to the 8 XCDs) so that the
-    // workgroups sharing a head's K/V stream share one L2; within an XCD the
-    // longest (latest) query tiles go first.
+    // Workgroup -> (batch*head, query tile).  Workgroup ids are dealt
+    // round-robin to the 8 XCDs; heads are grouped per XCD so the workgroups
+    // streaming one head's K/V share an L2, and within an XCD the longest
+    // (latest) query tiles start first.
     const int nbh = a.B * a.h;
     int bh, qt_rank;
     if (nbh % 8 == 0) {
@@ -185,19 +153,27 @@ struct FwdKernel {
     const int qt = a.n_qt - 1 - qt_rank;
     const int b = bh / a.h, head = bh % a.h;
     const int64_t q0 = static_cast<int64_t>(qt) * BM;
-    const int64_t qw = q0 + wv * 32;       // first query of this wavefront
-    const int64_t tq = qw + col;           // this lane's query
+    const int64_t qw = q0 + wv * 32;
+    const int64_t tq = qw + col;
+    const bool qvalid = tq < a.S;
 
     // Q fragments (B operand): query tq, dims hf*KPL + s*K + [0, KPL).
-    const InT* qp = static_cast<const InT*>(a.q);
-    typename M::frag qf[KS_QK];
+    const InT* qp = static_cast<const InT*>(a.q) + ((b * a.S + (qvalid ? tq : 0)) * a.h + head) * (DN + DR);
+    F qn[KS_N];
+    FR qr[KS_R];
 #pragma unroll
-    for (int s = 0; s < KS_QK; ++s) {
+    for (int s = 0; s < KS_N; ++s) {
       E tmp[M::KPL];
 #pragma unroll
-      for (int j = 0; j < M::KPL; ++j)
-        tmp[j] = M::from_f32(tq < a.S ? to_f32(qp[((b * a.S + tq) * a.h + head) * DQK + s * M::K + hf * M::KPL + j]) : 0.f);
-      qf[s] = *reinterpret_cast<typename M::frag*>(tmp);
+      for (int j = 0; j < M::KPL; ++j) tmp[j] = M::from_f32(qvalid ? to_f32(qp[s * M::K + hf * M::KPL + j]) : 0.f);
+      qn[s] = *reinterpret_cast<F*>(tmp);
+    }
+#pragma unroll
+    for (int s = 0; s < KS_R; ++s) {
+      ER tmp[MR::KPL];
+#pragma unroll
+      for (int j = 0; j < MR::KPL; ++j) tmp[j] = qvalid ? qp[DN + s * MR::K + hf * MR::KPL + j] : ER{};
+      qr[s] = *reinterpret_cast<FR*>(tmp);
     }
 
     f32x16 o[NO];
@@ -215,96 +191,97 @@ struct FwdKernel {
     load_block(a, b, head, 0, R);
     for (int kb = 0; kb < nkb; ++kb) {
       const int64_t key0 = static_cast<int64_t>(kb) * BN;
-      __syncthreads();
-      store_block(R, lds);
+      char* buf = lds + (kb & 1) * BUF_BYTES;
+      store_block(R, buf);
       __syncthreads();
       if (kb + 1 < nkb) load_block(a, b, head, key0 + BN, R);
       if (key0 > qw + 31) continue;  // whole block above this wavefront's diagonal
 
-      const E* Ks = lds;
-      const E* Kl = lds + LDS_K;
-      const E* Vt = lds + LDS_K + LDS_KL;
+      const E* Ks = reinterpret_cast<const E*>(buf);
+      const ER* Kr = reinterpret_cast<const ER*>(buf + K_ELEMS * sizeof(E));
+      const E* Vs = reinterpret_cast<const E*>(buf + K_ELEMS * sizeof(E) + R_BYTES);
 
-      f32x16 sc[NT];
+      f32x16 sc[2];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
+      for (int t = 0; t < 2; ++t) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sc[t][r] = 0.f;
-        const E* krow = Ks + (t * 32 + col) * LDK + hf * M::KPL;
+        const int krow = t * 32 + col;
 #pragma unroll
-        for (int s = 0; s < KS_QK; ++s) sc[t] = M::mma(lds_frag<M>(krow + s * M::K), qf[s], sc[t]);
-        if constexpr (SPLIT == 2) {
-          const E* lrow = Kl + (t * 32 + col) * LDKL + hf * M::KPL;
-#pragma unroll
-          for (int s = 0; s < KS_NOPE; ++s) sc[t] = M::mma(lds_frag<M>(lrow + s * M::K), qf[s], sc[t]);
+        for (int s = 0; s < KS_N; ++s) {
+          sc[t] = M::mma(lds_frag<M>(Ks + krow * LDK + s * M::K + hf * M::KPL), qn[s], sc[t]);
+          if constexpr (NS == 2)
+            sc[t] = M::mma(lds_frag<M>(Ks + BN * LDK + krow * LDK + s * M::K + hf * M::KPL), qn[s], sc[t]);
         }
+#pragma unroll
+        for (int s = 0; s < KS_R; ++s)
+          sc[t] = MR::mma(lds_frag<MR>(Kr + krow * LDR + s * MR::K + hf * MR::KPL), qr[s], sc[t]);
       }
 
-      // Scale into the log2 domain and mask keys past this lane's query.
+      // Row max of the raw scores (scale > 0 is folded into the exponent).
       const bool diag = key0 + BN - 1 > qw;
       float mloc = -INFINITY;
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float x = sc[t][r] * a.scale_log2;
           if (diag) {
             const int64_t u = key0 + t * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
-            if (u > tq) x = -INFINITY;
+            if (u > tq) sc[t][r] = -INFINITY;
           }
-          sc[t][r] = x;
-          mloc = fmaxf(mloc, x);
+          mloc = fmaxf(mloc, sc[t][r]);
         }
       mloc = fmaxf(mloc, swap_halves(mloc));
-      const float m_new = fmaxf(m_run, mloc);
-      const float alpha = exp2f(m_run - m_new);
+      const float m_new = fmaxf(m_run, mloc * a.scale_log2);
       float lsum = 0.f;
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = exp2f(sc[t][r] - m_new);
+          const float p = exp2f(fmaf(sc[t][r], a.scale_log2, -m_new));
           sc[t][r] = p;
           lsum += p;
         }
       lsum += swap_halves(lsum);
-      l_run = l_run * alpha + lsum;
+      if (__any(m_new != m_run)) {
+        const float alpha = exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int n = 0; n < NO; ++n)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[n][r] *= alpha;
+      }
+      l_run += lsum;
       m_run = m_new;
-#pragma unroll
-      for (int n = 0; n < NO; ++n)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[n][r] *= alpha;
 
-      // O^T += V^T P^T, one step covers K keys; accumulator r = step*KPL + j.
+      // O^T += V^T P^T; one step covers K keys, accumulator r = st*KPL + j.
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int st = 0; st < PV_STEPS; ++st) {
           E ph[M::KPL], pl[M::KPL];
 #pragma unroll
           for (int j = 0; j < M::KPL; ++j) {
-            E part[SPLIT];
-            split_to<M, SPLIT>(sc[t][st * M::KPL + j], part);
+            E part[NS];
+            split_to<M, NS>(sc[t][st * M::KPL + j], part);
             ph[j] = part[0];
-            if constexpr (SPLIT == 2) pl[j] = part[1];
+            if constexpr (NS == 2) pl[j] = part[1];
           }
-          const typename M::frag pfh = *reinterpret_cast<typename M::frag*>(ph);
-          const int r0 = st * M::KPL;
-          const int kcol = acc_key_col(t * 32 + 8 * (r0 / 4) + 4 * hf + (r0 % 4));
+          const F pfh = *reinterpret_cast<F*>(ph);
 #pragma unroll
           for (int n = 0; n < NO; ++n) {
-            const E* vrow = Vt + (n * 32 + col) * LDV + kcol;
-            o[n] = M::mma(lds_frag<M>(vrow), pfh, o[n]);
-            if constexpr (SPLIT == 2) {
-              const typename M::frag pfl = *reinterpret_cast<typename M::frag*>(pl);
-              o[n] = M::mma(lds_frag<M>(vrow + DV * LDV), pfh, o[n]);
-              o[n] = M::mma(lds_frag<M>(vrow), pfl, o[n]);
+            const F vh = v_frag(Vs, t, st, n * 32);
+            o[n] = M::mma(vh, pfh, o[n]);
+            if constexpr (NS == 2) {
+              const F pfl = *reinterpret_cast<F*>(pl);
+              o[n] = M::mma(v_frag(Vs + BN * LDV, t, st, n * 32), pfh, o[n]);
+              o[n] = M::mma(vh, pfl, o[n]);
             }
           }
         }
     }
 
-    if (tq < a.S) {
+    if (qvalid) {
       const float inv = 1.0f / l_run;
       float* op = a.o + ((b * a.S + tq) * a.h + head) * DV;
 #pragma unroll
@@ -314,29 +291,33 @@ struct FwdKernel {
           f32x4 w = {o[n][4 * g] * inv, o[n][4 * g + 1] * inv, o[n][4 * g + 2] * inv, o[n][4 * g + 3] * inv};
           *reinterpret_cast<f32x4*>(op + n * 32 + 8 * g + 4 * hf) = w;
         }
-      if (hf == 0) a.lse[(static_cast<int64_t>(b) * a.h + head) * a.S + tq] = (m_run + log2f(l_run)) * 0.69314718055994531f;
+      if (hf == 0)
+        a.lse[(static_cast<int64_t>(b) * a.h + head) * a.S + tq] = (m_run + log2f(l_run)) * 0.69314718055994531f;
     }
   }
 };
 
-template <class InT, class KvT, class M, int SPLIT, int DN, int DR, int DV>
-__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
-  typedef FwdKernel<InT, KvT, M, SPLIT, DN, DR, DV> Kn;
-  __shared__ __attribute__((aligned(16))) typename M::elem lds[Kn::LDS_ELEMS];
+template <class InT, class M, class MR, int NS, int DN, int DR, int DV, int NW>
+__global__ __launch_bounds__(NW * kWave) void attn_fwd_kernel(FwdArgs a) {
+  typedef Fwd<InT, M, MR, NS, DN, DR, DV, NW> Kn;
+  __shared__ __attribute__((aligned(16))) char lds[Kn::LDS_BYTES];
   Kn::run(a, lds);
 }
 
-template <class InT, class KvT, class M, int SPLIT, int DN, int DR, int DV>
+template <class InT, class M, class MR, int NS, int DN, int DR, int DV, int NW>
 hipError_t fwd_t(const Shape& s, const void* q, const void* kn, const void* kp, const void* v, float* o,
                  float* lse, hipStream_t st) {
+  typedef Fwd<InT, M, MR, NS, DN, DR, DV, NW> Kn;
   FwdArgs a;
   a.q = q; a.k_nope = kn; a.k_pe = kp; a.v = v; a.o = o; a.lse = lse;
   a.S = s.S; a.B = static_cast<int>(s.B); a.h = s.h;
-  a.n_qt = static_cast<int>((s.S + BM - 1) / BM);
+  a.plane_k = s.T * s.h * DN;
+  a.plane_v = s.T * s.h * DV;
+  a.n_qt = static_cast<int>((s.S + Kn::BM - 1) / Kn::BM);
   a.scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(DN + DR));
   const int64_t grid = static_cast<int64_t>(a.n_qt) * s.B * s.h;
-  hipLaunchKernelGGL((attn_fwd_kernel<InT, KvT, M, SPLIT, DN, DR, DV>), dim3(static_cast<unsigned>(grid)),
-                     dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<InT, M, MR, NS, DN, DR, DV, NW>), dim3(static_cast<unsigned>(grid)),
+                     dim3(Kn::NT), 0, st, a);
   return hipGetLastError();
 }
 
@@ -345,11 +326,11 @@ hipError_t fwd_t(const Shape& s, const void* q, const void* kn, const void* kp, 
 hipError_t launch_attn_fwd(const Shape& s, const void* q, const void* kn, const void* kp, const void* v,
                            float* o, float* lse, hipStream_t st) {
   if (s.bf16 && s.d_nope == 128 && s.d_rope == 64 && s.d_v == 128) {
-    if (s.split) return fwd_t<bf16_t, float, MmaF16, 2, 128, 64, 128>(s, q, kn, kp, v, o, lse, st);
-    return fwd_t<bf16_t, half_t, MmaF16, 1, 128, 64, 128>(s, q, kn, kp, v, o, lse, st);
+    if (s.split) return fwd_t<bf16_t, MmaF16, MmaBf16, 2, 128, 64, 128, 8>(s, q, kn, kp, v, o, lse, st);
+    return fwd_t<bf16_t, MmaF16, MmaBf16, 1, 128, 64, 128, 8>(s, q, kn, kp, v, o, lse, st);
   }
   if (!s.bf16 && s.d_nope == 32 && s.d_rope == 16 && s.d_v == 32)
-    return fwd_t<float, float, MmaF32, 1, 32, 16, 32>(s, q, kn, kp, v, o, lse, st);
+    return fwd_t<float, MmaF32, MmaF32, 1, 32, 16, 32, 4>(s, q, kn, kp, v, o, lse, st);
   return hipErrorInvalidValue;
 }
 

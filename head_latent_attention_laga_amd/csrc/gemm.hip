@@ -109,14 +109,26 @@ struct LoadNormRC {
 };
 
 // ----------------------------------------------------------------- epilogues
-template <class KvT>
-struct EpiKvUp {  // n = i*C + c -> k_nope[t,i,c] or v[t,i,c-d_nope]
-  KvT* kn; KvT* v; int64_t M; int N, C, dn, dv, h;
+// n = i*C + c -> k_nope[t,i,c] or v[t,i,c-d_nope]; with NS == 2 the value is
+// written as an fp16 hi part in plane 0 and the fp16 rest in plane 1.
+template <class KvT, int NS>
+struct EpiKvUp {
+  KvT* kn; KvT* v; int64_t M; int N, C, dn, dv, h; int64_t plane_k, plane_v;
   __device__ void operator()(int64_t m, int n, float val) const {
     if (m >= M || n >= N) return;
     const int i = n / C, c = n - i * C;
-    if (c < dn) kn[(m * h + i) * dn + c] = static_cast<KvT>(val);
-    else v[(m * h + i) * dv + (c - dn)] = static_cast<KvT>(val);
+    KvT part[NS];
+    if constexpr (NS == 1) {
+      part[0] = static_cast<KvT>(val);
+    } else {
+      part[0] = static_cast<KvT>(val);
+      part[1] = static_cast<KvT>(val - static_cast<float>(part[0]));
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (c < dn) kn[s * plane_k + (m * h + i) * dn + c] = part[s];
+      else v[s * plane_v + (m * h + i) * dv + (c - dn)] = part[s];
+    }
   }
 };
 
@@ -295,19 +307,20 @@ hipError_t launch_kv_up(const Shape& s, const float* L, const void* w, void* k_n
   if (s.bf16) {
     LoadInKC<bf16_t> lb{static_cast<const bf16_t*>(w) + static_cast<int64_t>(s.head_lo) * s.C() * s.d_kv,
                         s.d_kv, N, s.d_kv};
+    const int64_t pk = s.T * s.h * s.d_nope, pv = s.T * s.h * s.d_v;
     if (s.split) {
-      EpiKvUp<float> e{static_cast<float*>(k_nope), static_cast<float*>(v), s.T, static_cast<int>(N),
-                       s.C(), s.d_nope, s.d_v, s.h};
+      EpiKvUp<half_t, 2> e{static_cast<half_t*>(k_nope), static_cast<half_t*>(v), s.T, static_cast<int>(N),
+                           s.C(), s.d_nope, s.d_v, s.h, pk, pv};
       return run_gemm<MmaBf16, 2, 1>(la, lb, e, s.T, N, s.d_kv, 1, st);
     }
-    EpiKvUp<half_t> e{static_cast<half_t*>(k_nope), static_cast<half_t*>(v), s.T, static_cast<int>(N),
-                      s.C(), s.d_nope, s.d_v, s.h};
+    EpiKvUp<half_t, 1> e{static_cast<half_t*>(k_nope), static_cast<half_t*>(v), s.T, static_cast<int>(N),
+                         s.C(), s.d_nope, s.d_v, s.h, pk, pv};
     return run_gemm<MmaBf16, 2, 1>(la, lb, e, s.T, N, s.d_kv, 1, st);
   }
   LoadInKC<float> lb{static_cast<const float*>(w) + static_cast<int64_t>(s.head_lo) * s.C() * s.d_kv,
                      s.d_kv, N, s.d_kv};
-  EpiKvUp<float> e{static_cast<float*>(k_nope), static_cast<float*>(v), s.T, static_cast<int>(N),
-                   s.C(), s.d_nope, s.d_v, s.h};
+  EpiKvUp<float, 1> e{static_cast<float*>(k_nope), static_cast<float*>(v), s.T, static_cast<int>(N),
+                      s.C(), s.d_nope, s.d_v, s.h, 0, 0};
   return run_gemm<MmaF32, 1, 1>(la, lb, e, s.T, N, s.d_kv, 1, st);
 }
 

@@ -25,7 +25,11 @@ class LagaPath:
         kvb = _lib.kv_elem_bytes(self.dims)
         if kvb == 0:
             raise _lib.LagaError("laga_kv_elem_bytes", 2, "dims rejected")
-        self.kv_dtype = torch.float16 if kvb == 2 else torch.float32
+        # k_nope / v storage: [planes, B, S, h, d]; bf16 inputs store fp16 (two
+        # planes hi, lo with split operands), float32 inputs one float32 plane.
+        bf16 = dtype == "bf16"
+        self.kv_dtype = torch.float16 if bf16 else torch.float32
+        self.kv_planes = kvb // 2 if bf16 else 1
 
     def _empty(self, shape, dtype=torch.float32):
         return torch.empty(shape, dtype=dtype, device=self.device)
@@ -34,8 +38,8 @@ class LagaPath:
         B, S, h = self.B, self.S, self.h
         return dict(
             latent_n=self._empty((B, S, self.d_kv)), rstd=self._empty((B, S)),
-            k_nope=self._empty((B, S, h, self.d_nope), self.kv_dtype),
-            v=self._empty((B, S, h, self.d_v), self.kv_dtype),
+            k_nope=self._empty((self.kv_planes, B, S, h, self.d_nope), self.kv_dtype),
+            v=self._empty((self.kv_planes, B, S, h, self.d_v), self.kv_dtype),
             o=self._empty((B, S, h, self.d_v)), lse=self._empty((B, h, S)))
 
     def forward(self, x, out=None, stream=None):
@@ -45,6 +49,11 @@ class LagaPath:
         _lib.kv_up(self.dims, out["latent_n"], x["w_kv_b"], out["k_nope"], out["v"], stream)
         _lib.attn_fwd(self.dims, x["q"], out["k_nope"], x["k_pe"], out["v"], out["o"], out["lse"], stream)
         return out
+
+    @staticmethod
+    def kv_value(t):
+        """The value a k_nope / v buffer holds: the sum of its planes, as float32."""
+        return t.float().sum(0)
 
     def alloc_backward(self):
         B, S, h = self.B, self.S, self.h

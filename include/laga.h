@@ -35,8 +35,12 @@
  *                                    then the d_v V rows; rows of H_r are read
  *   q        [B, S, h, d_qk] in      nope part first, rope part already rotated
  *   k_pe     [B, S, d_rope] in       one band shared by every head
- *   k_nope   [B, S, h, d_nope] kv    kv element type, see laga_kv_elem_bytes
- *   v        [B, S, h, d_v]    kv
+ *   k_nope   [P, B, S, h, d_nope] kv  P value planes, see below
+ *   v        [P, B, S, h, d_v]    kv
+ * K/V storage ("kv"): float32 with P = 1 for LAGA_F32; fp16 with P = 1 for
+ * LAGA_BF16 + LAGA_OPERANDS_FP16; fp16 with P = 2 for LAGA_BF16 +
+ * LAGA_OPERANDS_SPLIT, where plane 0 holds hi = fp16(x) and plane 1 holds
+ * fp16(x - hi), the value being their sum.
  *   o        [B, S, h, d_v]  float32
  *   lse      [B, h, S]       float32 natural-log sum of exp(scores) per query
  */
@@ -65,7 +69,7 @@ typedef enum { LAGA_F32 = 0, LAGA_BF16 = 1 } laga_dtype;
  * Operand precision of the matrix-core contractions for LAGA_BF16 inputs.
  *  LAGA_OPERANDS_FP16:  K/V are stored as fp16; scores, probabilities and V
  *                       enter the MFMAs as single fp16 values (fp32 accumulate).
- *  LAGA_OPERANDS_SPLIT: K/V are stored as float32 and every computed operand
+ *  LAGA_OPERANDS_SPLIT: K/V are stored as fp16 hi/lo planes and every computed operand
  *                       (L, K, V, P, dS, and the fold operands) enters the
  *                       MFMAs as a hi+lo pair of fp16/bf16 values, giving
  *                       fp32-class results at 2-3x the matrix-core work.
@@ -98,8 +102,9 @@ typedef struct {
  * magnitude.
  */
 
-/* Bytes per element of k_nope / v for these dims: 2 (fp16) or 4 (float32).
- * Returns 0 when the dims are invalid or unsupported. */
+/* Bytes per logical element of k_nope / v for these dims, all planes counted:
+ * 2 (one fp16 plane) or 4 (two fp16 planes, or one float32 plane).  Returns 0
+ * when the dims are invalid or unsupported. */
 size_t laga_kv_elem_bytes(const laga_dims* dims);
 
 /*

@@ -35,6 +35,11 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
+def kv_host(t: torch.Tensor) -> np.ndarray:
+    """Value of a k_nope / v buffer ([planes, B, S, h, d]) in fp64."""
+    return t.detach().float().cpu().numpy().astype(np.float64).sum(0)
+
+
 def err(got: np.ndarray, ref: np.ndarray) -> tuple[float, float]:
     assert got.shape == ref.shape, (got.shape, ref.shape)
     assert np.all(np.isfinite(got)), "non-finite values in GPU output"

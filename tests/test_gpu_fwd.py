@@ -11,7 +11,7 @@ import torch
 
 import laga_inputs as li
 import oracle
-from gpu_util import FP16, SPLIT, announce, check, device_inputs, host, make_path, sample_rows
+from gpu_util import FP16, SPLIT, announce, check, device_inputs, host, kv_host, make_path, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -39,8 +39,8 @@ def _full_forward_check(d: li.Dims, precision: int, seed: int = 0):
                          sp_size=d.sp_size, sp_rank=d.sp_rank, d_nope=d.d_nope, eps=d.eps)
     check("L", host(out["latent_n"]), ref["L"], d.dtype)
     check("rstd", host(out["rstd"]), ref["rstd"], li.F32 if d.dtype == li.F32 else d.dtype)
-    check("k_nope", host(out["k_nope"]), ref["k_nope"], d.dtype)
-    check("v", host(out["v"]), ref["v"], d.dtype)
+    check("k_nope", kv_host(out["k_nope"]), ref["k_nope"], d.dtype)
+    check("v", kv_host(out["v"]), ref["v"], d.dtype)
     check("o", host(out["o"]), ref["O"], d.dtype)
     check("lse", host(out["lse"]), ref["lse"], d.dtype)
     return out
@@ -82,8 +82,8 @@ def test_full_size_workloads(name, precision):
     check("rstd", host(out["rstd"]), rstd, d.dtype)
     kn, vv = oracle.kv_up(L, v["w_kv_b"], heads, d.d_nope)
     del L
-    check("k_nope", host(out["k_nope"]), kn, d.dtype)
-    check("v", host(out["v"]), vv, d.dtype)
+    check("k_nope", kv_host(out["k_nope"]), kn, d.dtype)
+    check("v", kv_host(out["v"]), vv, d.dtype)
     rows = sample_rows(d.S)
     O, lse = oracle.attention_fwd_rows(v["q"], kn, v["k_pe"], vv, rows)
     check("o[rows]", host(out["o"])[:, rows], O, d.dtype)
