@@ -5,20 +5,24 @@
 //   o[t,i] = sum_u softmax_u(s) v[u,i],   lse[i,t] = ln sum_u exp(s[t,u])
 //
 // Flash-style: a workgroup of NW wavefronts owns BM = 32*NW queries of one
-// head and streams keys 0 .. (last query of the tile) in blocks of BN = 64
-// through double-buffered LDS (the next block's global loads are in flight in
-// registers while the current one is computed), with an online softmax, so no
-// S x S matrix ever exists.  Each wavefront keeps its 32 queries in registers
-// as the B operand of
+// head and streams keys 0 .. (last query of the tile) in blocks of BN = 64,
+// with an online softmax, so no S x S matrix ever exists.  Key blocks are
+// double-buffered in LDS: the next block's 16-byte global loads are in flight
+// in registers while the current block is computed, then stored as plain
+// 16-byte copies.  Tile rows are padded so that every LDS read below uses an
+// immediate offset and hits distinct banks: K and rope rows (one row per lane,
+// 16-byte reads) are 16 bytes longer than their data; V rows (transposing
+// reads of 4 rows x 64 bytes per half-wavefront) are 64 bytes longer.
+//
+// Each wavefront keeps its 32 queries in registers as the B operand of
 //     S^T[key, query] = K . Q^T          (A = K rows, 16-byte LDS reads)
-// so that the 32x32 accumulators hold one query per lane column: the running
-// max / sum are lane-local up to one exchange between wavefront halves, and
-// the probabilities already sit in the B-operand layout of
+// so the 32x32 accumulators hold one query per lane column: running max and
+// sum are lane-local up to one exchange between the wavefront halves, and the
+// probabilities already sit in the B-operand layout of
 //     O^T[dv, query] += V^T . P^T        (A = V^T via transposing LDS reads)
-// K, k_pe and V are staged as plain 16-byte copies in their storage layout:
-// the rope band stays bf16 and meets q_rope in bf16 MFMAs (both exact), the
+// The rope band stays bf16 and meets q_rope in bf16 MFMAs (both exact); the
 // nope part meets q_nope (converted once to fp16, exactly) in fp16 MFMAs.
-// The k_pe band is staged once per key block for all queries of the tile and
+// The k_pe band is loaded once per key block for all queries of the tile and
 // never expanded per head.  Blocks above a wavefront's diagonal are skipped;
 // only blocks crossing it are masked.
 //
@@ -32,7 +36,9 @@
 namespace laga {
 namespace {
 
-constexpr int BN = 64;  // keys per block
+constexpr int BN = 64;          // keys per block
+constexpr float kRescale = 8.f;  // lazy-rescale threshold of the running max (log2 units)
+
 
 struct FwdArgs {
   const void* q; const void* k_nope; const void* k_pe; const void* v;
@@ -40,8 +46,10 @@ struct FwdArgs {
   int64_t S, plane_k, plane_v; int B, h, n_qt; float scale_log2;
 };
 
-template <class M> struct Pads { static constexpr int k = 8, r = 8, v = 16; };
-template <> struct Pads<MmaF32> { static constexpr int k = 4, r = 4, v = 4; };
+// Row padding (elements) of the K, rope and V tiles; V rows of fp16 tiles are
+// padded by 64 bytes (conflict-free transposing reads) unless LDS is short.
+template <class M, int NS> struct Pads { static constexpr int k = 8, r = 8, v = NS == 1 ? 32 : 16; };
+template <int NS> struct Pads<MmaF32, NS> { static constexpr int k = 4, r = 4, v = 4; };
 
 // M: K/V/P operand type (fp16 or fp32); MR: rope operand type (bf16 or fp32);
 // InT: storage type of q and k_pe.
@@ -53,70 +61,74 @@ struct Fwd {
   typedef typename MR::frag FR;
   static constexpr int NT = NW * kWave;
   static constexpr int BM = 32 * NW;
-  static constexpr int LDK = DN + Pads<M>::k, LDR = DR + Pads<M>::r, LDV = DV + Pads<M>::v;
-  // LDS buffer: NS K planes | rope band | NS V planes (element offsets of E; rope in ER).
-  static constexpr int K_ELEMS = NS * BN * LDK;
-  static constexpr int R_BYTES = BN * LDR * sizeof(ER);
-  static constexpr int V_ELEMS = NS * BN * LDV;
-  static constexpr int BUF_BYTES = (K_ELEMS + V_ELEMS) * sizeof(E) + R_BYTES;
-  static constexpr int LDS_BYTES = 2 * BUF_BYTES;
-  // 16-byte chunks per block.
+  // Chunks (16 bytes) per row, elements per chunk, padded row pitches.
   static constexpr int EPC = 16 / sizeof(E), RPC = 16 / sizeof(ER);
-  static constexpr int K_CH = NS * BN * DN / EPC, R_CH = BN * DR / RPC, V_CH = NS * BN * DV / EPC;
-  static constexpr int ALL_CH = K_CH + R_CH + V_CH;
-  static constexpr int CH = (ALL_CH + NT - 1) / NT;
+  static constexpr int CK = DN / EPC, CR = DR / RPC, CV = DV / EPC;
+  static constexpr int LDK = DN + Pads<M, NS>::k, LDR = DR + Pads<M, NS>::r, LDV = DV + Pads<M, NS>::v;
+  // LDS buffer: NS K planes | rope band | NS V planes.
+  static constexpr int K_BYTES = NS * BN * LDK * sizeof(E);
+  static constexpr int R_BYTES = BN * LDR * sizeof(ER);
+  static constexpr int V_BYTES = NS * BN * LDV * sizeof(E);
+  static constexpr int BUF_BYTES = K_BYTES + R_BYTES + V_BYTES;
+  // 16-byte chunks of data per region (the padding is never loaded).
+  static constexpr int K_CH = NS * BN * CK, R_CH = BN * CR, V_CH = NS * BN * CV;
+  static_assert(K_CH % NT == 0 && R_CH % NT == 0 && V_CH % NT == 0, "staging passes");
   static constexpr int KS_N = DN / M::K, KS_R = DR / MR::K, NO = DV / 32, PV_STEPS = 32 / M::K;
   static_assert(DN % M::K == 0 && DR % MR::K == 0 && DV % 32 == 0, "head dims");
 
-  struct Regs { u32x4 c[CH]; };
+  // Staging: chunk c of a plane-major [planes][BN][CPR chunks] region, read
+  // from global memory in order (coalesced) and written to its padded row.
+  // Each region is a whole number of workgroup passes.
+  static constexpr int IK = K_CH / NT, IR = R_CH / NT, IV = V_CH / NT;
+  struct Regs { u32x4 k[IK]; u32x4 r[IR > 0 ? IR : 1]; u32x4 v[IV]; };
+
+  // Buffer loads: one scalar descriptor per (region, plane) and block, lane
+  // offsets fixed for the whole kernel.  Rows past the end of the sequence
+  // lie outside the descriptor's range and read as zero (masked anyway).
+  template <int CPR, int PER>
+  __device__ static void load_region(const char* block_base, int64_t plane_bytes, int row_bytes, int nk,
+                                     u32x4* out) {
+    static_assert((BN * CPR) % NT == 0, "a pass stays inside one plane");
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = i * NT + static_cast<int>(threadIdx.x);
+      const int plane = (i * NT) / (BN * CPR);
+      const int r = (c % (BN * CPR)) / CPR, lc = c % CPR;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(block_base + plane * plane_bytes), 0, nk * row_bytes, 0x00020000);
+      out[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, r * row_bytes + lc * 16, 0, 0);
+    }
+  }
+
+  template <int CPR, int PER, int PITCH_BYTES>
+  __device__ static void store_region(const u32x4* in, char* lds_region) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = i * NT + static_cast<int>(threadIdx.x);
+      const int plane = c / (BN * CPR), r = (c % (BN * CPR)) / CPR, lc = c % CPR;
+      *reinterpret_cast<u32x4*>(lds_region + (plane * BN + r) * PITCH_BYTES + lc * 16) = in[i];
+    }
+  }
 
   __device__ static void load_block(const FwdArgs& a, int b, int head, int64_t key0, Regs& R) {
-    const E* kn = static_cast<const E*>(a.k_nope);
-    const ER* kp = static_cast<const ER*>(a.k_pe);
-    const E* vg = static_cast<const E*>(a.v);
     const int nk = static_cast<int>(a.S - key0 < BN ? a.S - key0 : BN);
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      int c = i * NT + static_cast<int>(threadIdx.x);
-      u32x4 val{0u, 0u, 0u, 0u};
-      if (c < K_CH) {
-        const int p = c / (BN * DN / EPC), rem = c % (BN * DN / EPC);
-        const int r = rem / (DN / EPC), j = rem % (DN / EPC);
-        val = load_chunk(kn + p * a.plane_k + ((b * a.S + key0) * a.h + head) * DN, int64_t(a.h) * DN, r, j * EPC, nk);
-      } else if (c < K_CH + R_CH) {
-        c -= K_CH;
-        const int r = c / (DR / RPC), j = c % (DR / RPC);
-        val = load_chunk(kp + (b * a.S + key0) * DR, DR, r, j * RPC, nk);
-      } else if (c < ALL_CH) {
-        c -= K_CH + R_CH;
-        const int p = c / (BN * DV / EPC), rem = c % (BN * DV / EPC);
-        const int r = rem / (DV / EPC), j = rem % (DV / EPC);
-        val = load_chunk(vg + p * a.plane_v + ((b * a.S + key0) * a.h + head) * DV, int64_t(a.h) * DV, r, j * EPC, nk);
-      }
-      R.c[i] = val;
-    }
+    const int64_t row0 = (b * a.S + key0) * a.h + head;
+    load_region<CK, IK>(static_cast<const char*>(a.k_nope) + row0 * DN * sizeof(E), a.plane_k * sizeof(E),
+                        a.h * DN * static_cast<int>(sizeof(E)), nk, R.k);
+    load_region<CR, IR>(static_cast<const char*>(a.k_pe) + (b * a.S + key0) * DR * sizeof(ER), 0,
+                        DR * static_cast<int>(sizeof(ER)), nk, R.r);
+    load_region<CV, IV>(static_cast<const char*>(a.v) + row0 * DV * sizeof(E), a.plane_v * sizeof(E),
+                        a.h * DV * static_cast<int>(sizeof(E)), nk, R.v);
   }
 
   __device__ static void store_block(const Regs& R, char* buf) {
-    E* Ks = reinterpret_cast<E*>(buf);
-    ER* Kr = reinterpret_cast<ER*>(buf + K_ELEMS * sizeof(E));
-    E* Vs = reinterpret_cast<E*>(buf + K_ELEMS * sizeof(E) + R_BYTES);
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      int c = i * NT + static_cast<int>(threadIdx.x);
-      if (c < K_CH) {
-        const int p = c / (BN * DN / EPC), rem = c % (BN * DN / EPC);
-        store_chunk(Ks + p * BN * LDK, LDK, rem / (DN / EPC), (rem % (DN / EPC)) * EPC, R.c[i]);
-      } else if (c < K_CH + R_CH) {
-        c -= K_CH;
-        store_chunk(Kr, LDR, c / (DR / RPC), (c % (DR / RPC)) * RPC, R.c[i]);
-      } else if (c < ALL_CH) {
-        c -= K_CH + R_CH;
-        const int p = c / (BN * DV / EPC), rem = c % (BN * DV / EPC);
-        store_chunk(Vs + p * BN * LDV, LDV, rem / (DV / EPC), (rem % (DV / EPC)) * EPC, R.c[i]);
-      }
-    }
+    store_region<CK, IK, LDK * sizeof(E)>(R.k, buf);
+    store_region<CR, IR, LDR * sizeof(ER)>(R.r, buf + K_BYTES);
+    store_region<CV, IV, LDV * sizeof(E)>(R.v, buf + K_BYTES + R_BYTES);
   }
+
+  __device__ static F k_frag(const E* Kp, int r, int c0) { return lds_frag<M>(Kp + r * LDK + c0); }
+  __device__ static FR r_frag(const ER* Rp, int r, int c0) { return lds_frag<MR>(Rp + r * LDR + c0); }
 
   // A operand of O^T += V^T P^T for one MFMA step: rows dv n0 + lane%32, keys of
   // accumulator registers st*KPL .. of 32-key atom t (see acc_key_col).
@@ -128,6 +140,120 @@ struct Fwd {
       const int key = t * 32 + 8 * (st / 4) + 4 * (lane / 32) + (st % 4);
       return Vp[key * LDV + n0 + lane % 32];
     }
+  }
+
+  struct State {
+    F qn[KS_N];
+    FR qr[KS_R];
+    f32x16 o[NO];
+    float m_run, l_run;
+  };
+
+  __device__ static void compute_block(const FwdArgs& a, const char* buf, int64_t key0, int64_t qw, int64_t tq,
+                                       State& st_) {
+    const int lane = threadIdx.x % kWave;
+    const int hf = lane / 32, col = lane % 32;
+    const E* Ks = reinterpret_cast<const E*>(buf);
+    const ER* Kr = reinterpret_cast<const ER*>(buf + K_BYTES);
+    const E* Vs = reinterpret_cast<const E*>(buf + K_BYTES + R_BYTES);
+
+    f32x16 sc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[t][r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS_N; ++s)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int krow = t * 32 + col;
+        sc[t] = M::mma(k_frag(Ks, krow, s * M::K + hf * M::KPL), st_.qn[s], sc[t]);
+        if constexpr (NS == 2)
+          sc[t] = M::mma(k_frag(Ks + BN * LDK, krow, s * M::K + hf * M::KPL), st_.qn[s], sc[t]);
+      }
+#pragma unroll
+    for (int s = 0; s < KS_R; ++s)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) sc[t] = MR::mma(r_frag(Kr, t * 32 + col, s * MR::K + hf * MR::KPL), st_.qr[s], sc[t]);
+
+    // Causal mask, only on blocks that cross this wavefront's diagonal: key
+    // key0 + t*32 + 8(r/4) + 4hf + r%4 is masked when it exceeds the query.
+    if (__builtin_expect(key0 + BN - 1 > qw, 0)) {
+      const int rel = static_cast<int>(tq - key0) - 4 * hf;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (t * 32 + 8 * (r / 4) + (r % 4) > rel) sc[t][r] = -INFINITY;
+    }
+    // Row max of the raw scores (the scale > 0 is folded into the exponent).
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sc[t][r]);
+    mloc = pair_max(mloc) * a.scale_log2;
+    // The running max (log2 units) is raised only when a row's block max
+    // exceeds it by more than kRescale, so unnormalised probabilities stay
+    // below 2^kRescale and O / l are rescaled rarely.
+    if (__any(mloc > st_.m_run + kRescale)) {
+      const float m_new = fmaxf(st_.m_run, mloc);
+      const float alpha = __builtin_amdgcn_exp2f(st_.m_run - m_new);
+      st_.l_run *= alpha;
+#pragma unroll
+      for (int n = 0; n < NO; ++n)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st_.o[n][r] *= alpha;
+      st_.m_run = m_new;
+    }
+    float lsum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[t][r], a.scale_log2, -st_.m_run));
+        sc[t][r] = p;
+        lsum += p;
+      }
+    st_.l_run += pair_sum(lsum);
+
+    // O^T += V^T P^T; one step covers K keys, accumulator r = st*KPL + j.
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int st = 0; st < PV_STEPS; ++st) {
+        E ph[M::KPL], pl[M::KPL];
+#pragma unroll
+        for (int j = 0; j < M::KPL; ++j) {
+          E part[NS];
+          split_to<M, NS>(sc[t][st * M::KPL + j], part);
+          ph[j] = part[0];
+          if constexpr (NS == 2) pl[j] = part[1];
+        }
+        const F pfh = *reinterpret_cast<F*>(ph);
+#pragma unroll
+        for (int n = 0; n < NO; ++n) {
+          const F vh = v_frag(Vs, t, st, n * 32);
+          st_.o[n] = M::mma(vh, pfh, st_.o[n]);
+          if constexpr (NS == 2) {
+            const F pfl = *reinterpret_cast<F*>(pl);
+            st_.o[n] = M::mma(v_frag(Vs + BN * LDV, t, st, n * 32), pfh, st_.o[n]);
+            st_.o[n] = M::mma(vh, pfl, st_.o[n]);
+          }
+        }
+      }
+  }
+
+  // One key block: publish the prefetched block, prefetch the next one, and
+  // compute (ALL: every wavefront of the tile has keys <= its queries here).
+  template <bool ALL>
+  __device__ static void step(const FwdArgs& a, int kb, int nkb, int b, int head, int64_t qw, int64_t tq,
+                              char* cur, Regs& R, State& st_) {
+    store_block(R, cur);
+    __syncthreads();
+    const int64_t key0 = static_cast<int64_t>(kb) * BN;
+    if (kb + 1 < nkb) load_block(a, b, head, key0 + BN, R);
+    if (ALL || key0 <= qw + 31) compute_block(a, cur, key0, qw, tq, st_);
   }
 
   __device__ static void run(const FwdArgs& a, char* lds) {
@@ -157,150 +283,78 @@ struct Fwd {
     const int64_t tq = qw + col;
     const bool qvalid = tq < a.S;
 
-    // Q fragments (B operand): query tq, dims hf*KPL + s*K + [0, KPL).
-    const InT* qp = static_cast<const InT*>(a.q) + ((b * a.S + (qvalid ? tq : 0)) * a.h + head) * (DN + DR);
-    F qn[KS_N];
-    FR qr[KS_R];
-#pragma unroll
-    for (int s = 0; s < KS_N; ++s) {
-      E tmp[M::KPL];
-#pragma unroll
-      for (int j = 0; j < M::KPL; ++j) tmp[j] = M::from_f32(qvalid ? to_f32(qp[s * M::K + hf * M::KPL + j]) : 0.f);
-      qn[s] = *reinterpret_cast<F*>(tmp);
-    }
-#pragma unroll
-    for (int s = 0; s < KS_R; ++s) {
-      ER tmp[MR::KPL];
-#pragma unroll
-      for (int j = 0; j < MR::KPL; ++j) tmp[j] = qvalid ? qp[DN + s * MR::K + hf * MR::KPL + j] : ER{};
-      qr[s] = *reinterpret_cast<FR*>(tmp);
-    }
-
-    f32x16 o[NO];
-#pragma unroll
-    for (int n = 0; n < NO; ++n)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[n][r] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
-
     int64_t kend = q0 + BM;
     if (kend > a.S) kend = a.S;
     const int nkb = static_cast<int>((kend + BN - 1) / BN);
-
     Regs R;
     load_block(a, b, head, 0, R);
-    for (int kb = 0; kb < nkb; ++kb) {
-      const int64_t key0 = static_cast<int64_t>(kb) * BN;
-      char* buf = lds + (kb & 1) * BUF_BYTES;
-      store_block(R, buf);
-      __syncthreads();
-      if (kb + 1 < nkb) load_block(a, b, head, key0 + BN, R);
-      if (key0 > qw + 31) continue;  // whole block above this wavefront's diagonal
 
-      const E* Ks = reinterpret_cast<const E*>(buf);
-      const ER* Kr = reinterpret_cast<const ER*>(buf + K_ELEMS * sizeof(E));
-      const E* Vs = reinterpret_cast<const E*>(buf + K_ELEMS * sizeof(E) + R_BYTES);
-
-      f32x16 sc[2];
+    // Q fragments (B operand): query tq, dims hf*KPL + s*K + [0, KPL).
+    State st_;
+    const InT* qp = static_cast<const InT*>(a.q) + ((b * a.S + (qvalid ? tq : 0)) * a.h + head) * (DN + DR);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+    for (int s = 0; s < KS_N; ++s) {
+      E tmp[M::KPL];
+      if constexpr (M::KPL == 8 && sizeof(InT) == 2) {
+        const u16x8 raw = qvalid ? *reinterpret_cast<const u16x8*>(qp + s * M::K + hf * M::KPL) : u16x8{};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sc[t][r] = 0.f;
-        const int krow = t * 32 + col;
+        for (int j = 0; j < 8; ++j) tmp[j] = M::from_f32(to_f32(static_cast<InT>(raw[j])));
+      } else {
 #pragma unroll
-        for (int s = 0; s < KS_N; ++s) {
-          sc[t] = M::mma(lds_frag<M>(Ks + krow * LDK + s * M::K + hf * M::KPL), qn[s], sc[t]);
-          if constexpr (NS == 2)
-            sc[t] = M::mma(lds_frag<M>(Ks + BN * LDK + krow * LDK + s * M::K + hf * M::KPL), qn[s], sc[t]);
-        }
-#pragma unroll
-        for (int s = 0; s < KS_R; ++s)
-          sc[t] = MR::mma(lds_frag<MR>(Kr + krow * LDR + s * MR::K + hf * MR::KPL), qr[s], sc[t]);
+        for (int j = 0; j < M::KPL; ++j) tmp[j] = M::from_f32(qvalid ? to_f32(qp[s * M::K + hf * M::KPL + j]) : 0.f);
       }
-
-      // Row max of the raw scores (scale > 0 is folded into the exponent).
-      const bool diag = key0 + BN - 1 > qw;
-      float mloc = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (diag) {
-            const int64_t u = key0 + t * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
-            if (u > tq) sc[t][r] = -INFINITY;
-          }
-          mloc = fmaxf(mloc, sc[t][r]);
-        }
-      mloc = fmaxf(mloc, swap_halves(mloc));
-      const float m_new = fmaxf(m_run, mloc * a.scale_log2);
-      float lsum = 0.f;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = exp2f(fmaf(sc[t][r], a.scale_log2, -m_new));
-          sc[t][r] = p;
-          lsum += p;
-        }
-      lsum += swap_halves(lsum);
-      if (__any(m_new != m_run)) {
-        const float alpha = exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int n = 0; n < NO; ++n)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[n][r] *= alpha;
-      }
-      l_run += lsum;
-      m_run = m_new;
-
-      // O^T += V^T P^T; one step covers K keys, accumulator r = st*KPL + j.
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int st = 0; st < PV_STEPS; ++st) {
-          E ph[M::KPL], pl[M::KPL];
-#pragma unroll
-          for (int j = 0; j < M::KPL; ++j) {
-            E part[NS];
-            split_to<M, NS>(sc[t][st * M::KPL + j], part);
-            ph[j] = part[0];
-            if constexpr (NS == 2) pl[j] = part[1];
-          }
-          const F pfh = *reinterpret_cast<F*>(ph);
-#pragma unroll
-          for (int n = 0; n < NO; ++n) {
-            const F vh = v_frag(Vs, t, st, n * 32);
-            o[n] = M::mma(vh, pfh, o[n]);
-            if constexpr (NS == 2) {
-              const F pfl = *reinterpret_cast<F*>(pl);
-              o[n] = M::mma(v_frag(Vs + BN * LDV, t, st, n * 32), pfh, o[n]);
-              o[n] = M::mma(vh, pfl, o[n]);
-            }
-          }
-        }
+      st_.qn[s] = *reinterpret_cast<F*>(tmp);
     }
+#pragma unroll
+    for (int s = 0; s < KS_R; ++s) {
+      if constexpr (MR::KPL == 8 && sizeof(InT) == 2) {
+        st_.qr[s] = qvalid ? *reinterpret_cast<const FR*>(qp + DN + s * MR::K + hf * MR::KPL) : FR{};
+      } else {
+        ER tmp[MR::KPL];
+#pragma unroll
+        for (int j = 0; j < MR::KPL; ++j) tmp[j] = qvalid ? qp[DN + s * MR::K + hf * MR::KPL + j] : ER{};
+        st_.qr[s] = *reinterpret_cast<FR*>(tmp);
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < NO; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st_.o[n][r] = 0.f;
+    st_.m_run = -INFINITY;
+    st_.l_run = 0.f;
+
+    // Blocks with key0 <= q0 + 31 are computed by every wavefront; the last
+    // few (above the lower wavefronts' diagonals) are skipped per wavefront.
+    int nall = static_cast<int>((q0 + 31) / BN) + 1;
+    if (nall > nkb) nall = nkb;
+    int kb = 0;
+    for (; kb < nall; ++kb) step<true>(a, kb, nkb, b, head, qw, tq, lds + (kb & 1) * BUF_BYTES, R, st_);
+    for (; kb < nkb; ++kb) step<false>(a, kb, nkb, b, head, qw, tq, lds + (kb & 1) * BUF_BYTES, R, st_);
 
     if (qvalid) {
-      const float inv = 1.0f / l_run;
+      const float inv = 1.0f / st_.l_run;
       float* op = a.o + ((b * a.S + tq) * a.h + head) * DV;
 #pragma unroll
       for (int n = 0; n < NO; ++n)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          f32x4 w = {o[n][4 * g] * inv, o[n][4 * g + 1] * inv, o[n][4 * g + 2] * inv, o[n][4 * g + 3] * inv};
+          f32x4 w = {st_.o[n][4 * g] * inv, st_.o[n][4 * g + 1] * inv, st_.o[n][4 * g + 2] * inv,
+                     st_.o[n][4 * g + 3] * inv};
           *reinterpret_cast<f32x4*>(op + n * 32 + 8 * g + 4 * hf) = w;
         }
       if (hf == 0)
-        a.lse[(static_cast<int64_t>(b) * a.h + head) * a.S + tq] = (m_run + log2f(l_run)) * 0.69314718055994531f;
+        a.lse[(static_cast<int64_t>(b) * a.h + head) * a.S + tq] =
+            (st_.m_run + log2f(st_.l_run)) * 0.69314718055994531f;
     }
   }
 };
 
+// Two wavefronts per SIMD: either one 8-wavefront workgroup or two independent
+// 4-wavefront workgroups per CU (whose barriers do not line up).
 template <class InT, class M, class MR, int NS, int DN, int DR, int DV, int NW>
-__global__ __launch_bounds__(NW * kWave) void attn_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NW * kWave, 2) void attn_fwd_kernel(FwdArgs a) {
   typedef Fwd<InT, M, MR, NS, DN, DR, DV, NW> Kn;
-  __shared__ __attribute__((aligned(16))) char lds[Kn::LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds[2 * Kn::BUF_BYTES];
   Kn::run(a, lds);
 }
 

@@ -119,6 +119,18 @@ __device__ __forceinline__ float wave_sum(float v) {
 // Exchange with the lane 32 positions away (the other half of the wavefront).
 __device__ __forceinline__ float swap_halves(float v) { return __shfl_xor(v, 32, kWave); }
 
+// max / sum of v over lanes l and l ^ 32, in every lane, without LDS: gfx950's
+// v_permlane32_swap given (v, v) returns the lower half duplicated in one
+// result and the upper half duplicated in the other.
+__device__ __forceinline__ float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Position of key `k` (0..BN-1) inside an LDS row that a 32x32 atom reads as a
 // K-operand fed from accumulator registers: bits 2 and 3 of the key index are
 // swapped, so that the KPL keys one lane needs for one MFMA step are contiguous.
