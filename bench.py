@@ -40,8 +40,12 @@ def alg_flops(d) -> dict:
     pairs = d.S * (d.S + 1) / 2
     attn_fwd = 2 * pairs * (d.d_qk + d.d_v) * d.h * d.B
     kv_up = 2 * d.B * d.S * d.d_kv * d.h * (d.d_nope + d.d_v)
-    return dict(attn_fwd=attn_fwd, attn_bwd=2 * attn_fwd, kv_up=kv_up, fold=2 * kv_up,
-                fwd=attn_fwd + kv_up, step=3 * attn_fwd + 3 * kv_up)
+    # The backward's products dP, dV, dK, dq counted once each (no recompute of S):
+    # the dK/dV kernel owns dP, dV, dK and the dq kernel owns dq.
+    bwd_dkdv = 2 * pairs * (2 * d.d_v + d.d_qk) * d.h * d.B
+    bwd_dq = 2 * pairs * d.d_qk * d.h * d.B
+    return dict(attn_fwd=attn_fwd, attn_bwd=2 * attn_fwd, bwd_dkdv=bwd_dkdv, bwd_dq=bwd_dq, kv_up=kv_up,
+                fold=2 * kv_up, fwd=attn_fwd + kv_up, step=3 * attn_fwd + 3 * kv_up)
 
 
 def activation_bytes(d, kv_bytes: int) -> dict:
@@ -54,13 +58,36 @@ def activation_bytes(d, kv_bytes: int) -> dict:
     return dict(laga=laga, explicit=explicit, absorbed=absorbed)
 
 
-def kernel_traffic():
-    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter summary."""
+def source_digest(rel: str) -> str:
+    import hashlib
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def kernel_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter on a plain copy), or None
+    when no counters were taken or the kernel's source changed since they were."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
-        return {}
+        return None
     with open(path) as f:
-        return json.load(f)
+        rec = json.load(f).get("kernels", {}).get(kernel)
+    if not rec or source_digest(rec["source"]) != rec["source_sha256"]:
+        return None
+    return rec["bytes_per_launch"]
+
+
+def calibration_copy(nbytes: int = 256 << 20, reps: int = 3):
+    """A plain device copy of known size: the reference point that scales the HBM byte
+    counters of the other kernels in a counter-collection run."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def cpu_baseline(d) -> dict:
@@ -93,6 +120,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a 256 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU's share of the SP group; runs on more than one GPU "
@@ -103,6 +132,8 @@ def main():
     import laga_inputs as li
     from head_latent_attention_laga_amd import LagaPath, _lib
 
+    if args.calibrate_copy:
+        calibration_copy()
     d, _ = li.workload(WORKLOAD)
     inp = li.make_inputs(d, 0, backward=True)
     x = {k: li.to_torch(t) for k, t in inp.items()}
@@ -177,13 +208,13 @@ def main():
     # Roofline of the dominant kernel of the step.
     work = {"rmsnorm_fwd": ("hbm", d.B * d.S * d.d_kv * (2 + 4) + 4 * d.B * d.S + 2 * d.d_kv),
             "kv_up": ("mfma", fl["kv_up"]), "attn_fwd": ("mfma", fl["attn_fwd"]),
-            "attn_bwd_dkdv": ("mfma", fl["attn_bwd"] * 3 / 5), "attn_bwd_dq": ("mfma", fl["attn_bwd"] * 2 / 5),
+            "attn_bwd_dkdv": ("mfma", fl["bwd_dkdv"]), "attn_bwd_dq": ("mfma", fl["bwd_dq"]),
             "fold_dL": ("mfma", fl["kv_up"]), "fold_dW": ("mfma", fl["kv_up"])}
     dom = max((n for n in per if n in work), key=lambda n: per[n])
     bound, units = work[dom]
     ach = units / (per[dom] / 1e3) / (1e12 if bound == "mfma" else 1e9)
     peak = PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_HBM_GBS
-    tr = kernel_traffic().get(dom)
+    tr = kernel_traffic(dom)
     roofline = {"kernel": dom, "bound": bound, "achieved": round(ach, 2), "peak": peak,
                 "unit": "TFLOP/s" if bound == "mfma" else "GB/s", "frac": round(ach / peak, 4),
                 "traffic": tr}
