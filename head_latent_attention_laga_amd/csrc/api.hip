@@ -49,7 +49,7 @@ laga_status from_hip(hipError_t e) {
 
 // Backward workspace regions, each 256-byte aligned, in float32 elements.
 struct BwdLayout {
-  size_t delta, dkv, dkpe, dL, dw, dg, total;  // byte offsets, total bytes
+  size_t delta, dkv, dkpe, dL, lp, dw, dg, total;  // byte offsets, total bytes
 };
 
 size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
@@ -66,6 +66,7 @@ BwdLayout bwd_layout(const Shape& s) {
   L.dkv = take(static_cast<size_t>(s.T) * s.h * s.C());
   L.dkpe = take(static_cast<size_t>(s.h) * s.T * s.d_rope);
   L.dL = take(static_cast<size_t>(s.T) * s.d_kv);
+  L.lp = take(static_cast<size_t>(s.T) * s.d_kv);  // bf16 hi/lo planes or fp32
   L.dw = take(laga::fold_dw_partial_floats(s));
   L.dg = take(laga::norm_bwd_partial_floats(s));
   L.total = off;
@@ -143,7 +144,8 @@ laga_status laga_attn_bwd_traced(const laga_dims* dims, const void* q, const voi
   if (!aligned16(workspace)) return LAGA_ERR_ALIGN;
   char* ws = static_cast<char*>(workspace);
   float* delta = reinterpret_cast<float*>(ws + L.delta);
-  float* dkv = reinterpret_cast<float*>(ws + L.dkv);
+  void* dkv = ws + L.dkv;
+  void* lp = ws + L.lp;
   float* dkpe = reinterpret_cast<float*>(ws + L.dkpe);
   float* dL = reinterpret_cast<float*>(ws + L.dL);
   float* dw = reinterpret_cast<float*>(ws + L.dw);
@@ -167,7 +169,8 @@ laga_status laga_attn_bwd_traced(const laga_dims* dims, const void* q, const voi
   if ((e = mark(4)) != hipSuccess) return from_hip(e);
   if ((e = laga::launch_fold_dl(s, dkv, w_kv_b, dL, hs)) != hipSuccess) return from_hip(e);
   if ((e = mark(5)) != hipSuccess) return from_hip(e);
-  if ((e = laga::launch_fold_dw(s, dkv, latent, gamma, rstd, dw, d_w_kv_b, hs)) != hipSuccess) return from_hip(e);
+  if ((e = laga::launch_norm_planes(s, latent, gamma, rstd, lp, hs)) != hipSuccess) return from_hip(e);
+  if ((e = laga::launch_fold_dw(s, dkv, lp, dw, d_w_kv_b, hs)) != hipSuccess) return from_hip(e);
   if ((e = mark(6)) != hipSuccess) return from_hip(e);
   if ((e = laga::launch_norm_bwd(s, dL, latent, gamma, rstd, d_latent, dg, d_gamma, hs)) != hipSuccess)
     return from_hip(e);

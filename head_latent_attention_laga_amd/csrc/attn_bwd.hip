@@ -31,6 +31,8 @@
 // dW_kv_b, dLatent and dgamma use K, V, P and dS as fp16 hi + lo pairs (q and
 // dO are exact in fp16); dq uses the hi parts of K and V and single fp16 dS.
 // The float32 instantiation uses fp32 MFMAs.
+#include <type_traits>
+
 #include "attn_common.hpp"
 #include "launch.hpp"
 
@@ -43,8 +45,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 struct BwdArgs {
   const void* q; const void* k_nope; const void* k_pe; const void* v;
   const float* lse; const float* delta; const void* d_o;
-  float* dkv; float* dk_pe_part; float* dq;
-  int64_t S, plane_k, plane_v; int B, h; float scale_log2, scale;
+  void* dkv; float* dk_pe_part; float* dq;
+  int64_t S, plane_k, plane_v, plane_dkv; int B, h; float scale_log2, scale;
 };
 
 // Row pitches (elements) of LDS tiles: rows read one per lane with 16-byte
@@ -338,7 +340,7 @@ struct Dkdv {
 
     if (!kvalid) return;
     // Lane holds column `key`; accumulator r is row 8(r/4) + 4hf + r%4 of its 32-row atom.
-    float* out = a.dkv + ((b * a.S + key) * a.h + head) * C;
+    const int64_t orow = ((b * a.S + key) * a.h + head) * C;
 #pragma unroll
     for (int n = 0; n < NKT; ++n)
 #pragma unroll
@@ -348,7 +350,7 @@ struct Dkdv {
         f32x4 w = {dk[n][4 * g] * a.scale, dk[n][4 * g + 1] * a.scale, dk[n][4 * g + 2] * a.scale,
                    dk[n][4 * g + 3] * a.scale};
         if (d < DN)
-          *reinterpret_cast<f32x4*>(out + d) = w;
+          store_dkv(a, orow + d, w);
         else
           *reinterpret_cast<f32x4*>(a.dk_pe_part + (static_cast<int64_t>(head) * a.B * a.S + b * a.S + key) * DR +
                                     (d - DN)) = w;
@@ -359,8 +361,26 @@ struct Dkdv {
       for (int g = 0; g < 4; ++g) {
         const int d = n * 32 + 8 * g + 4 * hf;
         f32x4 w = {dvt[n][4 * g], dvt[n][4 * g + 1], dvt[n][4 * g + 2], dvt[n][4 * g + 3]};
-        *reinterpret_cast<f32x4*>(out + DN + d) = w;
+        store_dkv(a, orow + DN + d, w);
       }
+  }
+
+  // Four consecutive dK / dV values in the fold GEMMs' operand format: bf16 hi
+  // and lo planes (16-bit operand path) or fp32.
+  __device__ static void store_dkv(const BwdArgs& a, int64_t at, f32x4 w) {
+    if constexpr (std::is_same<M, MmaF32>::value) {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(a.dkv) + at) = w;
+    } else {
+      u16x4 hi, lo;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        hi[j] = f32_to_bf16(w[j]);
+        lo[j] = f32_to_bf16(w[j] - bf16_to_f32(hi[j]));
+      }
+      bf16_t* p = static_cast<bf16_t*>(a.dkv) + at;
+      *reinterpret_cast<u16x4*>(p) = hi;
+      *reinterpret_cast<u16x4*>(p + a.plane_dkv) = lo;
+    }
   }
 };
 
@@ -582,6 +602,7 @@ BwdArgs make_args(const Shape& s, const void* q, const void* kn, const void* kp,
   a.S = s.S; a.B = static_cast<int>(s.B); a.h = s.h;
   a.plane_k = s.T * s.h * s.d_nope;
   a.plane_v = s.T * s.h * s.d_v;
+  a.plane_dkv = s.T * s.h * s.C();
   a.scale = 1.0f / sqrtf(static_cast<float>(s.d_qk()));
   a.scale_log2 = kLog2e * a.scale;
   return a;
@@ -639,7 +660,7 @@ hipError_t launch_head_sum(const Shape& s, const float* part, float* out, hipStr
 }
 
 hipError_t launch_attn_bwd_dkdv(const Shape& s, const void* q, const void* kn, const void* kp, const void* v,
-                                const float* lse, const float* delta, const void* d_o, float* dkv,
+                                const float* lse, const float* delta, const void* d_o, void* dkv,
                                 float* dk_pe_part, hipStream_t st) {
   BwdArgs a = make_args(s, q, kn, kp, v, lse, delta, d_o);
   a.dkv = dkv;

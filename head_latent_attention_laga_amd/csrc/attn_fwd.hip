@@ -27,8 +27,10 @@
 // only blocks crossing it are masked.
 //
 // Precision: NS == 1 uses single fp16 K, V and P.  NS == 2 reads K and V as
-// fp16 hi/lo planes (as laga_kv_up writes them) and splits P:
-// S = Q.K_hi + Q.K_lo, O = P_hi V_hi + P_hi V_lo + P_lo V_hi (fp32-class).
+// fp16 hi/lo planes (as laga_kv_up writes them): S = Q.K_hi + Q.K_lo with
+// fp32-class accuracy, and O = P.V_hi + P.V_lo with P in fp16, whose rounding
+// is independent from pair to pair and averages out in O and in the backward's
+// delta = sum dO o.
 // The float32 instantiation uses fp32 MFMAs throughout.
 #include "attn_common.hpp"
 #include "launch.hpp"
@@ -222,24 +224,14 @@ struct Fwd {
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int st = 0; st < PV_STEPS; ++st) {
-        E ph[M::KPL], pl[M::KPL];
+        E ph[M::KPL];
 #pragma unroll
-        for (int j = 0; j < M::KPL; ++j) {
-          E part[NS];
-          split_to<M, NS>(sc[t][st * M::KPL + j], part);
-          ph[j] = part[0];
-          if constexpr (NS == 2) pl[j] = part[1];
-        }
-        const F pfh = *reinterpret_cast<F*>(ph);
+        for (int j = 0; j < M::KPL; ++j) ph[j] = M::from_f32(sc[t][st * M::KPL + j]);
+        const F pf = *reinterpret_cast<F*>(ph);
 #pragma unroll
         for (int n = 0; n < NO; ++n) {
-          const F vh = v_frag(Vs, t, st, n * 32);
-          st_.o[n] = M::mma(vh, pfh, st_.o[n]);
-          if constexpr (NS == 2) {
-            const F pfl = *reinterpret_cast<F*>(pl);
-            st_.o[n] = M::mma(v_frag(Vs + BN * LDV, t, st, n * 32), pfh, st_.o[n]);
-            st_.o[n] = M::mma(vh, pfl, st_.o[n]);
-          }
+          st_.o[n] = M::mma(v_frag(Vs, t, st, n * 32), pf, st_.o[n]);
+          if constexpr (NS == 2) st_.o[n] = M::mma(v_frag(Vs + BN * LDV, t, st, n * 32), pf, st_.o[n]);
         }
       }
   }

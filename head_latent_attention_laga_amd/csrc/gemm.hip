@@ -6,18 +6,27 @@
 //           scattered into k_nope[t, i, c] (c < d_nope) and v[t, i, c - d_nope]
 //   fold_dl C[t, k] = sum_n dKV[t, n] W_r[n, k]         (dL, input of the norm backward)
 //   fold_dw C[n, k] = sum_t dKV[t, n] L[t, k]           (the (full_seq, H_r) shard
-//           of the W_kv_b gradient [LAGA §5.2]); L is rebuilt on the fly from
-//           the latent, gamma and rstd, and the reduction over t is split into
-//           chunks summed by a second, deterministic kernel.
+//           of the W_kv_b gradient [LAGA §5.2]); the reduction over t is split
+//           into chunks summed by a second, deterministic kernel.
 //
 // One kernel template serves all three: a 128x128 output tile per 256-thread
 // workgroup (four wavefronts in 2x2, each 64x64 = 2x2 MFMA atoms of 32x32),
-// K staged through LDS 32 at a time.  Loaders read each operand along its
-// contiguous axis with 16-byte loads and write LDS rows in the K-contiguous
-// order the atoms read.  Float operands are split on the way into LDS into NS
-// bf16 terms (hi, lo); the product keeps the terms with sa + sb < max(NSA, NSB),
-// which makes a bf16 matrix-core GEMM accurate to about 2^-16 relative.
-#include "device.hpp"
+// K staged through double-buffered LDS 32 at a time, one barrier per step.
+// Each operand slab moves global -> registers -> LDS in 16-byte chunks along
+// the operand's contiguous axis:
+//   KC operands (k contiguous in memory) land as LDS rows [row][k] and are
+//      read with 16-byte fragment loads;
+//   RC operands (row contiguous: the k axis strides memory) land as [k][row]
+//      and 16-bit fragments come from gfx950's transposing LDS read.
+// Operands are stored as NS planes of the MFMA element type (x ~= sum of the
+// planes).  bf16 planes are written by the producing kernels, except the
+// normalised latent of the up-projection, which arrives in fp32 and is split
+// into bf16 hi + lo while it is staged.  The product keeps the term pairs
+// (sa, sb) with sa + sb < max(NSA, NSB), which makes the bf16 GEMM accurate to
+// about 2^-16 relative.
+#include <type_traits>
+
+#include "attn_common.hpp"
 #include "launch.hpp"
 
 namespace laga {
@@ -26,85 +35,102 @@ namespace {
 constexpr int BM = 128, BN = 128, BK = 32;
 constexpr int kThreads = 256;
 
-template <class M> struct Pad { static constexpr int v = 8; };
-template <> struct Pad<MmaF32> { static constexpr int v = 1; };
-
-// ------------------------------------------------------------------- loaders
-// load4(row, k, out): four consecutive elements along the operand's contiguous
-// axis (k for K-contiguous operands, row otherwise), zero outside [0,R)x[0,K).
-
-struct LoadF32KC {  // float src[row * ld + k]
-  static constexpr bool KC = true;
-  const float* p; int64_t ld, R, K;
-  __device__ void load4(int64_t r, int64_t k, float* o) const {
-    if (r < R && k + 3 < K) {
-      f32x4 v = *reinterpret_cast<const f32x4*>(p + r * ld + k);
-      o[0] = v[0]; o[1] = v[1]; o[2] = v[2]; o[3] = v[3];
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) o[j] = (r < R && k + j < K) ? p[r * ld + k + j] : 0.f;
-    }
-  }
+// A GEMM operand in global memory: element (row r, k) of plane s at
+//   p + s * plane + r * ld + k   (KC)   or   p + s * plane + k * ld + r   (RC).
+// Rows >= R and k >= K read as zero.
+template <class Src>
+struct Operand {
+  const Src* p;
+  int64_t ld, plane, R, K;
 };
 
-template <class InT>
-struct LoadInKC {  // input-dtype src[row * ld + k]
-  static constexpr bool KC = true;
-  const InT* p; int64_t ld, R, K;
-  __device__ void load4(int64_t r, int64_t k, float* o) const {
-    if constexpr (sizeof(InT) == 2) {
-      if (r < R && k + 3 < K) {
-        u16x4 v = *reinterpret_cast<const u16x4*>(p + r * ld + k);
+// ROWS x BK slab of one operand, in NS LDS planes of the MFMA element type.
+template <class M, int NS, bool KC, int ROWS, class Src>
+struct SlabT {
+  typedef typename M::elem E;
+  typedef typename M::frag F;
+  static constexpr int EPC = 16 / sizeof(E);  // elements per 16-byte chunk
+  static constexpr bool SPLIT = !std::is_same<Src, E>::value;
+  static_assert(!SPLIT || (std::is_same<Src, float>::value && NS == 2 && EPC == 8),
+                "only fp32 -> 16-bit hi/lo splitting");
+  static constexpr int LD = KC ? BK + EPC : ROWS + (sizeof(E) == 2 ? 32 : 4);  // LDS pitch, elements
+  static constexpr int PLANE = (KC ? ROWS : BK) * LD;
+  static constexpr int BYTES = NS * PLANE * static_cast<int>(sizeof(E));
+  static constexpr int CHUNKS = ROWS * BK / EPC;  // per plane
+  static constexpr int PER = CHUNKS / kThreads;
+  static_assert(CHUNKS % kThreads == 0, "whole chunks per thread");
+  static constexpr int NP = SPLIT ? 1 : NS;  // planes read from memory
+  static constexpr int WORDS = SPLIT ? 2 : 1;  // 16-byte words per chunk read
+
+  u32x4 reg[NP][PER][WORDS];
+
+  __device__ static void chunk_pos(int c, int& r, int& k) {
+    if constexpr (KC) {
+      r = c / (BK / EPC);
+      k = (c % (BK / EPC)) * EPC;
+    } else {
+      k = c / (ROWS / EPC);
+      r = (c % (ROWS / EPC)) * EPC;
+    }
+  }
+
+  __device__ void load(const Operand<Src>& op, int64_t row0, int64_t k0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = bf16_to_f32(v[j]);
-        return;
+    for (int i = 0; i < PER; ++i) {
+      int r, k;
+      chunk_pos(i * kThreads + static_cast<int>(threadIdx.x), r, k);
+      const int64_t gr = row0 + r, gk = k0 + k;
+      // KC: rows are whole; K is a multiple of the chunk.  RC: R is a multiple of the chunk.
+      const bool ok = gr < op.R && gk < op.K;
+      const Src* src = op.p + (KC ? gr * op.ld + gk : gk * op.ld + gr);
+#pragma unroll
+      for (int s = 0; s < NP; ++s)
+#pragma unroll
+        for (int w = 0; w < WORDS; ++w)
+          reg[s][i][w] = ok ? *reinterpret_cast<const u32x4*>(src + s * op.plane + w * (16 / sizeof(Src)))
+                            : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  __device__ void store(E* lds) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      int r, k;
+      chunk_pos(i * kThreads + static_cast<int>(threadIdx.x), r, k);
+      E* dst = lds + (KC ? r * LD + k : k * LD + r);
+      if constexpr (SPLIT) {
+        E part[NS][EPC];
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          const f32x4 x = __builtin_bit_cast(f32x4, reg[0][i][w]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            E t[NS];
+            split_to<M, NS>(x[j], t);
+#pragma unroll
+            for (int s = 0; s < NS; ++s) part[s][4 * w + j] = t[s];
+          }
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) *reinterpret_cast<u32x4*>(dst + s * PLANE) = *reinterpret_cast<u32x4*>(part[s]);
+      } else {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) *reinterpret_cast<u32x4*>(dst + s * PLANE) = reg[s][i][0];
       }
-    } else {
-      if (r < R && k + 3 < K) {
-        f32x4 v = *reinterpret_cast<const f32x4*>(p + r * ld + k);
-        o[0] = v[0]; o[1] = v[1]; o[2] = v[2]; o[3] = v[3];
-        return;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = (r < R && k + j < K) ? to_f32(p[r * ld + k + j]) : 0.f;
-  }
-};
-
-struct LoadF32RC {  // float src[k * ld + row]
-  static constexpr bool KC = false;
-  const float* p; int64_t ld, R, K;
-  __device__ void load4(int64_t r, int64_t k, float* o) const {
-    if (k < K && r + 3 < R) {
-      f32x4 v = *reinterpret_cast<const f32x4*>(p + k * ld + r);
-      o[0] = v[0]; o[1] = v[1]; o[2] = v[2]; o[3] = v[3];
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) o[j] = (k < K && r + j < R) ? p[k * ld + r + j] : 0.f;
     }
   }
-};
 
-template <class InT>
-struct LoadInRC {  // input-dtype src[k * ld + row]
-  static constexpr bool KC = false;
-  const InT* p; int64_t ld, R, K;
-  __device__ void load4(int64_t r, int64_t k, float* o) const {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = (k < K && r + j < R) ? to_f32(p[k * ld + r + j]) : 0.f;
-  }
-};
-
-// L[t, c] = gamma[c] * x[t, c] * rstd[t], read as B(row = c, k = t).
-template <class InT>
-struct LoadNormRC {
-  static constexpr bool KC = false;
-  const InT* x; const InT* gamma; const float* rstd; int64_t ld, R, K;
-  __device__ void load4(int64_t r, int64_t k, float* o) const {
-    const float rs = (k < K) ? rstd[k] : 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      o[j] = (k < K && r + j < R) ? to_f32(gamma[r + j]) * (to_f32(x[k * ld + r + j]) * rs) : 0.f;
+  // Fragment of atom rows n0 .. n0+31 for the MFMA step at k = kk (natural k order).
+  __device__ static F frag(const E* lds, int s, int n0, int kk) {
+    const int lane = threadIdx.x % kWave;
+    const E* plane = lds + s * PLANE;
+    if constexpr (KC) {
+      return lds_frag<M>(plane + (n0 + lane % 32) * LD + kk + (lane / 32) * M::KPL);
+    } else if constexpr (sizeof(E) == 2) {
+      return __builtin_bit_cast(F, tr_frag(plane, LD, kk, n0));
+    } else {
+      return plane[(kk + lane / 32) * LD + n0 + lane % 32];
+    }
   }
 };
 
@@ -141,57 +167,14 @@ struct EpiStore {  // out[m * ld + n] (+ chunk offset)
 };
 
 // ------------------------------------------------------------------- kernel
-template <class M, int NS>
-__device__ __forceinline__ void put(typename M::elem* base, int64_t stride_plane, float x) {
-  typename M::elem part[NS];
-  split_to<M, NS>(x, part);
-#pragma unroll
-  for (int s = 0; s < NS; ++s) base[s * stride_plane] = part[s];
-}
-
-template <class M, int NS, class L, int ROWS>
-struct Stage {
-  static constexpr int LD = BK + Pad<M>::v;
-  static constexpr int GROUPS = ROWS * BK / 4 / kThreads;
-  float reg[GROUPS][4];
-  __device__ void load(const L& ld, int64_t row0, int64_t k0) {
-#pragma unroll
-    for (int g = 0; g < GROUPS; ++g) {
-      const int idx = g * kThreads + threadIdx.x;
-      if constexpr (L::KC) {
-        ld.load4(row0 + idx / (BK / 4), k0 + (idx % (BK / 4)) * 4, reg[g]);
-      } else {
-        ld.load4(row0 + (idx % (ROWS / 4)) * 4, k0 + idx / (ROWS / 4), reg[g]);
-      }
-    }
-  }
-  __device__ void store(typename M::elem* lds) const {
-    constexpr int64_t plane = static_cast<int64_t>(ROWS) * LD;
-#pragma unroll
-    for (int g = 0; g < GROUPS; ++g) {
-      const int idx = g * kThreads + threadIdx.x;
-      if constexpr (L::KC) {
-        const int r = idx / (BK / 4), k = (idx % (BK / 4)) * 4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) put<M, NS>(lds + r * LD + k + j, plane, reg[g][j]);
-      } else {
-        const int r = (idx % (ROWS / 4)) * 4, k = idx / (ROWS / 4);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) put<M, NS>(lds + (r + j) * LD + k, plane, reg[g][j]);
-      }
-    }
-  }
-};
-
-template <class M, int NSA, int NSB, class LA, class LB, class EPI>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(LA la, LB lb, EPI epi, int64_t k_chunk,
-                                                        int64_t K) {
+template <class M, class SA, class SB, class EPI>
+__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(Operand<typename SA::Src_t> A,
+                                                           Operand<typename SB::Src_t> B, EPI epi,
+                                                           int64_t k_chunk, int64_t K) {
   typedef typename M::elem E;
-  constexpr int LD = BK + Pad<M>::v;
-  __shared__ __attribute__((aligned(16))) E As[NSA * BM * LD];
-  __shared__ __attribute__((aligned(16))) E Bs[NSB * BN * LD];
+  constexpr int STAGE = SA::BYTES + SB::BYTES;
+  __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
 
-  const int lane = threadIdx.x % kWave;
   const int wv = threadIdx.x / kWave;
   const int wm = wv / 2, wn = wv % 2;
   const int64_t m0 = static_cast<int64_t>(blockIdx.y) * BM;
@@ -207,37 +190,37 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(LA la, LB lb, EPI epi, i
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-  Stage<M, NSA, LA, BM> sa;
-  Stage<M, NSB, LB, BN> sb;
+  typename SA::Slab sa;
+  typename SB::Slab sb;
+  constexpr int NSA = SA::Slab::NS_, NSB = SB::Slab::NS_;
   constexpr int NSMAX = NSA > NSB ? NSA : NSB;
-  const int row = lane % 32, kofs = (lane / 32) * M::KPL;
 
   if (kbeg < kend) {
-    sa.load(la, m0, kbeg);
-    sb.load(lb, n0, kbeg);
+    sa.load(A, m0, kbeg);
+    sb.load(B, n0, kbeg);
   }
-  for (int64_t k0 = kbeg; k0 < kend; k0 += BK) {
-    __syncthreads();
-    sa.store(As);
-    sb.store(Bs);
-    __syncthreads();
+  int buf = 0;
+  for (int64_t k0 = kbeg; k0 < kend; k0 += BK, buf ^= 1) {
+    E* as = reinterpret_cast<E*>(lds + buf * STAGE);
+    E* bs = reinterpret_cast<E*>(lds + buf * STAGE + SA::BYTES);
+    sa.store(as);
+    sb.store(bs);
+    __syncthreads();  // also orders the reads of this buffer two steps ago before the stores above
     if (k0 + BK < kend) {
-      sa.load(la, m0, k0 + BK);
-      sb.load(lb, n0, k0 + BK);
+      sa.load(A, m0, k0 + BK);
+      sb.load(B, n0, k0 + BK);
     }
 #pragma unroll
-    for (int ks = 0; ks < BK / M::K; ++ks) {
+    for (int kk = 0; kk < BK; kk += M::K) {
       typename M::frag af[NSA][2], bfr[NSB][2];
 #pragma unroll
       for (int s = 0; s < NSA; ++s)
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
-          af[s][a] = lds_frag<M>(As + s * BM * LD + (wm * 64 + a * 32 + row) * LD + ks * M::K + kofs);
+        for (int a = 0; a < 2; ++a) af[s][a] = SA::Slab::frag(as, s, wm * 64 + a * 32, kk);
 #pragma unroll
       for (int s = 0; s < NSB; ++s)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-          bfr[s][b] = lds_frag<M>(Bs + s * BN * LD + (wn * 64 + b * 32 + row) * LD + ks * M::K + kofs);
+        for (int b = 0; b < 2; ++b) bfr[s][b] = SB::Slab::frag(bs, s, wn * 64 + b * 32, kk);
 #pragma unroll
       for (int s1 = 0; s1 < NSA; ++s1)
 #pragma unroll
@@ -251,6 +234,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(LA la, LB lb, EPI epi, i
     }
   }
   // C[r]: row 8*(r/4) + 4*(lane/32) + r%4 of the atom, column lane%32.
+  const int lane = threadIdx.x % kWave;
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -263,15 +247,22 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(LA la, LB lb, EPI epi, i
       }
 }
 
-template <class M, int NSA, int NSB, class LA, class LB, class EPI>
-hipError_t run_gemm(LA la, LB lb, EPI epi, int64_t Mrows, int64_t Ncols, int64_t K, int chunks,
-                    hipStream_t st) {
+// Operand description: MFMA type, planes, orientation, rows per tile, source element.
+template <class M, int NS, bool KC, int ROWS, class Src>
+struct Side {
+  struct Slab : SlabT<M, NS, KC, ROWS, Src> { static constexpr int NS_ = NS; };
+  typedef Src Src_t;
+  static constexpr int BYTES = Slab::BYTES;
+};
+
+template <class M, class SA, class SB, class EPI>
+hipError_t run_gemm(Operand<typename SA::Src_t> A, Operand<typename SB::Src_t> B, EPI epi, int64_t Mrows,
+                    int64_t Ncols, int64_t K, int chunks, hipStream_t st) {
   const int64_t per = ((K + chunks - 1) / chunks + BK - 1) / BK * BK;
   const int nchunks = static_cast<int>((K + per - 1) / per);
   dim3 grid(static_cast<unsigned>((Ncols + BN - 1) / BN), static_cast<unsigned>((Mrows + BM - 1) / BM),
             static_cast<unsigned>(nchunks));
-  hipLaunchKernelGGL((gemm_kernel<M, NSA, NSB, LA, LB, EPI>), grid, dim3(kThreads), 0, st, la, lb,
-                     epi, per, K);
+  hipLaunchKernelGGL((gemm_kernel<M, SA, SB, EPI>), grid, dim3(kThreads), 0, st, A, B, epi, per, K);
   return hipGetLastError();
 }
 
@@ -303,61 +294,70 @@ __global__ __launch_bounds__(256) void chunk_sum_kernel(const float* __restrict_
 hipError_t launch_kv_up(const Shape& s, const float* L, const void* w, void* k_nope, void* v,
                         hipStream_t st) {
   const int64_t N = static_cast<int64_t>(s.h) * s.C();
-  LoadF32KC la{L, s.d_kv, s.T, s.d_kv};
+  const int64_t w0 = static_cast<int64_t>(s.head_lo) * s.C() * s.d_kv;
+  const int64_t pk = s.T * s.h * s.d_nope, pv = s.T * s.h * s.d_v;
+  Operand<float> A{L, s.d_kv, 0, s.T, s.d_kv};
   if (s.bf16) {
-    LoadInKC<bf16_t> lb{static_cast<const bf16_t*>(w) + static_cast<int64_t>(s.head_lo) * s.C() * s.d_kv,
-                        s.d_kv, N, s.d_kv};
-    const int64_t pk = s.T * s.h * s.d_nope, pv = s.T * s.h * s.d_v;
+    typedef Side<MmaBf16, 2, true, BM, float> SA;
+    typedef Side<MmaBf16, 1, true, BN, bf16_t> SB;
+    Operand<bf16_t> B{static_cast<const bf16_t*>(w) + w0, s.d_kv, 0, N, s.d_kv};
     if (s.split) {
       EpiKvUp<half_t, 2> e{static_cast<half_t*>(k_nope), static_cast<half_t*>(v), s.T, static_cast<int>(N),
                            s.C(), s.d_nope, s.d_v, s.h, pk, pv};
-      return run_gemm<MmaBf16, 2, 1>(la, lb, e, s.T, N, s.d_kv, 1, st);
+      return run_gemm<MmaBf16, SA, SB>(A, B, e, s.T, N, s.d_kv, 1, st);
     }
     EpiKvUp<half_t, 1> e{static_cast<half_t*>(k_nope), static_cast<half_t*>(v), s.T, static_cast<int>(N),
                          s.C(), s.d_nope, s.d_v, s.h, pk, pv};
-    return run_gemm<MmaBf16, 2, 1>(la, lb, e, s.T, N, s.d_kv, 1, st);
+    return run_gemm<MmaBf16, SA, SB>(A, B, e, s.T, N, s.d_kv, 1, st);
   }
-  LoadInKC<float> lb{static_cast<const float*>(w) + static_cast<int64_t>(s.head_lo) * s.C() * s.d_kv,
-                     s.d_kv, N, s.d_kv};
+  typedef Side<MmaF32, 1, true, BM, float> SA;
+  typedef Side<MmaF32, 1, true, BN, float> SB;
+  Operand<float> B{static_cast<const float*>(w) + w0, s.d_kv, 0, N, s.d_kv};
   EpiKvUp<float, 1> e{static_cast<float*>(k_nope), static_cast<float*>(v), s.T, static_cast<int>(N),
                       s.C(), s.d_nope, s.d_v, s.h, 0, 0};
-  return run_gemm<MmaF32, 1, 1>(la, lb, e, s.T, N, s.d_kv, 1, st);
+  return run_gemm<MmaF32, SA, SB>(A, B, e, s.T, N, s.d_kv, 1, st);
 }
 
-hipError_t launch_fold_dl(const Shape& s, const float* dkv, const void* w, float* dL,
-                          hipStream_t st) {
+hipError_t launch_fold_dl(const Shape& s, const void* dkv, const void* w, float* dL, hipStream_t st) {
   const int64_t Kd = static_cast<int64_t>(s.h) * s.C();
-  LoadF32KC la{dkv, Kd, s.T, Kd};
+  const int64_t w0 = static_cast<int64_t>(s.head_lo) * s.C() * s.d_kv;
   EpiStore e{dL, s.T, s.d_kv, s.d_kv, 0};
   if (s.bf16) {
-    LoadInRC<bf16_t> lb{static_cast<const bf16_t*>(w) + static_cast<int64_t>(s.head_lo) * s.C() * s.d_kv,
-                        s.d_kv, s.d_kv, Kd};
-    return run_gemm<MmaBf16, 2, 1>(la, lb, e, s.T, s.d_kv, Kd, 1, st);
+    typedef Side<MmaBf16, 2, true, BM, bf16_t> SA;    // dKV[t, n]: bf16 hi/lo planes
+    typedef Side<MmaBf16, 1, false, BN, bf16_t> SB;   // W_r[n, k]: reduction over n strides memory
+    Operand<bf16_t> A{static_cast<const bf16_t*>(dkv), Kd, s.T * Kd, s.T, Kd};
+    Operand<bf16_t> B{static_cast<const bf16_t*>(w) + w0, s.d_kv, 0, s.d_kv, Kd};
+    return run_gemm<MmaBf16, SA, SB>(A, B, e, s.T, s.d_kv, Kd, 1, st);
   }
-  LoadInRC<float> lb{static_cast<const float*>(w) + static_cast<int64_t>(s.head_lo) * s.C() * s.d_kv,
-                     s.d_kv, s.d_kv, Kd};
-  return run_gemm<MmaF32, 1, 1>(la, lb, e, s.T, s.d_kv, Kd, 1, st);
+  typedef Side<MmaF32, 1, true, BM, float> SA;
+  typedef Side<MmaF32, 1, false, BN, float> SB;
+  Operand<float> A{static_cast<const float*>(dkv), Kd, 0, s.T, Kd};
+  Operand<float> B{static_cast<const float*>(w) + w0, s.d_kv, 0, s.d_kv, Kd};
+  return run_gemm<MmaF32, SA, SB>(A, B, e, s.T, s.d_kv, Kd, 1, st);
 }
 
 size_t fold_dw_partial_floats(const Shape& s) {
   return static_cast<size_t>(dw_chunks(s)) * s.h * s.C() * s.d_kv;
 }
 
-hipError_t launch_fold_dw(const Shape& s, const float* dkv, const void* latent, const void* gamma,
-                          const float* rstd, float* partial, float* d_w, hipStream_t st) {
+hipError_t launch_fold_dw(const Shape& s, const void* dkv, const void* lplanes, float* partial, float* d_w,
+                          hipStream_t st) {
   const int64_t Mr = static_cast<int64_t>(s.h) * s.C();
   const int chunks = dw_chunks(s);
-  LoadF32RC la{dkv, Mr, Mr, s.T};
   EpiStore e{partial, Mr, s.d_kv, s.d_kv, Mr * s.d_kv};
   hipError_t err;
   if (s.bf16) {
-    LoadNormRC<bf16_t> lb{static_cast<const bf16_t*>(latent), static_cast<const bf16_t*>(gamma), rstd,
-                          s.d_kv, s.d_kv, s.T};
-    err = run_gemm<MmaBf16, 2, 2>(la, lb, e, Mr, s.d_kv, s.T, chunks, st);
+    typedef Side<MmaBf16, 2, false, BM, bf16_t> SA;   // dKV[t, n] read as A(row = n, k = t)
+    typedef Side<MmaBf16, 2, false, BN, bf16_t> SB;   // L[t, c] read as B(row = c, k = t)
+    Operand<bf16_t> A{static_cast<const bf16_t*>(dkv), Mr, s.T * Mr, Mr, s.T};
+    Operand<bf16_t> B{static_cast<const bf16_t*>(lplanes), s.d_kv, s.T * s.d_kv, s.d_kv, s.T};
+    err = run_gemm<MmaBf16, SA, SB>(A, B, e, Mr, s.d_kv, s.T, chunks, st);
   } else {
-    LoadNormRC<float> lb{static_cast<const float*>(latent), static_cast<const float*>(gamma), rstd,
-                         s.d_kv, s.d_kv, s.T};
-    err = run_gemm<MmaF32, 1, 1>(la, lb, e, Mr, s.d_kv, s.T, chunks, st);
+    typedef Side<MmaF32, 1, false, BM, float> SA;
+    typedef Side<MmaF32, 1, false, BN, float> SB;
+    Operand<float> A{static_cast<const float*>(dkv), Mr, 0, Mr, s.T};
+    Operand<float> B{static_cast<const float*>(lplanes), s.d_kv, 0, s.d_kv, s.T};
+    err = run_gemm<MmaF32, SA, SB>(A, B, e, Mr, s.d_kv, s.T, chunks, st);
   }
   if (err != hipSuccess) return err;
   const int64_t n = Mr * s.d_kv;

@@ -31,17 +31,20 @@ hipError_t launch_bwd_dot(const Shape& s, const float* o, const void* d_o, float
                           hipStream_t st);
 hipError_t launch_attn_bwd_dkdv(const Shape& s, const void* q, const void* k_nope,
                                 const void* k_pe, const void* v, const float* lse,
-                                const float* delta, const void* d_o, float* dkv,
+                                const float* delta, const void* d_o, void* dkv,
                                 float* dk_pe_part, hipStream_t st);
 hipError_t launch_attn_bwd_dq(const Shape& s, const void* q, const void* k_nope, const void* k_pe,
                               const void* v, const float* lse, const float* delta,
                               const void* d_o, float* dq, hipStream_t st);
 hipError_t launch_head_sum(const Shape& s, const float* part, float* out, hipStream_t st);
-hipError_t launch_fold_dl(const Shape& s, const float* dkv, const void* w, float* dL,
-                          hipStream_t st);
+// dkv: [T, h, d_nope + d_v] as bf16 hi/lo planes (bf16 inputs) or one fp32 plane.
+hipError_t launch_fold_dl(const Shape& s, const void* dkv, const void* w, float* dL, hipStream_t st);
 size_t fold_dw_partial_floats(const Shape& s);
-hipError_t launch_fold_dw(const Shape& s, const float* dkv, const void* latent, const void* gamma,
-                          const float* rstd, float* partial, float* d_w, hipStream_t st);
+// lplanes: the normalised latent [T, d_kv] in the same plane format (launch_norm_planes).
+hipError_t launch_fold_dw(const Shape& s, const void* dkv, const void* lplanes, float* partial, float* d_w,
+                          hipStream_t st);
+hipError_t launch_norm_planes(const Shape& s, const void* latent, const void* gamma, const float* rstd,
+                              void* lplanes, hipStream_t st);
 size_t norm_bwd_partial_floats(const Shape& s);
 hipError_t launch_norm_bwd(const Shape& s, const float* dL, const void* latent, const void* gamma,
                            const float* rstd, float* d_latent, float* dgamma_part, float* d_gamma,

@@ -134,15 +134,65 @@ __global__ __launch_bounds__(kNormBlock) void rmsnorm_bwd_kernel(
   }
 }
 
-// out[c] = sum_p part[p, c] in increasing p (deterministic).
+// out[c] = sum_p part[p, c] in a fixed order (deterministic): a workgroup owns
+// kSumCols columns; thread group g adds rows g, g + kSumGroups, ... and the
+// group sums are added in increasing g.
+constexpr int kSumCols = 32, kSumGroups = kNormBlock / kSumCols;
 __global__ __launch_bounds__(kNormBlock) void column_sum_kernel(const float* __restrict__ part,
                                                                 float* __restrict__ out, int rows,
                                                                 int cols) {
-  const int c = blockIdx.x * kNormBlock + threadIdx.x;
-  if (c >= cols) return;
+  __shared__ float red[kSumGroups][kSumCols];
+  const int cl = threadIdx.x % kSumCols, g = threadIdx.x / kSumCols;
+  const int c = blockIdx.x * kSumCols + cl;
   float s = 0.f;
-  for (int p = 0; p < rows; ++p) s += part[static_cast<int64_t>(p) * cols + c];
-  out[c] = s;
+  if (c < cols)
+    for (int p = g; p < rows; p += kSumGroups) s += part[static_cast<int64_t>(p) * cols + c];
+  red[g][cl] = s;
+  __syncthreads();
+  if (g == 0 && c < cols) {
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < kSumGroups; ++i) t += red[i][cl];
+    out[c] = t;
+  }
+}
+
+// L = gamma * x * rstd, the normalised latent rebuilt from the saved rstd, as
+// NS planes of the MFMA element type of the W_kv_b-gradient GEMM (bf16 hi + lo,
+// or one fp32 plane); planes are `plane` elements apart.
+template <class M, int NS, class InT, int D>
+__global__ __launch_bounds__(kNormBlock) void norm_planes_kernel(const InT* __restrict__ x,
+                                                                 const InT* __restrict__ gamma,
+                                                                 const float* __restrict__ rstd,
+                                                                 typename M::elem* __restrict__ out,
+                                                                 int64_t T, int64_t plane) {
+  typedef typename M::elem E;
+  constexpr int EPL = D / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + threadIdx.x / kWave;
+  if (t >= T) return;
+  float v[EPL], g[EPL];
+  load_run<EPL>(x + t * D + lane * EPL, v);
+  load_run<EPL>(gamma + lane * EPL, g);
+  const float r = rstd[t];
+  E part[NS][EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    E p[NS];
+    split_to<M, NS>(g[j] * (v[j] * r), p);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) part[s][j] = p[s];
+  }
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    E* dst = out + s * plane + t * D + lane * EPL;
+    if constexpr (EPL * sizeof(E) == 16) {
+      *reinterpret_cast<u16x8*>(dst) = *reinterpret_cast<const u16x8*>(part[s]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) dst[j] = part[s][j];
+    }
+  }
 }
 
 constexpr int kNormBwdBlocks = 512;
@@ -168,8 +218,8 @@ hipError_t norm_bwd_t(const Shape& s, const float* dL, const void* x, const void
   const int blocks = norm_bwd_blocks(s);
   hipLaunchKernelGGL((rmsnorm_bwd_kernel<InT, D>), dim3(blocks), dim3(kNormBlock), 0, st, dL,
                      static_cast<const InT*>(x), static_cast<const InT*>(g), rstd, dx, part, s.T);
-  hipLaunchKernelGGL(column_sum_kernel, dim3((D + kNormBlock - 1) / kNormBlock), dim3(kNormBlock),
-                     0, st, part, dgamma, blocks, D);
+  hipLaunchKernelGGL(column_sum_kernel, dim3((D + kSumCols - 1) / kSumCols), dim3(kNormBlock), 0, st, part,
+                     dgamma, blocks, D);
   return hipGetLastError();
 }
 
@@ -180,6 +230,24 @@ hipError_t launch_norm_fwd(const Shape& s, const void* x, const void* g, float* 
   if (s.bf16 && s.d_kv == 512) return norm_fwd_t<bf16_t, 512>(s, x, g, L, rstd, st);
   if (!s.bf16 && s.d_kv == 64) return norm_fwd_t<float, 64>(s, x, g, L, rstd, st);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_norm_planes(const Shape& s, const void* x, const void* g, const float* rstd, void* out,
+                              hipStream_t st) {
+  const unsigned blocks = static_cast<unsigned>((s.T + kRowsPerBlock - 1) / kRowsPerBlock);
+  const int64_t plane = s.T * s.d_kv;
+  if (s.bf16 && s.d_kv == 512) {
+    hipLaunchKernelGGL((norm_planes_kernel<MmaBf16, 2, bf16_t, 512>), dim3(blocks), dim3(kNormBlock), 0, st,
+                       static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(g), rstd,
+                       static_cast<bf16_t*>(out), s.T, plane);
+  } else if (!s.bf16 && s.d_kv == 64) {
+    hipLaunchKernelGGL((norm_planes_kernel<MmaF32, 1, float, 64>), dim3(blocks), dim3(kNormBlock), 0, st,
+                       static_cast<const float*>(x), static_cast<const float*>(g), rstd, static_cast<float*>(out),
+                       s.T, plane);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 size_t norm_bwd_partial_floats(const Shape& s) {
