@@ -74,16 +74,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const T* base, int bytes)
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), 0, bytes, 0x00020000);
 }
 
-// KPL elements of a global row as an operand fragment (zero when !valid).
-template <class M, class Src>
-__device__ __forceinline__ typename M::frag load_frag(const Src* p, bool valid) {
-  typedef typename M::elem E;
-  E tmp[M::KPL];
-#pragma unroll
-  for (int j = 0; j < M::KPL; ++j) tmp[j] = M::from_f32(valid ? to_f32(p[j]) : 0.f);
-  return *reinterpret_cast<typename M::frag*>(tmp);
-}
-
 // ============================================================ dK / dV kernel
 template <class InT, class M, int NS, int DN, int DR, int DV>
 struct Dkdv {
@@ -111,7 +101,15 @@ struct Dkdv {
   static constexpr int IQ = (QCH + kThreads - 1) / kThreads, IO = (OCH + kThreads - 1) / kThreads;
   static_assert(DQK % IPC == 0 && DV % IPC == 0, "rows of whole chunks");
 
-  struct Regs { u32x4 q[IQ]; u32x4 o[IO]; float lse2, dlt; };
+  struct Regs { u32x4 q[IQ]; u32x4 o[IO]; float lse2, dlt; };  // lse2: natural-log lse until stored
+
+  // Stationary operands of one wavefront: its 32 keys' K (nope hi plane, rope)
+  // and V (hi plane) fragments in registers; the lo planes are read from LDS.
+  struct Stat {
+    F kf[KS_N], kr[KS_QK - KS_N], vf[KS_V];
+    const E* klo_row; const E* vlo_row;
+  };
+  struct Acc { f32x16 dk[NKT], dvt[NVT]; };
 
   __device__ static void load(const BwdArgs& a, int b, int head, int64_t q0, Regs& R) {
     const int nq = static_cast<int>(a.S - q0 < BQ ? a.S - q0 : BQ);
@@ -125,18 +123,19 @@ struct Dkdv {
     for (int i = 0; i < IQ; ++i) {
       const int c = i * kThreads + tid;
       const int r = c / (DQK / IPC), j = c % (DQK / IPC);
-      R.q[i] = (c < QCH) ? __builtin_amdgcn_raw_buffer_load_b128(rq, r * qrow_b + j * 16, 0, 0) : u32x4{};
+      if (QCH % kThreads == 0 || c < QCH) R.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, r * qrow_b + j * 16, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < IO; ++i) {
       const int c = i * kThreads + tid;
       const int r = c / (DV / IPC), j = c % (DV / IPC);
-      R.o[i] = (c < OCH) ? __builtin_amdgcn_raw_buffer_load_b128(ro, r * orow_b + j * 16, 0, 0) : u32x4{};
+      if (OCH % kThreads == 0 || c < OCH) R.o[i] = __builtin_amdgcn_raw_buffer_load_b128(ro, r * orow_b + j * 16, 0, 0);
     }
+    // Statistics of the block's queries; rows past the sequence read as zero.
     const int t = tid % BQ;
-    const int64_t si = (static_cast<int64_t>(b) * a.h + head) * a.S + q0 + t;
-    R.lse2 = t < nq ? a.lse[si] * kLog2e : 0.f;
-    R.dlt = t < nq ? a.delta[si] : 0.f;
+    const int64_t si0 = (static_cast<int64_t>(b) * a.h + head) * a.S + q0;
+    R.lse2 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.lse + si0, nq * 4), t * 4, 0, 0));
+    R.dlt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.delta + si0, nq * 4), t * 4, 0, 0));
   }
 
   __device__ static void store(const Regs& R, char* buf) {
@@ -149,7 +148,7 @@ struct Dkdv {
 #pragma unroll
     for (int i = 0; i < IQ; ++i) {
       const int c = i * kThreads + tid;
-      if (c >= QCH) continue;
+      if (QCH % kThreads != 0 && c >= QCH) continue;
       const int r = c / (DQK / IPC), col = (c % (DQK / IPC)) * IPC;
       E tmp[IPC];
       convert_chunk<E, InT>(R.q[i], tmp);
@@ -162,7 +161,7 @@ struct Dkdv {
 #pragma unroll
     for (int i = 0; i < IO; ++i) {
       const int c = i * kThreads + tid;
-      if (c >= OCH) continue;
+      if (OCH % kThreads != 0 && c >= OCH) continue;
       const int r = c / (DV / IPC), col = (c % (DV / IPC)) * IPC;
       E tmp[IPC];
       convert_chunk<E, InT>(R.o[i], tmp);
@@ -173,7 +172,7 @@ struct Dkdv {
       }
     }
     if (tid < BQ) {
-      st[tid] = R.lse2;
+      st[tid] = R.lse2 * kLog2e;
       st[BQ + tid] = R.dlt;
     }
   }
@@ -191,8 +190,120 @@ struct Dkdv {
     }
   }
 
+  // Fragment of a stationary K / V row held in memory as E (16-byte loads) or
+  // as the input type (converted).
+  template <class Src>
+  __device__ static F row_frag(const Src* p) {
+    if constexpr (std::is_same<Src, E>::value && sizeof(F) == 16) {
+      return *reinterpret_cast<const F*>(p);
+    } else {
+      E tmp[M::KPL];
+#pragma unroll
+      for (int j = 0; j < M::KPL; ++j) tmp[j] = M::from_f32(to_f32(p[j]));
+      return *reinterpret_cast<F*>(tmp);
+    }
+  }
+
+  // One block of BQ queries starting at q0 against the wavefront's 32 keys
+  // from wk0 (lane column `col`).  MASK: the block may cross the causal
+  // diagonal or the end of the sequence (and may lie wholly before the keys).
+  template <bool MASK>
+  __device__ static void block(const BwdArgs& a, const char* buf, int64_t q0, int64_t wk0, const Stat& K,
+                               Acc& acc) {
+    const int lane = threadIdx.x % kWave;
+    const int hf = lane / 32, col = lane % 32;
+    if (MASK && q0 + BQ - 1 < wk0) return;  // every query of the block precedes these keys
+    const E* Qr = reinterpret_cast<const E*>(buf);
+    const E* Qt = reinterpret_cast<const E*>(buf + QR_B);
+    const E* Or = reinterpret_cast<const E*>(buf + QR_B + QT_B);
+    const E* Ot = reinterpret_cast<const E*>(buf + QR_B + QT_B + OR_B);
+    const float* st = reinterpret_cast<const float*>(buf + QR_B + QT_B + OR_B + OT_B);
+
+    // S[q, key], dP[q, key]: rows = queries 8g + 4hf + i, column = key.  The
+    // two chains are interleaved so that each one's operand reads overlap the
+    // other's products.
+    f32x16 sc, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { sc[r] = 0.f; dp[r] = 0.f; }
+    const E* qrow = Qr + col * LQR + hf * M::KPL;
+    const E* orow = Or + col * LOR + hf * M::KPL;
+    static_assert(KS_N == KS_V, "nope and value widths interleave step for step");
+#pragma unroll
+    for (int s = 0; s < KS_N; ++s) {
+      const F qa = lds_frag<M>(qrow + s * M::K);
+      const F oa = lds_frag<M>(orow + s * M::K);
+      sc = M::mma(qa, K.kf[s], sc);
+      dp = M::mma(oa, K.vf[s], dp);
+      if constexpr (NS == 2) {
+        sc = M::mma(qa, lds_frag<M>(K.klo_row + s * M::K), sc);
+        dp = M::mma(oa, lds_frag<M>(K.vlo_row + s * M::K), dp);
+      }
+    }
+#pragma unroll
+    for (int s = KS_N; s < KS_QK; ++s) sc = M::mma(lds_frag<M>(qrow + s * M::K), K.kr[s - KS_N], sc);
+
+    // P = exp(s - lse) and dS = P (dP - delta), per query row of the block.
+    const int rel = static_cast<int>(wk0 - q0) + col;  // key - q0
+    const int nq = static_cast<int>(a.S - q0 < BQ ? a.S - q0 : BQ);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(st + 8 * g + 4 * hf);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(st + BQ + 8 * g + 4 * hf);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;
+        float p = __builtin_amdgcn_exp2f(fmaf(sc[r], a.scale_log2, -l4[i]));
+        if constexpr (MASK) {
+          const int qi = 8 * g + 4 * hf + i;
+          if (rel > qi || qi >= nq) p = 0.f;
+        }
+        sc[r] = p;
+        dp[r] = p * (dp[r] - d4[i]);
+      }
+    }
+
+    // dV^T[dv, key] += dO^T P ; dK^T[d, key] += q^T dS   (k = queries)
+#pragma unroll
+    for (int stp = 0; stp < STEPS; ++stp) {
+      E ph[NS][M::KPL], dh[NS][M::KPL];
+#pragma unroll
+      for (int j = 0; j < M::KPL; ++j) {
+        E t1[NS], t2[NS];
+        split_to<M, NS>(sc[stp * M::KPL + j], t1);
+        split_to<M, NS>(dp[stp * M::KPL + j], t2);
+#pragma unroll
+        for (int p = 0; p < NS; ++p) { ph[p][j] = t1[p]; dh[p][j] = t2[p]; }
+      }
+#pragma unroll
+      for (int n = 0; n < NVT; ++n) {
+        const F oa = tr_frag(Ot, Or, LOT, LOR, stp, n * 32);
+#pragma unroll
+        for (int p = 0; p < NS; ++p) acc.dvt[n] = M::mma(oa, *reinterpret_cast<F*>(ph[p]), acc.dvt[n]);
+      }
+#pragma unroll
+      for (int n = 0; n < NKT; ++n) {
+        const F qa = tr_frag(Qt, Qr, LQT, LQR, stp, n * 32);
+#pragma unroll
+        for (int p = 0; p < NS; ++p) acc.dk[n] = M::mma(qa, *reinterpret_cast<F*>(dh[p]), acc.dk[n]);
+      }
+    }
+  }
+
+  // Publish the staged block `it`, start loading the next one, compute.
+  template <bool MASK>
+  __device__ static void step(const BwdArgs& a, char* lds, int it, int nqb, int b, int head, int64_t k0,
+                              int64_t wk0, Regs& R, const Stat& K, Acc& acc) {
+    const int64_t q0 = k0 + static_cast<int64_t>(it) * BQ;
+    char* buf = lds + (it & 1) * BUF_BYTES;
+    store(R, buf);
+    __syncthreads();
+    if (it + 1 < nqb) load(a, b, head, q0 + BQ, R);
+    block<MASK>(a, buf, q0, wk0, K, acc);
+  }
+
   __device__ static void run(const BwdArgs& a, char* lds) {
-    const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int hf = lane / 32, col = lane % 32;
     // Longest key blocks (smallest key index: most queries) first.
     const int nbh = a.B * a.h;
@@ -203,19 +314,20 @@ struct Dkdv {
     const int64_t wk0 = k0 + wv * 32;
     const int64_t key = wk0 + col;  // this lane's key (B-operand column)
     const bool kvalid = key < a.S;
+    // Keys past the sequence use row 0's values: every product they enter is
+    // masked and their gradients are not stored.
     const int64_t kc = kvalid ? key : 0;
 
-    // Stationary K (nope hi/lo planes, rope) and V (hi/lo planes) fragments.
+    Stat K;
     const E* kn = static_cast<const E*>(a.k_nope) + ((b * a.S + kc) * a.h + head) * DN;
     const E* vg = static_cast<const E*>(a.v) + ((b * a.S + kc) * a.h + head) * DV;
     const InT* kp = static_cast<const InT*>(a.k_pe) + (b * a.S + kc) * DR;
-    F kf[KS_N], kr[KS_QK - KS_N], vf[KS_V];
 #pragma unroll
-    for (int s = 0; s < KS_N; ++s) kf[s] = load_frag<M>(kn + s * M::K + hf * M::KPL, kvalid);
+    for (int s = 0; s < KS_N; ++s) K.kf[s] = row_frag(kn + s * M::K + hf * M::KPL);
 #pragma unroll
-    for (int s = 0; s < KS_V; ++s) vf[s] = load_frag<M>(vg + s * M::K + hf * M::KPL, kvalid);
+    for (int s = 0; s < KS_V; ++s) K.vf[s] = row_frag(vg + s * M::K + hf * M::KPL);
 #pragma unroll
-    for (int s = 0; s < KS_QK - KS_N; ++s) kr[s] = load_frag<M>(kp + s * M::K + hf * M::KPL, kvalid);
+    for (int s = 0; s < KS_QK - KS_N; ++s) K.kr[s] = row_frag(kp + s * M::K + hf * M::KPL);
     E* klo = reinterpret_cast<E*>(lds + 2 * BUF_BYTES);
     E* vlo = reinterpret_cast<E*>(lds + 2 * BUF_BYTES + LO_B);
     if constexpr (NS == 2) {
@@ -240,103 +352,34 @@ struct Dkdv {
         *reinterpret_cast<u32x4*>(vlo + r * LLO + j * EPC) = __builtin_amdgcn_raw_buffer_load_b128(rv, r * vrb + j * 16, 0, 0);
       }
     }
-    const E* klo_row = klo + (wv * 32 + col) * LLO + hf * M::KPL;  // this lane's key
-    const E* vlo_row = vlo + (wv * 32 + col) * LLO + hf * M::KPL;
+    K.klo_row = klo + (wv * 32 + col) * LLO + hf * M::KPL;  // this lane's key
+    K.vlo_row = vlo + (wv * 32 + col) * LLO + hf * M::KPL;
 
-    f32x16 dk[NKT], dvt[NVT];
+    Acc acc;
 #pragma unroll
     for (int n = 0; n < NKT; ++n)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dk[n][r] = 0.f;
+      for (int r = 0; r < 16; ++r) acc.dk[n][r] = 0.f;
 #pragma unroll
     for (int n = 0; n < NVT; ++n)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dvt[n][r] = 0.f;
+      for (int r = 0; r < 16; ++r) acc.dvt[n][r] = 0.f;
 
+    // Query blocks from the diagonal: the first BK / BQ cross the workgroup's
+    // keys, the ones after them up to the last whole block need no mask, and
+    // a ragged last block is masked again.
     const int nqb = static_cast<int>((a.S - k0 + BQ - 1) / BQ);
+    const int ndiag = nqb < BK / BQ ? nqb : BK / BQ;
+    const int nfull = static_cast<int>((a.S - k0) / BQ);
+    const int nmid = nfull > ndiag ? nfull : ndiag;
     Regs R;
     load(a, b, head, k0, R);
-    for (int it = 0; it < nqb; ++it) {
-      const int64_t q0 = k0 + static_cast<int64_t>(it) * BQ;
-      char* buf = lds + (it & 1) * BUF_BYTES;
-      store(R, buf);
-      __syncthreads();
-      if (it + 1 < nqb) load(a, b, head, q0 + BQ, R);
-      if (q0 + BQ - 1 < wk0) continue;  // every query of the block precedes this wavefront's keys
-
-      const E* Qr = reinterpret_cast<const E*>(buf);
-      const E* Qt = reinterpret_cast<const E*>(buf + QR_B);
-      const E* Or = reinterpret_cast<const E*>(buf + QR_B + QT_B);
-      const E* Ot = reinterpret_cast<const E*>(buf + QR_B + QT_B + OR_B);
-      const float* st = reinterpret_cast<const float*>(buf + QR_B + QT_B + OR_B + OT_B);
-      const int nq = static_cast<int>(a.S - q0 < BQ ? a.S - q0 : BQ);
-
-      // S[q, key], dP[q, key]: rows = queries 8g + 4hf + i, column = key.
-      f32x16 sc, dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) { sc[r] = 0.f; dp[r] = 0.f; }
-      const E* qrow = Qr + col * LQR + hf * M::KPL;
-#pragma unroll
-      for (int s = 0; s < KS_N; ++s) {
-        const F qa = lds_frag<M>(qrow + s * M::K);
-        sc = M::mma(qa, kf[s], sc);
-        if constexpr (NS == 2) sc = M::mma(qa, lds_frag<M>(klo_row + s * M::K), sc);
-      }
-#pragma unroll
-      for (int s = KS_N; s < KS_QK; ++s) sc = M::mma(lds_frag<M>(qrow + s * M::K), kr[s - KS_N], sc);
-      const E* orow = Or + col * LOR + hf * M::KPL;
-#pragma unroll
-      for (int s = 0; s < KS_V; ++s) {
-        const F oa = lds_frag<M>(orow + s * M::K);
-        dp = M::mma(oa, vf[s], dp);
-        if constexpr (NS == 2) dp = M::mma(oa, lds_frag<M>(vlo_row + s * M::K), dp);
-      }
-
-      // P = exp(s - lse) and dS = P (dP - delta), per query row of the block.
-      const bool edge = q0 < wk0 + 31 || nq < BQ;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(st + 8 * g + 4 * hf);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(st + BQ + 8 * g + 4 * hf);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * g + i;
-          float p = __builtin_amdgcn_exp2f(fmaf(sc[r], a.scale_log2, -l4[i]));
-          if (edge) {
-            const int qi = 8 * g + 4 * hf + i;
-            if (key > q0 + qi || qi >= nq) p = 0.f;
-          }
-          sc[r] = p;
-          dp[r] = p * (dp[r] - d4[i]);
-        }
-      }
-
-      // dV^T[dv, key] += dO^T P ; dK^T[d, key] += q^T dS   (k = queries)
-#pragma unroll
-      for (int stp = 0; stp < STEPS; ++stp) {
-        E ph[NS][M::KPL], dh[NS][M::KPL];
-#pragma unroll
-        for (int j = 0; j < M::KPL; ++j) {
-          E t1[NS], t2[NS];
-          split_to<M, NS>(sc[stp * M::KPL + j], t1);
-          split_to<M, NS>(dp[stp * M::KPL + j], t2);
-#pragma unroll
-          for (int p = 0; p < NS; ++p) { ph[p][j] = t1[p]; dh[p][j] = t2[p]; }
-        }
-#pragma unroll
-        for (int n = 0; n < NVT; ++n) {
-          const F oa = tr_frag(Ot, Or, LOT, LOR, stp, n * 32);
-#pragma unroll
-          for (int p = 0; p < NS; ++p) dvt[n] = M::mma(oa, *reinterpret_cast<F*>(ph[p]), dvt[n]);
-        }
-#pragma unroll
-        for (int n = 0; n < NKT; ++n) {
-          const F qa = tr_frag(Qt, Qr, LQT, LQR, stp, n * 32);
-#pragma unroll
-          for (int p = 0; p < NS; ++p) dk[n] = M::mma(qa, *reinterpret_cast<F*>(dh[p]), dk[n]);
-        }
-      }
-    }
+    int it = 0;
+    for (; it < ndiag; ++it) step<true>(a, lds, it, nqb, b, head, k0, wk0, R, K, acc);
+    for (; it < nmid; ++it) step<false>(a, lds, it, nqb, b, head, k0, wk0, R, K, acc);
+    for (; it < nqb; ++it) step<true>(a, lds, it, nqb, b, head, k0, wk0, R, K, acc);
+    const f32x16* dk = acc.dk;
+    const f32x16* dvt = acc.dvt;
 
     if (!kvalid) return;
     // Lane holds column `key`; accumulator r is row 8(r/4) + 4hf + r%4 of its 32-row atom.
@@ -420,19 +463,19 @@ struct Dq {
     for (int i = 0; i < IK; ++i) {
       const int c = i * kThreads + tid;
       const int r = c / (DN / EPC), j = c % (DN / EPC);
-      R.k[i] = (c < KCH) ? __builtin_amdgcn_raw_buffer_load_b128(rk, r * krow_b + j * 16, 0, 0) : u32x4{};
+      if (KCH % kThreads == 0 || c < KCH) R.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, r * krow_b + j * 16, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < IP; ++i) {
       const int c = i * kThreads + tid;
       const int r = c / (DR / IPC), j = c % (DR / IPC);
-      R.p[i] = (c < PCH) ? __builtin_amdgcn_raw_buffer_load_b128(rp, r * prow_b + j * 16, 0, 0) : u32x4{};
+      if (PCH % kThreads == 0 || c < PCH) R.p[i] = __builtin_amdgcn_raw_buffer_load_b128(rp, r * prow_b + j * 16, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < IV; ++i) {
       const int c = i * kThreads + tid;
       const int r = c / (DV / EPC), j = c % (DV / EPC);
-      R.v[i] = (c < VCH) ? __builtin_amdgcn_raw_buffer_load_b128(rv, r * vrow_b + j * 16, 0, 0) : u32x4{};
+      if (VCH % kThreads == 0 || c < VCH) R.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, r * vrow_b + j * 16, 0, 0);
     }
   }
 
@@ -444,7 +487,7 @@ struct Dq {
 #pragma unroll
     for (int i = 0; i < IK; ++i) {
       const int c = i * kThreads + tid;
-      if (c >= KCH) continue;
+      if (KCH % kThreads != 0 && c >= KCH) continue;
       const int r = c / (DN / EPC), col = (c % (DN / EPC)) * EPC;
       *reinterpret_cast<u32x4*>(Kr + r * LKR + col) = R.k[i];
       if constexpr (TR) *reinterpret_cast<u32x4*>(Kt + r * LKT + col) = R.k[i];
@@ -452,7 +495,7 @@ struct Dq {
 #pragma unroll
     for (int i = 0; i < IP; ++i) {
       const int c = i * kThreads + tid;
-      if (c >= PCH) continue;
+      if (PCH % kThreads != 0 && c >= PCH) continue;
       const int r = c / (DR / IPC), col = DN + (c % (DR / IPC)) * IPC;
       E tmp[IPC];
       convert_chunk<E, InT>(R.p[i], tmp);
@@ -465,9 +508,22 @@ struct Dq {
 #pragma unroll
     for (int i = 0; i < IV; ++i) {
       const int c = i * kThreads + tid;
-      if (c >= VCH) continue;
+      if (VCH % kThreads != 0 && c >= VCH) continue;
       const int r = c / (DV / EPC), col = (c % (DV / EPC)) * EPC;
       *reinterpret_cast<u32x4*>(Vr + r * LVR + col) = R.v[i];
+    }
+  }
+
+  // KPL input elements at byte offset `off` of a buffer (zero outside it) as a fragment.
+  __device__ static F frag_from(__amdgpu_buffer_rsrc_t r, int off) {
+    if constexpr (sizeof(InT) * M::KPL == 16) {
+      const u32x4 raw = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+      E tmp[M::KPL];
+      convert_chunk<E, InT>(raw, tmp);
+      return *reinterpret_cast<F*>(tmp);
+    } else {
+      static_assert(sizeof(InT) == 4 && M::KPL == 1, "fp32 rows feed one element per lane");
+      return M::from_f32(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0)));
     }
   }
 
@@ -482,8 +538,78 @@ struct Dq {
     }
   }
 
+  // Stationary operands of one wavefront: its 32 queries' q and dO
+  // fragments (B operands) and softmax statistics.
+  struct Stat { F qf[KS_QK], of[KS_V]; float lse2, dl; };
+
+  // One block of BN keys from key0 against the wavefront's 32 queries from qw
+  // (lane column = query tq).  MASK: the block may cross the diagonal, reach
+  // past the sequence, or lie wholly after the wavefront's queries.
+  template <bool MASK>
+  __device__ static void block(const BwdArgs& a, const char* buf, int64_t key0, int64_t qw, const Stat& Q,
+                               f32x16* dq) {
+    const int lane = threadIdx.x % kWave;
+    const int hf = lane / 32, col = lane % 32;
+    if (MASK && key0 > qw + 31) return;  // every key of the block follows these queries
+    const E* Kr = reinterpret_cast<const E*>(buf);
+    const E* Kt = reinterpret_cast<const E*>(buf + KR_B);
+    const E* Vr = reinterpret_cast<const E*>(buf + KR_B + KT_B);
+    // S^T[key, q], dP^T[key, q] for the NT key atoms, chains interleaved.
+    f32x16 sc[NT], dp[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { sc[t][r] = 0.f; dp[t][r] = 0.f; }
+#pragma unroll
+    for (int s = 0; s < KS_QK; ++s)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        sc[t] = M::mma(lds_frag<M>(Kr + (t * 32 + col) * LKR + hf * M::KPL + s * M::K), Q.qf[s], sc[t]);
+        if (s < KS_V)
+          dp[t] = M::mma(lds_frag<M>(Vr + (t * 32 + col) * LVR + hf * M::KPL + s * M::K), Q.of[s], dp[t]);
+      }
+    // rel = key - query of accumulator row 0 of atom t (32-bit: within a block).
+    const int rel = static_cast<int>(key0 - qw) - col;
+    const int kin = static_cast<int>(a.S - key0);  // keys of the block inside the sequence
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = __builtin_amdgcn_exp2f(fmaf(sc[t][r], a.scale_log2, -Q.lse2));
+        if constexpr (MASK) {
+          const int u = t * 32 + 8 * (r / 4) + 4 * hf + (r % 4);  // key offset in the block
+          if (rel + u > 0 || u >= kin) p = 0.f;
+        }
+        dp[t][r] = p * (dp[t][r] - Q.dl);
+      }
+    // dq^T[d, q] += K^T dS^T  (k = keys of the accumulators)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int stp = 0; stp < STEPS; ++stp) {
+        E dh[M::KPL];
+#pragma unroll
+        for (int j = 0; j < M::KPL; ++j) dh[j] = M::from_f32(dp[t][stp * M::KPL + j]);
+        const F df = *reinterpret_cast<F*>(dh);
+#pragma unroll
+        for (int n = 0; n < NQT; ++n) dq[n] = M::mma(kt_frag(Kt, Kr, t, stp, n * 32), df, dq[n]);
+      }
+  }
+
+  template <bool MASK>
+  __device__ static void step(const BwdArgs& a, char* lds, int kb, int nkb, int b, int head, int64_t qw,
+                              Regs& R, const Stat& Q, f32x16* dq) {
+    const int64_t key0 = static_cast<int64_t>(kb) * BN;
+    char* buf = lds + (kb & 1) * BUF_BYTES;
+    store(R, buf);
+    __syncthreads();
+    if (kb + 1 < nkb) load(a, b, head, key0 + BN, R);
+    block<MASK>(a, buf, key0, qw, Q, dq);
+  }
+
   __device__ static void run(const BwdArgs& a, char* lds) {
-    const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int hf = lane / 32, col = lane % 32;
     const int n_qt = static_cast<int>((a.S + BM - 1) / BM);
     const int nbh = a.B * a.h;
@@ -495,17 +621,26 @@ struct Dq {
     const int64_t tq = qw + col;
     const bool qvalid = tq < a.S;
 
+    // q / dO rows of the wavefront; rows past the sequence read as zero, which
+    // with zero statistics makes their dS zero.
+    Stat Q;
+    {
+      const int nq = static_cast<int>(a.S - qw < 32 ? (a.S - qw > 0 ? a.S - qw : 0) : 32);
+      const int64_t row0 = (b * a.S + qw) * a.h + head;
+      const int qrb = a.h * DQK * static_cast<int>(sizeof(InT)), orb = a.h * DV * static_cast<int>(sizeof(InT));
+      const auto rq = rsrc(static_cast<const InT*>(a.q) + row0 * DQK, nq * qrb);
+      const auto ro = rsrc(static_cast<const InT*>(a.d_o) + row0 * DV, nq * orb);
+#pragma unroll
+      for (int s = 0; s < KS_QK; ++s)
+        Q.qf[s] = frag_from(rq, col * qrb + (s * M::K + hf * M::KPL) * static_cast<int>(sizeof(InT)));
+#pragma unroll
+      for (int s = 0; s < KS_V; ++s)
+        Q.of[s] = frag_from(ro, col * orb + (s * M::K + hf * M::KPL) * static_cast<int>(sizeof(InT)));
+      const int64_t si0 = (static_cast<int64_t>(b) * a.h + head) * a.S + qw;
+      Q.lse2 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.lse + si0, nq * 4), col * 4, 0, 0)) * kLog2e;
+      Q.dl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.delta + si0, nq * 4), col * 4, 0, 0));
+    }
     const int64_t qrow = (b * a.S + (qvalid ? tq : 0)) * a.h + head;
-    const InT* qg = static_cast<const InT*>(a.q) + qrow * DQK;
-    const InT* og = static_cast<const InT*>(a.d_o) + qrow * DV;
-    F qf[KS_QK], of[KS_V];
-#pragma unroll
-    for (int s = 0; s < KS_QK; ++s) qf[s] = load_frag<M>(qg + s * M::K + hf * M::KPL, qvalid);
-#pragma unroll
-    for (int s = 0; s < KS_V; ++s) of[s] = load_frag<M>(og + s * M::K + hf * M::KPL, qvalid);
-    const int64_t si = (static_cast<int64_t>(b) * a.h + head) * a.S + (qvalid ? tq : 0);
-    const float lse2 = qvalid ? a.lse[si] * kLog2e : 0.f;
-    const float dl = qvalid ? a.delta[si] : 0.f;
 
     f32x16 dq[NQT];
 #pragma unroll
@@ -513,59 +648,17 @@ struct Dq {
 #pragma unroll
       for (int r = 0; r < 16; ++r) dq[n][r] = 0.f;
 
+    // Key blocks wholly at or below the workgroup's first query need no mask.
     int64_t kend = q0 + BM;
     if (kend > a.S) kend = a.S;
     const int nkb = static_cast<int>((kend + BN - 1) / BN);
+    int nfree = static_cast<int>((q0 + 1) / BN);
+    if (nfree > nkb) nfree = nkb;
     Regs R;
     load(a, b, head, 0, R);
-    for (int kb = 0; kb < nkb; ++kb) {
-      const int64_t key0 = static_cast<int64_t>(kb) * BN;
-      char* buf = lds + (kb & 1) * BUF_BYTES;
-      store(R, buf);
-      __syncthreads();
-      if (kb + 1 < nkb) load(a, b, head, key0 + BN, R);
-      if (key0 > qw + 31) continue;  // whole block above this wavefront's diagonal
-
-      const E* Kr = reinterpret_cast<const E*>(buf);
-      const E* Kt = reinterpret_cast<const E*>(buf + KR_B);
-      const E* Vr = reinterpret_cast<const E*>(buf + KR_B + KT_B);
-      f32x16 sc[NT], dp[NT];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) { sc[t][r] = 0.f; dp[t][r] = 0.f; }
-        const E* krow = Kr + (t * 32 + col) * LKR + hf * M::KPL;
-#pragma unroll
-        for (int s = 0; s < KS_QK; ++s) sc[t] = M::mma(lds_frag<M>(krow + s * M::K), qf[s], sc[t]);
-        const E* vrow = Vr + (t * 32 + col) * LVR + hf * M::KPL;
-#pragma unroll
-        for (int s = 0; s < KS_V; ++s) dp[t] = M::mma(lds_frag<M>(vrow + s * M::K), of[s], dp[t]);
-      }
-      const bool edge = key0 + BN - 1 > qw || key0 + BN > a.S;
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = __builtin_amdgcn_exp2f(fmaf(sc[t][r], a.scale_log2, -lse2));
-          if (edge) {
-            const int64_t u = key0 + t * 32 + 8 * (r / 4) + 4 * hf + (r % 4);
-            if (u > tq || u >= a.S) p = 0.f;
-          }
-          dp[t][r] = p * (dp[t][r] - dl);
-        }
-      // dq^T[d, q] += K^T dS^T  (k = keys of the accumulators)
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int stp = 0; stp < STEPS; ++stp) {
-          E dh[M::KPL];
-#pragma unroll
-          for (int j = 0; j < M::KPL; ++j) dh[j] = M::from_f32(dp[t][stp * M::KPL + j]);
-          const F df = *reinterpret_cast<F*>(dh);
-#pragma unroll
-          for (int n = 0; n < NQT; ++n) dq[n] = M::mma(kt_frag(Kt, Kr, t, stp, n * 32), df, dq[n]);
-        }
-    }
+    int kb = 0;
+    for (; kb < nfree; ++kb) step<false>(a, lds, kb, nkb, b, head, qw, R, Q, dq);
+    for (; kb < nkb; ++kb) step<true>(a, lds, kb, nkb, b, head, qw, R, Q, dq);
     if (!qvalid) return;
     float* out = a.dq + qrow * DQK;
 #pragma unroll
