@@ -25,6 +25,11 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
           f"-I{INCLUDE}"] + DEVICE_FLAGS
+# Per-file code generation choices.  The dq kernel keeps its matrix-core
+# accumulators in VGPRs: with the default AGPR form the register allocator
+# copies part of the dq accumulators between the register files on every
+# key block.
+FILE_FLAGS = {"attn_bwd_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc() -> str:
@@ -36,7 +41,7 @@ def hipcc() -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *CFLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if verbose:
         cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -20,9 +20,9 @@
 //    feed dK^T = q^T dS and dV^T = dO^T P.  The 32x32 accumulators of S / dP
 //    hold one key per lane column, which is the B-operand layout of the
 //    dK / dV products, so P and dS never leave registers.
-//  * dq: a workgroup of 4 wavefronts owns 128 queries (q and dO in
-//    registers) and walks keys 0 .. diagonal, 64 at a time, computing
-//    S^T = K q^T and dP^T = V dO^T (one query per lane column) and
+//  * dq (attn_bwd_dq.hip): a workgroup of 4 wavefronts owns 128 queries (q
+//    and dO in registers) and walks keys 0 .. diagonal, 64 at a time,
+//    computing S^T = K q^T and dP^T = V dO^T (one query per lane column) and
 //    dq^T = K^T dS^T with K^T from transposing reads.
 // dk_pe is written per head into a workspace and summed over heads in a fixed
 // order (deterministic, no atomics).
@@ -31,48 +31,11 @@
 // dW_kv_b, dLatent and dgamma use K, V, P and dS as fp16 hi + lo pairs (q and
 // dO are exact in fp16); dq uses the hi parts of K and V and single fp16 dS.
 // The float32 instantiation uses fp32 MFMAs.
-#include <type_traits>
-
-#include "attn_common.hpp"
-#include "launch.hpp"
+#include "attn_bwd_common.hpp"
 
 namespace laga {
 namespace {
-
-constexpr int kThreads = 256;  // 4 wavefronts, one per SIMD
-constexpr float kLog2e = 1.4426950408889634f;
-
-struct BwdArgs {
-  const void* q; const void* k_nope; const void* k_pe; const void* v;
-  const float* lse; const float* delta; const void* d_o;
-  void* dkv; float* dk_pe_part; float* dq;
-  int64_t S, plane_k, plane_v, plane_dkv; int B, h; float scale_log2, scale;
-};
-
-// Row pitches (elements) of LDS tiles: rows read one per lane with 16-byte
-// reads are padded by 16 bytes; rows read with transposing reads (4 rows x
-// 64 bytes per half-wavefront) are padded to a pitch of 16 mod 64 dwords.
-template <class M> struct TilePad { static constexpr int row = 8, tr = 32; };
-template <> struct TilePad<MmaF32> { static constexpr int row = 4, tr = 4; };  // keeps 16-byte row alignment
-
-// 16-byte chunk of `E` converted from a 16-byte chunk of the input type.
-template <class E, class InT>
-__device__ __forceinline__ void convert_chunk(u32x4 raw, E* out) {
-  if constexpr (sizeof(InT) == 2 && sizeof(E) == 2) {     // bf16 -> fp16
-    const u16x8 v = __builtin_bit_cast(u16x8, raw);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) out[j] = static_cast<E>(bf16_to_f32(v[j]));
-  } else if constexpr (sizeof(InT) == sizeof(E)) {        // same type
-    *reinterpret_cast<u32x4*>(out) = raw;
-  } else {
-    static_assert(sizeof(InT) == sizeof(E), "unsupported conversion");
-  }
-}
-
-template <class T>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const T* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), 0, bytes, 0x00020000);
-}
+using namespace bwd;
 
 // ============================================================ dK / dV kernel
 template <class InT, class M, int NS, int DN, int DR, int DV>
@@ -427,252 +390,6 @@ struct Dkdv {
   }
 };
 
-// ================================================================ dq kernel
-template <class InT, class M, int NS, int DN, int DR, int DV>
-struct Dq {
-  typedef typename M::elem E;
-  typedef typename M::frag F;
-  static constexpr int DQK = DN + DR;
-  static constexpr int BM = 128, BN = 64;
-  static constexpr bool TR = M::KPL == 8;
-  static constexpr int LKR = DQK + TilePad<M>::row, LKT = DQK + TilePad<M>::tr, LVR = DV + TilePad<M>::row;
-  static constexpr int KR_B = BN * LKR * sizeof(E), KT_B = TR ? BN * LKT * sizeof(E) : 0;
-  static constexpr int VR_B = BN * LVR * sizeof(E);
-  static constexpr int BUF_BYTES = KR_B + KT_B + VR_B;
-  static constexpr int KS_QK = DQK / M::K, KS_V = DV / M::K;
-  static constexpr int NT = BN / 32, NQT = (DQK + 31) / 32, STEPS = 32 / M::K;
-  // Staging chunks (16 bytes): nope part of K (hi plane), rope band (input type), V (hi plane).
-  static constexpr int EPC = 16 / sizeof(E), IPC = 16 / sizeof(InT);
-  static constexpr int KCH = BN * DN / EPC, PCH = BN * DR / IPC, VCH = BN * DV / EPC;
-  static constexpr int IK = (KCH + kThreads - 1) / kThreads, IP = (PCH + kThreads - 1) / kThreads;
-  static constexpr int IV = (VCH + kThreads - 1) / kThreads;
-
-  struct Regs { u32x4 k[IK]; u32x4 p[IP]; u32x4 v[IV]; };
-
-  __device__ static void load(const BwdArgs& a, int b, int head, int64_t key0, Regs& R) {
-    const int nk = static_cast<int>(a.S - key0 < BN ? a.S - key0 : BN);
-    const int64_t row0 = (b * a.S + key0) * a.h + head;
-    const int krow_b = a.h * DN * static_cast<int>(sizeof(E));
-    const int vrow_b = a.h * DV * static_cast<int>(sizeof(E));
-    const int prow_b = DR * static_cast<int>(sizeof(InT));
-    const auto rk = rsrc(static_cast<const E*>(a.k_nope) + row0 * DN, nk * krow_b);
-    const auto rv = rsrc(static_cast<const E*>(a.v) + row0 * DV, nk * vrow_b);
-    const auto rp = rsrc(static_cast<const InT*>(a.k_pe) + (b * a.S + key0) * DR, nk * prow_b);
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < IK; ++i) {
-      const int c = i * kThreads + tid;
-      const int r = c / (DN / EPC), j = c % (DN / EPC);
-      if (KCH % kThreads == 0 || c < KCH) R.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, r * krow_b + j * 16, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < IP; ++i) {
-      const int c = i * kThreads + tid;
-      const int r = c / (DR / IPC), j = c % (DR / IPC);
-      if (PCH % kThreads == 0 || c < PCH) R.p[i] = __builtin_amdgcn_raw_buffer_load_b128(rp, r * prow_b + j * 16, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < IV; ++i) {
-      const int c = i * kThreads + tid;
-      const int r = c / (DV / EPC), j = c % (DV / EPC);
-      if (VCH % kThreads == 0 || c < VCH) R.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, r * vrow_b + j * 16, 0, 0);
-    }
-  }
-
-  __device__ static void store(const Regs& R, char* buf) {
-    E* Kr = reinterpret_cast<E*>(buf);
-    E* Kt = reinterpret_cast<E*>(buf + KR_B);
-    E* Vr = reinterpret_cast<E*>(buf + KR_B + KT_B);
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < IK; ++i) {
-      const int c = i * kThreads + tid;
-      if (KCH % kThreads != 0 && c >= KCH) continue;
-      const int r = c / (DN / EPC), col = (c % (DN / EPC)) * EPC;
-      *reinterpret_cast<u32x4*>(Kr + r * LKR + col) = R.k[i];
-      if constexpr (TR) *reinterpret_cast<u32x4*>(Kt + r * LKT + col) = R.k[i];
-    }
-#pragma unroll
-    for (int i = 0; i < IP; ++i) {
-      const int c = i * kThreads + tid;
-      if (PCH % kThreads != 0 && c >= PCH) continue;
-      const int r = c / (DR / IPC), col = DN + (c % (DR / IPC)) * IPC;
-      E tmp[IPC];
-      convert_chunk<E, InT>(R.p[i], tmp);
-#pragma unroll
-      for (int j = 0; j < IPC; j += EPC) {
-        *reinterpret_cast<u32x4*>(Kr + r * LKR + col + j) = *reinterpret_cast<u32x4*>(tmp + j);
-        if constexpr (TR) *reinterpret_cast<u32x4*>(Kt + r * LKT + col + j) = *reinterpret_cast<u32x4*>(tmp + j);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < IV; ++i) {
-      const int c = i * kThreads + tid;
-      if (VCH % kThreads != 0 && c >= VCH) continue;
-      const int r = c / (DV / EPC), col = (c % (DV / EPC)) * EPC;
-      *reinterpret_cast<u32x4*>(Vr + r * LVR + col) = R.v[i];
-    }
-  }
-
-  // KPL input elements at byte offset `off` of a buffer (zero outside it) as a fragment.
-  __device__ static F frag_from(__amdgpu_buffer_rsrc_t r, int off) {
-    if constexpr (sizeof(InT) * M::KPL == 16) {
-      const u32x4 raw = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-      E tmp[M::KPL];
-      convert_chunk<E, InT>(raw, tmp);
-      return *reinterpret_cast<F*>(tmp);
-    } else {
-      static_assert(sizeof(InT) == 4 && M::KPL == 1, "fp32 rows feed one element per lane");
-      return M::from_f32(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0)));
-    }
-  }
-
-  // A operand of dq^T += K^T dS^T for one MFMA step of key atom t.
-  __device__ static F kt_frag(const E* Kt, const E* Kr, int t, int st, int n0) {
-    if constexpr (TR) {
-      return tr_frag_acc(Kt, LKT, t * 32 + st * 16, n0);
-    } else {
-      const int lane = threadIdx.x % kWave;
-      const int k = t * 32 + 8 * (st / 4) + 4 * (lane / 32) + (st % 4);
-      return Kr[k * LKR + n0 + lane % 32];
-    }
-  }
-
-  // Stationary operands of one wavefront: its 32 queries' q and dO
-  // fragments (B operands) and softmax statistics.
-  struct Stat { F qf[KS_QK], of[KS_V]; float lse2, dl; };
-
-  // One block of BN keys from key0 against the wavefront's 32 queries from qw
-  // (lane column = query tq).  MASK: the block may cross the diagonal, reach
-  // past the sequence, or lie wholly after the wavefront's queries.
-  template <bool MASK>
-  __device__ static void block(const BwdArgs& a, const char* buf, int64_t key0, int64_t qw, const Stat& Q,
-                               f32x16* dq) {
-    const int lane = threadIdx.x % kWave;
-    const int hf = lane / 32, col = lane % 32;
-    if (MASK && key0 > qw + 31) return;  // every key of the block follows these queries
-    const E* Kr = reinterpret_cast<const E*>(buf);
-    const E* Kt = reinterpret_cast<const E*>(buf + KR_B);
-    const E* Vr = reinterpret_cast<const E*>(buf + KR_B + KT_B);
-    // S^T[key, q], dP^T[key, q] for the NT key atoms, chains interleaved.
-    f32x16 sc[NT], dp[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) { sc[t][r] = 0.f; dp[t][r] = 0.f; }
-#pragma unroll
-    for (int s = 0; s < KS_QK; ++s)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        sc[t] = M::mma(lds_frag<M>(Kr + (t * 32 + col) * LKR + hf * M::KPL + s * M::K), Q.qf[s], sc[t]);
-        if (s < KS_V)
-          dp[t] = M::mma(lds_frag<M>(Vr + (t * 32 + col) * LVR + hf * M::KPL + s * M::K), Q.of[s], dp[t]);
-      }
-    // rel = key - query of accumulator row 0 of atom t (32-bit: within a block).
-    const int rel = static_cast<int>(key0 - qw) - col;
-    const int kin = static_cast<int>(a.S - key0);  // keys of the block inside the sequence
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = __builtin_amdgcn_exp2f(fmaf(sc[t][r], a.scale_log2, -Q.lse2));
-        if constexpr (MASK) {
-          const int u = t * 32 + 8 * (r / 4) + 4 * hf + (r % 4);  // key offset in the block
-          if (rel + u > 0 || u >= kin) p = 0.f;
-        }
-        dp[t][r] = p * (dp[t][r] - Q.dl);
-      }
-    // dq^T[d, q] += K^T dS^T  (k = keys of the accumulators)
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int stp = 0; stp < STEPS; ++stp) {
-        E dh[M::KPL];
-#pragma unroll
-        for (int j = 0; j < M::KPL; ++j) dh[j] = M::from_f32(dp[t][stp * M::KPL + j]);
-        const F df = *reinterpret_cast<F*>(dh);
-#pragma unroll
-        for (int n = 0; n < NQT; ++n) dq[n] = M::mma(kt_frag(Kt, Kr, t, stp, n * 32), df, dq[n]);
-      }
-  }
-
-  template <bool MASK>
-  __device__ static void step(const BwdArgs& a, char* lds, int kb, int nkb, int b, int head, int64_t qw,
-                              Regs& R, const Stat& Q, f32x16* dq) {
-    const int64_t key0 = static_cast<int64_t>(kb) * BN;
-    char* buf = lds + (kb & 1) * BUF_BYTES;
-    store(R, buf);
-    __syncthreads();
-    if (kb + 1 < nkb) load(a, b, head, key0 + BN, R);
-    block<MASK>(a, buf, key0, qw, Q, dq);
-  }
-
-  __device__ static void run(const BwdArgs& a, char* lds) {
-    const int lane = threadIdx.x % kWave;
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
-    const int hf = lane / 32, col = lane % 32;
-    const int n_qt = static_cast<int>((a.S + BM - 1) / BM);
-    const int nbh = a.B * a.h;
-    const int qt = n_qt - 1 - static_cast<int>(blockIdx.x / nbh);  // longest first
-    const int bh = blockIdx.x % nbh;
-    const int b = bh / a.h, head = bh % a.h;
-    const int64_t q0 = static_cast<int64_t>(qt) * BM;
-    const int64_t qw = q0 + wv * 32;
-    const int64_t tq = qw + col;
-    const bool qvalid = tq < a.S;
-
-    // q / dO rows of the wavefront; rows past the sequence read as zero, which
-    // with zero statistics makes their dS zero.
-    Stat Q;
-    {
-      const int nq = static_cast<int>(a.S - qw < 32 ? (a.S - qw > 0 ? a.S - qw : 0) : 32);
-      const int64_t row0 = (b * a.S + qw) * a.h + head;
-      const int qrb = a.h * DQK * static_cast<int>(sizeof(InT)), orb = a.h * DV * static_cast<int>(sizeof(InT));
-      const auto rq = rsrc(static_cast<const InT*>(a.q) + row0 * DQK, nq * qrb);
-      const auto ro = rsrc(static_cast<const InT*>(a.d_o) + row0 * DV, nq * orb);
-#pragma unroll
-      for (int s = 0; s < KS_QK; ++s)
-        Q.qf[s] = frag_from(rq, col * qrb + (s * M::K + hf * M::KPL) * static_cast<int>(sizeof(InT)));
-#pragma unroll
-      for (int s = 0; s < KS_V; ++s)
-        Q.of[s] = frag_from(ro, col * orb + (s * M::K + hf * M::KPL) * static_cast<int>(sizeof(InT)));
-      const int64_t si0 = (static_cast<int64_t>(b) * a.h + head) * a.S + qw;
-      Q.lse2 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.lse + si0, nq * 4), col * 4, 0, 0)) * kLog2e;
-      Q.dl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.delta + si0, nq * 4), col * 4, 0, 0));
-    }
-    const int64_t qrow = (b * a.S + (qvalid ? tq : 0)) * a.h + head;
-
-    f32x16 dq[NQT];
-#pragma unroll
-    for (int n = 0; n < NQT; ++n)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dq[n][r] = 0.f;
-
-    // Key blocks wholly at or below the workgroup's first query need no mask.
-    int64_t kend = q0 + BM;
-    if (kend > a.S) kend = a.S;
-    const int nkb = static_cast<int>((kend + BN - 1) / BN);
-    int nfree = static_cast<int>((q0 + 1) / BN);
-    if (nfree > nkb) nfree = nkb;
-    Regs R;
-    load(a, b, head, 0, R);
-    int kb = 0;
-    for (; kb < nfree; ++kb) step<false>(a, lds, kb, nkb, b, head, qw, R, Q, dq);
-    for (; kb < nkb; ++kb) step<true>(a, lds, kb, nkb, b, head, qw, R, Q, dq);
-    if (!qvalid) return;
-    float* out = a.dq + qrow * DQK;
-#pragma unroll
-    for (int n = 0; n < NQT; ++n)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        if (n * 32 + 8 * g + 4 * hf >= DQK) continue;
-        f32x4 w = {dq[n][4 * g] * a.scale, dq[n][4 * g + 1] * a.scale, dq[n][4 * g + 2] * a.scale,
-                   dq[n][4 * g + 3] * a.scale};
-        *reinterpret_cast<f32x4*>(out + n * 32 + 8 * g + 4 * hf) = w;
-      }
-  }
-};
-
 template <class InT, class M, int NS, int DN, int DR, int DV>
 __global__ __launch_bounds__(kThreads) void dkdv_kernel(BwdArgs a) {
   typedef Dkdv<InT, M, NS, DN, DR, DV> Kn;
@@ -680,26 +397,6 @@ __global__ __launch_bounds__(kThreads) void dkdv_kernel(BwdArgs a) {
   Kn::run(a, lds);
 }
 
-template <class InT, class M, int NS, int DN, int DR, int DV>
-__global__ __launch_bounds__(kThreads) void dq_kernel(BwdArgs a) {
-  typedef Dq<InT, M, NS, DN, DR, DV> Kn;
-  __shared__ __attribute__((aligned(16))) char lds[2 * Kn::BUF_BYTES];
-  Kn::run(a, lds);
-}
-
-BwdArgs make_args(const Shape& s, const void* q, const void* kn, const void* kp, const void* v, const float* lse,
-                  const float* delta, const void* d_o) {
-  BwdArgs a;
-  a.q = q; a.k_nope = kn; a.k_pe = kp; a.v = v; a.lse = lse; a.delta = delta; a.d_o = d_o;
-  a.dkv = nullptr; a.dk_pe_part = nullptr; a.dq = nullptr;
-  a.S = s.S; a.B = static_cast<int>(s.B); a.h = s.h;
-  a.plane_k = s.T * s.h * s.d_nope;
-  a.plane_v = s.T * s.h * s.d_v;
-  a.plane_dkv = s.T * s.h * s.C();
-  a.scale = 1.0f / sqrtf(static_cast<float>(s.d_qk()));
-  a.scale_log2 = kLog2e * a.scale;
-  return a;
-}
 
 // delta[b, i, t] = sum_c d_o[b, t, i, c] * o[b, t, i, c]  (one wavefront per row).
 template <class InT, int DV>
@@ -763,20 +460,6 @@ hipError_t launch_attn_bwd_dkdv(const Shape& s, const void* q, const void* kn, c
     hipLaunchKernelGGL((dkdv_kernel<bf16_t, MmaF16, 2, 128, 64, 128>), dim3(grid), dim3(kThreads), 0, st, a);
   else if (!s.bf16 && s.d_nope == 32 && s.d_rope == 16 && s.d_v == 32)
     hipLaunchKernelGGL((dkdv_kernel<float, MmaF32, 1, 32, 16, 32>), dim3(grid), dim3(kThreads), 0, st, a);
-  else
-    return hipErrorNotSupported;
-  return hipGetLastError();
-}
-
-hipError_t launch_attn_bwd_dq(const Shape& s, const void* q, const void* kn, const void* kp, const void* v,
-                              const float* lse, const float* delta, const void* d_o, float* dq, hipStream_t st) {
-  BwdArgs a = make_args(s, q, kn, kp, v, lse, delta, d_o);
-  a.dq = dq;
-  const unsigned grid = static_cast<unsigned>(((s.S + 127) / 128) * s.B * s.h);
-  if (s.bf16 && s.split && s.d_nope == 128 && s.d_rope == 64 && s.d_v == 128)
-    hipLaunchKernelGGL((dq_kernel<bf16_t, MmaF16, 2, 128, 64, 128>), dim3(grid), dim3(kThreads), 0, st, a);
-  else if (!s.bf16 && s.d_nope == 32 && s.d_rope == 16 && s.d_v == 32)
-    hipLaunchKernelGGL((dq_kernel<float, MmaF32, 1, 32, 16, 32>), dim3(grid), dim3(kThreads), 0, st, a);
   else
     return hipErrorNotSupported;
   return hipGetLastError();

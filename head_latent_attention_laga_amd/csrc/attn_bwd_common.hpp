@@ -1,0 +1,68 @@
+// Pieces shared by the two attention-backward kernels (dK/dV and dq): the
+// argument block, LDS tile padding and staging helpers.
+#pragma once
+
+#include <type_traits>
+
+#include "attn_common.hpp"
+#include "launch.hpp"
+
+namespace laga {
+namespace bwd {
+
+constexpr int kThreads = 256;  // 4 wavefronts, one per SIMD
+constexpr float kLog2e = 1.4426950408889634f;
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
+constexpr int kReadAhead = 3;  // LDS operand reads kept in flight ahead of the products
+
+struct BwdArgs {
+  const void* q; const void* k_nope; const void* k_pe; const void* v;
+  const float* lse; const float* delta; const void* d_o;
+  void* dkv; float* dk_pe_part; float* dq;
+  int64_t S, plane_k, plane_v, plane_dkv; int B, h; float scale_log2, scale;
+};
+
+// Row pitches (elements) of LDS tiles: rows read one per lane with 16-byte
+// reads are padded by 16 bytes; rows read with transposing reads (4 rows x
+// 64 bytes per half-wavefront) are padded to a pitch of 16 mod 64 dwords.
+template <class M> struct TilePad { static constexpr int row = 8, tr = 32; };
+template <> struct TilePad<MmaF32> { static constexpr int row = 4, tr = 4; };  // keeps 16-byte row alignment
+
+// 16-byte chunk of `E` converted from a 16-byte chunk of the input type.
+template <class E, class InT>
+__device__ __forceinline__ void convert_chunk(u32x4 raw, E* out) {
+  if constexpr (sizeof(InT) == 2 && sizeof(E) == 2) {     // bf16 -> fp16
+    const u16x8 v = __builtin_bit_cast(u16x8, raw);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) out[j] = static_cast<E>(bf16_to_f32(v[j]));
+  } else if constexpr (sizeof(InT) == sizeof(E)) {        // same type
+    *reinterpret_cast<u32x4*>(out) = raw;
+  } else {
+    static_assert(sizeof(InT) == sizeof(E), "unsupported conversion");
+  }
+}
+
+template <class T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const T* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), 0, bytes, 0x00020000);
+}
+
+
+inline BwdArgs make_args(const Shape& s, const void* q, const void* kn, const void* kp, const void* v, const float* lse,
+                  const float* delta, const void* d_o) {
+  BwdArgs a;
+  a.q = q; a.k_nope = kn; a.k_pe = kp; a.v = v; a.lse = lse; a.delta = delta; a.d_o = d_o;
+  a.dkv = nullptr; a.dk_pe_part = nullptr; a.dq = nullptr;
+  a.S = s.S; a.B = static_cast<int>(s.B); a.h = s.h;
+  a.plane_k = s.T * s.h * s.d_nope;
+  a.plane_v = s.T * s.h * s.d_v;
+  a.plane_dkv = s.T * s.h * s.C();
+  a.scale = 1.0f / sqrtf(static_cast<float>(s.d_qk()));
+  a.scale_log2 = kLog2e * a.scale;
+  return a;
+}
+
+
+}  // namespace bwd
+}  // namespace laga
