@@ -183,35 +183,38 @@ struct Dkdv {
     const float* st = reinterpret_cast<const float*>(buf + QR_B + QT_B + OR_B + OT_B);
 
     // S[q, key], dP[q, key]: rows = queries 8g + 4hf + i, column = key.  The
-    // two chains are interleaved so that each one's operand reads overlap the
-    // other's products.
+    // chains run one after the other so that the vector work on each result
+    // (P from S, dS from dP) overlaps the next chain of products:
+    //   S | dP + P | dV + dS | dK
+    const E* qrow = Qr + col * LQR + hf * M::KPL;
+    const E* orow = Or + col * LOR + hf * M::KPL;
     f32x16 sc, dp;
 #pragma unroll
     for (int r = 0; r < 16; ++r) { sc[r] = 0.f; dp[r] = 0.f; }
-    const E* qrow = Qr + col * LQR + hf * M::KPL;
-    const E* orow = Or + col * LOR + hf * M::KPL;
-    static_assert(KS_N == KS_V, "nope and value widths interleave step for step");
 #pragma unroll
     for (int s = 0; s < KS_N; ++s) {
       const F qa = lds_frag<M>(qrow + s * M::K);
-      const F oa = lds_frag<M>(orow + s * M::K);
       sc = M::mma(qa, K.kf[s], sc);
-      dp = M::mma(oa, K.vf[s], dp);
-      if constexpr (NS == 2) {
-        sc = M::mma(qa, lds_frag<M>(K.klo_row + s * M::K), sc);
-        dp = M::mma(oa, lds_frag<M>(K.vlo_row + s * M::K), dp);
-      }
+      if constexpr (NS == 2) sc = M::mma(qa, lds_frag<M>(K.klo_row + s * M::K), sc);
     }
 #pragma unroll
     for (int s = KS_N; s < KS_QK; ++s) sc = M::mma(lds_frag<M>(qrow + s * M::K), K.kr[s - KS_N], sc);
+#pragma unroll
+    for (int s = 0; s < KS_V; ++s) {
+      const F oa = lds_frag<M>(orow + s * M::K);
+      dp = M::mma(oa, K.vf[s], dp);
+      if constexpr (NS == 2) dp = M::mma(oa, lds_frag<M>(K.vlo_row + s * M::K), dp);
+    }
 
-    // P = exp(s - lse) and dS = P (dP - delta), per query row of the block.
+    // P = exp(s - lse) per query row of the block, split into NS terms
+    // grouped by MFMA step (k = queries of accumulator registers).
     const int rel = static_cast<int>(wk0 - q0) + col;  // key - q0
     const int nq = static_cast<int>(a.S - q0 < BQ ? a.S - q0 : BQ);
+    float pv[16];
+    E ph[STEPS][NS][M::KPL];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(st + 8 * g + 4 * hf);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(st + BQ + 8 * g + 4 * hf);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * g + i;
@@ -220,36 +223,46 @@ struct Dkdv {
           const int qi = 8 * g + 4 * hf + i;
           if (rel > qi || qi >= nq) p = 0.f;
         }
-        sc[r] = p;
-        dp[r] = p * (dp[r] - d4[i]);
+        pv[r] = p;
+        E t[NS];
+        split_to<M, NS>(p, t);
+#pragma unroll
+        for (int q = 0; q < NS; ++q) ph[r / M::KPL][q][r % M::KPL] = t[q];
       }
     }
-
-    // dV^T[dv, key] += dO^T P ; dK^T[d, key] += q^T dS   (k = queries)
+    // dV^T[dv, key] += dO^T P   (k = queries)
 #pragma unroll
-    for (int stp = 0; stp < STEPS; ++stp) {
-      E ph[NS][M::KPL], dh[NS][M::KPL];
-#pragma unroll
-      for (int j = 0; j < M::KPL; ++j) {
-        E t1[NS], t2[NS];
-        split_to<M, NS>(sc[stp * M::KPL + j], t1);
-        split_to<M, NS>(dp[stp * M::KPL + j], t2);
-#pragma unroll
-        for (int p = 0; p < NS; ++p) { ph[p][j] = t1[p]; dh[p][j] = t2[p]; }
-      }
+    for (int stp = 0; stp < STEPS; ++stp)
 #pragma unroll
       for (int n = 0; n < NVT; ++n) {
         const F oa = tr_frag(Ot, Or, LOT, LOR, stp, n * 32);
 #pragma unroll
-        for (int p = 0; p < NS; ++p) acc.dvt[n] = M::mma(oa, *reinterpret_cast<F*>(ph[p]), acc.dvt[n]);
+        for (int q = 0; q < NS; ++q) acc.dvt[n] = M::mma(oa, *reinterpret_cast<F*>(ph[stp][q]), acc.dvt[n]);
       }
+
+    // dS = P (dP - delta), split the same way.
+    E dh[STEPS][NS][M::KPL];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(st + BQ + 8 * g + 4 * hf);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;
+        E t[NS];
+        split_to<M, NS>(pv[r] * (dp[r] - d4[i]), t);
+#pragma unroll
+        for (int q = 0; q < NS; ++q) dh[r / M::KPL][q][r % M::KPL] = t[q];
+      }
+    }
+    // dK^T[d, key] += q^T dS   (k = queries)
+#pragma unroll
+    for (int stp = 0; stp < STEPS; ++stp)
 #pragma unroll
       for (int n = 0; n < NKT; ++n) {
         const F qa = tr_frag(Qt, Qr, LQT, LQR, stp, n * 32);
 #pragma unroll
-        for (int p = 0; p < NS; ++p) acc.dk[n] = M::mma(qa, *reinterpret_cast<F*>(dh[p]), acc.dk[n]);
+        for (int q = 0; q < NS; ++q) acc.dk[n] = M::mma(qa, *reinterpret_cast<F*>(dh[stp][q]), acc.dk[n]);
       }
-    }
   }
 
   // Publish the staged block `it`, start loading the next one, compute.
