@@ -49,7 +49,7 @@ laga_status from_hip(hipError_t e) {
 
 // Backward workspace regions, each 256-byte aligned, in float32 elements.
 struct BwdLayout {
-  size_t delta, dkv, dkpe, dL, lp, dw, dg, total;  // byte offsets, total bytes
+  size_t delta, cvt, dkv, dkpe, dL, lp, dw, dg, total;  // byte offsets, total bytes
 };
 
 size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
@@ -63,6 +63,8 @@ BwdLayout bwd_layout(const Shape& s) {
     return at;
   };
   L.delta = take(static_cast<size_t>(s.B) * s.h * s.S);
+  // fp16 copies of q, dO and k_pe (bfloat16 inputs only), in float units.
+  L.cvt = take(s.bf16 ? (static_cast<size_t>(s.T) * (s.h * (s.d_qk() + s.d_v) + s.d_rope) + 1) / 2 : 0);
   L.dkv = take(static_cast<size_t>(s.T) * s.h * s.C());
   L.dkpe = take(static_cast<size_t>(s.h) * s.T * s.d_rope);
   L.dL = take(static_cast<size_t>(s.T) * s.d_kv);
@@ -157,7 +159,17 @@ laga_status laga_attn_bwd_traced(const laga_dims* dims, const void* q, const voi
 
   hipError_t e;
   if ((e = mark(0)) != hipSuccess) return from_hip(e);
-  if ((e = laga::launch_bwd_dot(s, o, d_o, delta, hs)) != hipSuccess) return from_hip(e);
+  // bfloat16 inputs reach the attention kernels as exact fp16 copies.
+  uint16_t* q16 = reinterpret_cast<uint16_t*>(ws + L.cvt);
+  uint16_t* do16 = q16 + static_cast<size_t>(s.T) * s.h * s.d_qk();
+  uint16_t* kpe16 = do16 + static_cast<size_t>(s.T) * s.h * s.d_v;
+  if ((e = laga::launch_bwd_prep(s, o, q, d_o, k_pe, delta, q16, do16, kpe16, hs)) != hipSuccess)
+    return from_hip(e);
+  if (s.bf16) {
+    q = q16;
+    d_o = do16;
+    k_pe = kpe16;
+  }
   if ((e = mark(1)) != hipSuccess) return from_hip(e);
   if ((e = laga::launch_attn_bwd_dkdv(s, q, k_nope, k_pe, v, lse, delta, d_o, dkv, dkpe, hs)) != hipSuccess)
     return from_hip(e);

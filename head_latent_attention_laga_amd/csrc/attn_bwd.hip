@@ -3,7 +3,7 @@
 // local heads; the K/V gradients are folded back through W_kv_b elsewhere].
 //
 // With P = softmax(s), s = q.K^T / sqrt(d_qk) (causal), and upstream dO:
-//   delta[t] = sum_c dO[t,c] o[t,c]                         (bwd_dot_kernel)
+//   delta[t] = sum_c dO[t,c] o[t,c]                (bwd_prep_kernel, bwd_dot_kernel)
 //   dV  = P^T dO,  dP = dO V^T,  dS = P * (dP - delta)
 //   dK  = dS^T q / sqrt(d_qk)  -> dk_nope = dK[:, :d_nope], dk_pe = sum_i dK[:, d_nope:]
 //   dq  = dS K / sqrt(d_qk)
@@ -431,6 +431,55 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(const float* __restrict__ 
   }
 }
 
+// bfloat16 inputs: delta as above, plus fp16 copies (exact) of the q and dO
+// rows and of the k_pe band, which the attention-backward kernels then stage
+// with plain 16-byte copies.  One wavefront per (b, t, i) row: the first DV/8
+// lanes take 8 elements of dO and o each, the next DQK/8 lanes 8 elements of
+// q, and on the i == 0 row the next DR/8 lanes 8 elements of k_pe.
+template <int DQK, int DV, int DR>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__ o, const bf16_t* __restrict__ q,
+                                                       const bf16_t* __restrict__ d_o,
+                                                       const bf16_t* __restrict__ k_pe, float* __restrict__ delta,
+                                                       half_t* __restrict__ q16, half_t* __restrict__ do16,
+                                                       half_t* __restrict__ kpe16, int64_t rows, int h, int64_t S) {
+  constexpr int NO = DV / 8, NQ = DQK / 8, NR = DR / 8;
+  static_assert(NO + NQ + NR <= kWave && DV % 8 == 0 && DQK % 8 == 0 && DR % 8 == 0, "one chunk per lane");
+  const int lane = threadIdx.x % kWave;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;  // (b, t, i)
+  if (row >= rows) return;
+  const int64_t bt = row / h;
+  const int i = static_cast<int>(row % h);
+  auto to_half8 = [](u16x8 v, float* f) {
+    half8 r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      f[j] = bf16_to_f32(v[j]);
+      r[j] = static_cast<half_t>(f[j]);
+    }
+    return r;
+  };
+  float acc = 0.f;
+  float f[8];
+  if (lane < NO) {
+    const int64_t at = row * DV + lane * 8;
+    *reinterpret_cast<half8*>(do16 + at) = to_half8(*reinterpret_cast<const u16x8*>(d_o + at), f);
+    const f32x4 o0 = *reinterpret_cast<const f32x4*>(o + at), o1 = *reinterpret_cast<const f32x4*>(o + at + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc += f[j] * o0[j] + f[4 + j] * o1[j];
+  } else if (lane < NO + NQ) {
+    const int64_t at = row * DQK + (lane - NO) * 8;
+    *reinterpret_cast<half8*>(q16 + at) = to_half8(*reinterpret_cast<const u16x8*>(q + at), f);
+  } else if (lane < NO + NQ + NR && i == 0) {
+    const int64_t at = bt * DR + (lane - NO - NQ) * 8;
+    *reinterpret_cast<half8*>(kpe16 + at) = to_half8(*reinterpret_cast<const u16x8*>(k_pe + at), f);
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) {
+    const int64_t b = bt / S, t = bt % S;
+    delta[(b * h + i) * S + t] = acc;
+  }
+}
+
 // out[t, c] = sum_i part[i, t, c] in increasing i (deterministic head sum).
 __global__ __launch_bounds__(256) void head_sum_kernel(const float* __restrict__ part, float* __restrict__ out,
                                                        int64_t n, int h) {
@@ -443,15 +492,20 @@ __global__ __launch_bounds__(256) void head_sum_kernel(const float* __restrict__
 
 }  // namespace
 
-hipError_t launch_bwd_dot(const Shape& s, const float* o, const void* d_o, float* delta, hipStream_t st) {
+hipError_t launch_bwd_prep(const Shape& s, const float* o, const void* q, const void* d_o, const void* k_pe,
+                           float* delta, void* q16, void* do16, void* kpe16, hipStream_t st) {
   const int64_t rows = s.T * s.h;
   const unsigned blocks = static_cast<unsigned>((rows + 3) / 4);
-  if (s.bf16)
-    hipLaunchKernelGGL((bwd_dot_kernel<bf16_t, 128>), dim3(blocks), dim3(256), 0, st, o,
-                       static_cast<const bf16_t*>(d_o), delta, rows, s.h, s.S);
-  else
+  if (s.bf16 && s.d_nope == 128 && s.d_rope == 64 && s.d_v == 128)
+    hipLaunchKernelGGL((bwd_prep_kernel<192, 128, 64>), dim3(blocks), dim3(256), 0, st, o,
+                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(d_o),
+                       static_cast<const bf16_t*>(k_pe), delta, static_cast<half_t*>(q16),
+                       static_cast<half_t*>(do16), static_cast<half_t*>(kpe16), rows, s.h, s.S);
+  else if (!s.bf16 && s.d_v == 32)
     hipLaunchKernelGGL((bwd_dot_kernel<float, 32>), dim3(blocks), dim3(256), 0, st, o,
                        static_cast<const float*>(d_o), delta, rows, s.h, s.S);
+  else
+    return hipErrorNotSupported;
   return hipGetLastError();
 }
 
@@ -470,7 +524,7 @@ hipError_t launch_attn_bwd_dkdv(const Shape& s, const void* q, const void* kn, c
   a.dk_pe_part = dk_pe_part;
   const unsigned grid = static_cast<unsigned>(((s.S + 127) / 128) * s.B * s.h);
   if (s.bf16 && s.split && s.d_nope == 128 && s.d_rope == 64 && s.d_v == 128)
-    hipLaunchKernelGGL((dkdv_kernel<bf16_t, MmaF16, 2, 128, 64, 128>), dim3(grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((dkdv_kernel<half_t, MmaF16, 2, 128, 64, 128>), dim3(grid), dim3(kThreads), 0, st, a);
   else if (!s.bf16 && s.d_nope == 32 && s.d_rope == 16 && s.d_v == 32)
     hipLaunchKernelGGL((dkdv_kernel<float, MmaF32, 1, 32, 16, 32>), dim3(grid), dim3(kThreads), 0, st, a);
   else

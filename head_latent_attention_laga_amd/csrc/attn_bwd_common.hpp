@@ -32,14 +32,14 @@ template <> struct TilePad<MmaF32> { static constexpr int row = 4, tr = 4; };  /
 // 16-byte chunk of `E` converted from a 16-byte chunk of the input type.
 template <class E, class InT>
 __device__ __forceinline__ void convert_chunk(u32x4 raw, E* out) {
-  if constexpr (sizeof(InT) == 2 && sizeof(E) == 2) {     // bf16 -> fp16
+  if constexpr (std::is_same<InT, E>::value) {  // same type
+    *reinterpret_cast<u32x4*>(out) = raw;
+  } else if constexpr (std::is_same<InT, bf16_t>::value && std::is_same<E, half_t>::value) {  // bf16 -> fp16
     const u16x8 v = __builtin_bit_cast(u16x8, raw);
 #pragma unroll
     for (int j = 0; j < 8; ++j) out[j] = static_cast<E>(bf16_to_f32(v[j]));
-  } else if constexpr (sizeof(InT) == sizeof(E)) {        // same type
-    *reinterpret_cast<u32x4*>(out) = raw;
   } else {
-    static_assert(sizeof(InT) == sizeof(E), "unsupported conversion");
+    static_assert(std::is_same<InT, E>::value, "unsupported conversion");
   }
 }
 

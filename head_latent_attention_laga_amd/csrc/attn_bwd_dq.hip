@@ -294,7 +294,7 @@ hipError_t launch_attn_bwd_dq(const Shape& s, const void* q, const void* kn, con
   a.dq = dq;
   const unsigned grid = static_cast<unsigned>(((s.S + 127) / 128) * s.B * s.h);
   if (s.bf16 && s.split && s.d_nope == 128 && s.d_rope == 64 && s.d_v == 128)
-    hipLaunchKernelGGL((dq_kernel<bf16_t, MmaF16, 2, 128, 64, 128>), dim3(grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((dq_kernel<half_t, MmaF16, 2, 128, 64, 128>), dim3(grid), dim3(kThreads), 0, st, a);
   else if (!s.bf16 && s.d_nope == 32 && s.d_rope == 16 && s.d_v == 32)
     hipLaunchKernelGGL((dq_kernel<float, MmaF32, 1, 32, 16, 32>), dim3(grid), dim3(kThreads), 0, st, a);
   else

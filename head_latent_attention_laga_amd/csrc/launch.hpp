@@ -27,8 +27,11 @@ hipError_t launch_attn_fwd(const Shape& s, const void* q, const void* k_nope, co
                            const void* v, float* o, float* lse, hipStream_t st);
 
 // Backward pieces.  Workspace carving lives in the API layer.
-hipError_t launch_bwd_dot(const Shape& s, const float* o, const void* d_o, float* delta,
-                          hipStream_t st);
+// delta = rowsum(dO * o); for bfloat16 inputs also fp16 copies of q, dO and
+// k_pe (q16 [T,h,d_qk], do16 [T,h,d_v], kpe16 [T,d_rope]), which the two
+// attention-backward launchers then take in place of the inputs.
+hipError_t launch_bwd_prep(const Shape& s, const float* o, const void* q, const void* d_o, const void* k_pe,
+                           float* delta, void* q16, void* do16, void* kpe16, hipStream_t st);
 hipError_t launch_attn_bwd_dkdv(const Shape& s, const void* q, const void* k_nope,
                                 const void* k_pe, const void* v, const float* lse,
                                 const float* delta, const void* d_o, void* dkv,
