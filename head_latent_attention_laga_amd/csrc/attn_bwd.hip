@@ -45,11 +45,10 @@ struct Dkdv {
   static constexpr int DQK = DN + DR, C = DN + DV;
   static constexpr int BQ = 32, BK = 128;
   static constexpr bool TR = M::KPL == 8;  // 16-bit operands: separate transposed-read tiles
-  static constexpr int LQR = DQK + TilePad<M>::row, LQT = DQK + TilePad<M>::tr;
-  static constexpr int LOR = DV + TilePad<M>::row, LOT = DV + TilePad<M>::tr;
-  static constexpr int QR_B = BQ * LQR * sizeof(E), QT_B = TR ? BQ * LQT * sizeof(E) : 0;
-  static constexpr int OR_B = BQ * LOR * sizeof(E), OT_B = TR ? BQ * LOT * sizeof(E) : 0;
-  static constexpr int BUF_BYTES = QR_B + QT_B + OR_B + OT_B + 2 * BQ * 4;
+  // One q tile and one dO tile per block, read both as rows and transposed.
+  static constexpr int LQR = DQK + TilePad<M>::both, LOR = DV + TilePad<M>::both;
+  static constexpr int QR_B = BQ * LQR * sizeof(E), OR_B = BQ * LOR * sizeof(E);
+  static constexpr int BUF_BYTES = QR_B + OR_B + 2 * BQ * 4;
   // The lo planes of the workgroup's K and V (split operands) stay in LDS for
   // the whole kernel; the hi parts live in registers.
   static constexpr int LLO = (DN > DV ? DN : DV) + TilePad<M>::row;
@@ -103,10 +102,8 @@ struct Dkdv {
 
   __device__ static void store(const Regs& R, char* buf) {
     E* Qr = reinterpret_cast<E*>(buf);
-    E* Qt = reinterpret_cast<E*>(buf + QR_B);
-    E* Or = reinterpret_cast<E*>(buf + QR_B + QT_B);
-    E* Ot = reinterpret_cast<E*>(buf + QR_B + QT_B + OR_B);
-    float* st = reinterpret_cast<float*>(buf + QR_B + QT_B + OR_B + OT_B);
+    E* Or = reinterpret_cast<E*>(buf + QR_B);
+    float* st = reinterpret_cast<float*>(buf + QR_B + OR_B);
     const int tid = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < IQ; ++i) {
@@ -118,7 +115,6 @@ struct Dkdv {
 #pragma unroll
       for (int j = 0; j < IPC; j += 16 / sizeof(E)) {
         *reinterpret_cast<u32x4*>(Qr + r * LQR + col + j) = *reinterpret_cast<u32x4*>(tmp + j);
-        if constexpr (TR) *reinterpret_cast<u32x4*>(Qt + r * LQT + col + j) = *reinterpret_cast<u32x4*>(tmp + j);
       }
     }
 #pragma unroll
@@ -131,7 +127,6 @@ struct Dkdv {
 #pragma unroll
       for (int j = 0; j < IPC; j += 16 / sizeof(E)) {
         *reinterpret_cast<u32x4*>(Or + r * LOR + col + j) = *reinterpret_cast<u32x4*>(tmp + j);
-        if constexpr (TR) *reinterpret_cast<u32x4*>(Ot + r * LOT + col + j) = *reinterpret_cast<u32x4*>(tmp + j);
       }
     }
     if (tid < BQ) {
@@ -143,13 +138,13 @@ struct Dkdv {
   // A operand of a product whose k index runs over the queries of the block:
   // rows n0 + lane%32 of the transposed tile (dims), queries of accumulator
   // registers st*KPL .. (see acc_key_col).
-  __device__ static F tr_frag(const E* Rt, const E* Rr, int ldt, int ldr, int st, int n0) {
+  __device__ static F tr_frag(const E* T, int ld, int st, int n0) {
     if constexpr (TR) {
-      return tr_frag_acc(Rt, ldt, st * 16, n0);
+      return tr_frag_acc(T, ld, st * 16, n0);
     } else {
       const int lane = threadIdx.x % kWave;
       const int qi = 8 * (st / 4) + 4 * (lane / 32) + (st % 4);
-      return Rr[qi * ldr + n0 + lane % 32];
+      return T[qi * ld + n0 + lane % 32];
     }
   }
 
@@ -177,10 +172,8 @@ struct Dkdv {
     const int hf = lane / 32, col = lane % 32;
     if (MASK && q0 + BQ - 1 < wk0) return;  // every query of the block precedes these keys
     const E* Qr = reinterpret_cast<const E*>(buf);
-    const E* Qt = reinterpret_cast<const E*>(buf + QR_B);
-    const E* Or = reinterpret_cast<const E*>(buf + QR_B + QT_B);
-    const E* Ot = reinterpret_cast<const E*>(buf + QR_B + QT_B + OR_B);
-    const float* st = reinterpret_cast<const float*>(buf + QR_B + QT_B + OR_B + OT_B);
+    const E* Or = reinterpret_cast<const E*>(buf + QR_B);
+    const float* st = reinterpret_cast<const float*>(buf + QR_B + OR_B);
 
     // S[q, key], dP[q, key]: rows = queries 8g + 4hf + i, column = key.  The
     // chains run one after the other so that the vector work on each result
@@ -235,7 +228,7 @@ struct Dkdv {
     for (int stp = 0; stp < STEPS; ++stp)
 #pragma unroll
       for (int n = 0; n < NVT; ++n) {
-        const F oa = tr_frag(Ot, Or, LOT, LOR, stp, n * 32);
+        const F oa = tr_frag(Or, LOR, stp, n * 32);
 #pragma unroll
         for (int q = 0; q < NS; ++q) acc.dvt[n] = M::mma(oa, *reinterpret_cast<F*>(ph[stp][q]), acc.dvt[n]);
       }
@@ -259,7 +252,7 @@ struct Dkdv {
     for (int stp = 0; stp < STEPS; ++stp)
 #pragma unroll
       for (int n = 0; n < NKT; ++n) {
-        const F qa = tr_frag(Qt, Qr, LQT, LQR, stp, n * 32);
+        const F qa = tr_frag(Qr, LQR, stp, n * 32);
 #pragma unroll
         for (int q = 0; q < NS; ++q) acc.dk[n] = M::mma(qa, *reinterpret_cast<F*>(dh[stp][q]), acc.dk[n]);
       }

@@ -26,8 +26,12 @@ struct BwdArgs {
 // Row pitches (elements) of LDS tiles: rows read one per lane with 16-byte
 // reads are padded by 16 bytes; rows read with transposing reads (4 rows x
 // 64 bytes per half-wavefront) are padded to a pitch of 16 mod 64 dwords.
-template <class M> struct TilePad { static constexpr int row = 8, tr = 32; };
-template <> struct TilePad<MmaF32> { static constexpr int row = 4, tr = 4; };  // keeps 16-byte row alignment
+// Row padding (elements) of LDS tiles.  `row`: tiles read only with 16-byte
+// row fragments.  `both`: tiles also read with transposing reads; a pitch of
+// 8 (mod 16) dwords keeps the eight rows of a 16-byte read and the four rows
+// of a transposing read on distinct banks.
+template <class M> struct TilePad { static constexpr int row = 8, both = 16; };
+template <> struct TilePad<MmaF32> { static constexpr int row = 4, both = 4; };  // keeps 16-byte row alignment
 
 // 16-byte chunk of `E` converted from a 16-byte chunk of the input type.
 template <class E, class InT>

@@ -30,10 +30,11 @@ struct Dq {
   static constexpr int DQK = DN + DR;
   static constexpr int BM = 128, BN = 64;
   static constexpr bool TR = M::KPL == 8;
-  static constexpr int LKR = DQK + TilePad<M>::row, LKT = DQK + TilePad<M>::tr, LVR = DV + TilePad<M>::row;
-  static constexpr int KR_B = BN * LKR * sizeof(E), KT_B = TR ? BN * LKT * sizeof(E) : 0;
+  // One K tile read both as rows (S^T) and transposed (dq^T); V rows only.
+  static constexpr int LKR = DQK + TilePad<M>::both, LVR = DV + TilePad<M>::row;
+  static constexpr int KR_B = BN * LKR * sizeof(E);
   static constexpr int VR_B = BN * LVR * sizeof(E);
-  static constexpr int BUF_BYTES = KR_B + KT_B + VR_B;
+  static constexpr int BUF_BYTES = KR_B + VR_B;
   static constexpr int KS_QK = DQK / M::K, KS_V = DV / M::K;
   static constexpr int NT = BN / 32, NQT = (DQK + 31) / 32, STEPS = 32 / M::K;
   // Staging chunks (16 bytes): nope part of K (hi plane), rope band (input type), V (hi plane).
@@ -76,8 +77,7 @@ struct Dq {
 
   __device__ static void store(const Regs& R, char* buf) {
     E* Kr = reinterpret_cast<E*>(buf);
-    E* Kt = reinterpret_cast<E*>(buf + KR_B);
-    E* Vr = reinterpret_cast<E*>(buf + KR_B + KT_B);
+    E* Vr = reinterpret_cast<E*>(buf + KR_B);
     const int tid = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < IK; ++i) {
@@ -85,7 +85,6 @@ struct Dq {
       if (KCH % kThreads != 0 && c >= KCH) continue;
       const int r = c / (DN / EPC), col = (c % (DN / EPC)) * EPC;
       *reinterpret_cast<u32x4*>(Kr + r * LKR + col) = R.k[i];
-      if constexpr (TR) *reinterpret_cast<u32x4*>(Kt + r * LKT + col) = R.k[i];
     }
 #pragma unroll
     for (int i = 0; i < IP; ++i) {
@@ -97,7 +96,6 @@ struct Dq {
 #pragma unroll
       for (int j = 0; j < IPC; j += EPC) {
         *reinterpret_cast<u32x4*>(Kr + r * LKR + col + j) = *reinterpret_cast<u32x4*>(tmp + j);
-        if constexpr (TR) *reinterpret_cast<u32x4*>(Kt + r * LKT + col + j) = *reinterpret_cast<u32x4*>(tmp + j);
       }
     }
 #pragma unroll
@@ -123,9 +121,9 @@ struct Dq {
   }
 
   // A operand of dq^T += K^T dS^T for one MFMA step of key atom t.
-  __device__ static F kt_frag(const E* Kt, const E* Kr, int t, int st, int n0) {
+  __device__ static F kt_frag(const E* Kr, int t, int st, int n0) {
     if constexpr (TR) {
-      return tr_frag_acc(Kt, LKT, t * 32 + st * 16, n0);
+      return tr_frag_acc(Kr, LKR, t * 32 + st * 16, n0);
     } else {
       const int lane = threadIdx.x % kWave;
       const int k = t * 32 + 8 * (st / 4) + 4 * (lane / 32) + (st % 4);
@@ -147,8 +145,7 @@ struct Dq {
     const int hf = lane / 32, col = lane % 32;
     if (MASK && key0 > qw + 31) return;  // every key of the block follows these queries
     const E* Kr = reinterpret_cast<const E*>(buf);
-    const E* Kt = reinterpret_cast<const E*>(buf + KR_B);
-    const E* Vr = reinterpret_cast<const E*>(buf + KR_B + KT_B);
+    const E* Vr = reinterpret_cast<const E*>(buf + KR_B);
     // S^T[key, q], dP^T[key, q] for the NT key atoms, chains interleaved.
     f32x16 sc[NT], dp[NT];
 #pragma unroll
@@ -197,7 +194,7 @@ struct Dq {
         for (int j = 0; j < M::KPL; ++j) dh[j] = M::from_f32(dp[t][stp * M::KPL + j]);
         const F df = *reinterpret_cast<F*>(dh);
 #pragma unroll
-        for (int n = 0; n < NQT; ++n) dq[n] = M::mma(kt_frag(Kt, Kr, t, stp, n * 32), df, dq[n]);
+        for (int n = 0; n < NQT; ++n) dq[n] = M::mma(kt_frag(Kr, t, stp, n * 32), df, dq[n]);
       }
   }
 
