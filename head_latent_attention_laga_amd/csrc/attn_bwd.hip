@@ -225,13 +225,15 @@ struct Dkdv {
     }
     // dV^T[dv, key] += dO^T P   (k = queries)
 #pragma unroll
-    for (int stp = 0; stp < STEPS; ++stp)
+    for (int stp = 0; stp < STEPS; ++stp) {
+      F oa[NVT];
 #pragma unroll
-      for (int n = 0; n < NVT; ++n) {
-        const F oa = tr_frag(Or, LOR, stp, n * 32);
+      for (int n = 0; n < NVT; ++n) oa[n] = tr_frag(Or, LOR, stp, n * 32);
 #pragma unroll
-        for (int q = 0; q < NS; ++q) acc.dvt[n] = M::mma(oa, *reinterpret_cast<F*>(ph[stp][q]), acc.dvt[n]);
-      }
+      for (int q = 0; q < NS; ++q)
+#pragma unroll
+        for (int n = 0; n < NVT; ++n) acc.dvt[n] = M::mma(oa[n], *reinterpret_cast<F*>(ph[stp][q]), acc.dvt[n]);
+    }
 
     // dS = P (dP - delta), split the same way.
     E dh[STEPS][NS][M::KPL];
@@ -249,13 +251,15 @@ struct Dkdv {
     }
     // dK^T[d, key] += q^T dS   (k = queries)
 #pragma unroll
-    for (int stp = 0; stp < STEPS; ++stp)
+    for (int stp = 0; stp < STEPS; ++stp) {
+      F qa[NKT];
 #pragma unroll
-      for (int n = 0; n < NKT; ++n) {
-        const F qa = tr_frag(Qr, LQR, stp, n * 32);
+      for (int n = 0; n < NKT; ++n) qa[n] = tr_frag(Qr, LQR, stp, n * 32);
 #pragma unroll
-        for (int q = 0; q < NS; ++q) acc.dk[n] = M::mma(qa, *reinterpret_cast<F*>(dh[stp][q]), acc.dk[n]);
-      }
+      for (int q = 0; q < NS; ++q)
+#pragma unroll
+        for (int n = 0; n < NKT; ++n) acc.dk[n] = M::mma(qa[n], *reinterpret_cast<F*>(dh[stp][q]), acc.dk[n]);
+    }
   }
 
   // Publish the staged block `it`, start loading the next one, compute.

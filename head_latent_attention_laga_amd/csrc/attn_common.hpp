@@ -56,6 +56,28 @@ __device__ __forceinline__ half8 tr_frag(const E* tile, int ld, int k0, int n0) 
   return __builtin_bit_cast(half8, r);
 }
 
+// Tiles read only with transposing reads can go unpadded with an XOR swizzle
+// of their 16-byte blocks: block b of row r is stored at b ^ (4 * (r % 4)).
+// A transposing read takes four consecutive rows x 64 bytes per 32 lanes;
+// with a row pitch of a multiple of 256 bytes the swizzle puts those four
+// 64-byte spans in four different windows of the 64 banks.
+__device__ __forceinline__ int swz_block(int r, int b) { return b ^ (4 * (r & 3)); }
+
+// tr_frag_acc on a swizzled tile (ld a multiple of 128 elements, k0 % 4 == 0).
+template <class E>
+__device__ __forceinline__ half8 tr_frag_acc_swz(const E* tile, int ld, int k0, int n0) {
+  static_assert(sizeof(E) == 2, "16-bit tiles only");
+  const int lane = threadIdx.x % kWave;
+  const int g = lane / 16, s = lane % 16, hf = lane / 32;
+  const int row = k0 + 4 * hf + s / 4;  // row % 4 == s / 4
+  const int col = 8 * swz_block(s / 4, n0 / 8 + 2 * (g % 2) + (s % 4) / 2) + 4 * (s % 2);
+  s16x4 a = ds_read_tr16(tile + row * ld + col);
+  s16x4 b = ds_read_tr16(tile + (row + 8) * ld + col);
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(half8, r);
+}
+
 // One 16-byte chunk of a [rows x cols] tile copied from global memory:
 // row r of the source starts at src + r*ld (elements), rows >= nrows read as 0.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

@@ -48,10 +48,10 @@ struct FwdArgs {
   int64_t S, plane_k, plane_v; int B, h, n_qt; float scale_log2;
 };
 
-// Row padding (elements) of the K, rope and V tiles; V rows of fp16 tiles are
-// padded by 64 bytes (conflict-free transposing reads) unless LDS is short.
-template <class M, int NS> struct Pads { static constexpr int k = 8, r = 8, v = NS == 1 ? 32 : 16; };
-template <int NS> struct Pads<MmaF32, NS> { static constexpr int k = 4, r = 4, v = 4; };
+// Row padding (elements) of the K, rope and V tiles.  16-bit V tiles are
+// read only with transposing reads and go unpadded with swizzled blocks.
+template <class M, int NS> struct Pads { static constexpr int k = 8, r = 8, v = 0; static constexpr bool swz = true; };
+template <int NS> struct Pads<MmaF32, NS> { static constexpr int k = 4, r = 4, v = 4; static constexpr bool swz = false; };
 
 // M: K/V/P operand type (fp16 or fp32); MR: rope operand type (bf16 or fp32);
 // InT: storage type of q and k_pe.
@@ -102,13 +102,15 @@ struct Fwd {
     }
   }
 
-  template <int CPR, int PER, int PITCH_BYTES>
+  template <int CPR, int PER, int PITCH_BYTES, bool SWZ = false>
   __device__ static void store_region(const u32x4* in, char* lds_region) {
+    static_assert(!SWZ || (CPR >= 16 && PITCH_BYTES % 256 == 0), "swizzled rows span whole 256-byte windows");
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int c = i * NT + static_cast<int>(threadIdx.x);
       const int plane = c / (BN * CPR), r = (c % (BN * CPR)) / CPR, lc = c % CPR;
-      *reinterpret_cast<u32x4*>(lds_region + (plane * BN + r) * PITCH_BYTES + lc * 16) = in[i];
+      const int pc = SWZ ? swz_block(r, lc) : lc;
+      *reinterpret_cast<u32x4*>(lds_region + (plane * BN + r) * PITCH_BYTES + pc * 16) = in[i];
     }
   }
 
@@ -126,7 +128,7 @@ struct Fwd {
   __device__ static void store_block(const Regs& R, char* buf) {
     store_region<CK, IK, LDK * sizeof(E)>(R.k, buf);
     store_region<CR, IR, LDR * sizeof(ER)>(R.r, buf + K_BYTES);
-    store_region<CV, IV, LDV * sizeof(E)>(R.v, buf + K_BYTES + R_BYTES);
+    store_region<CV, IV, LDV * sizeof(E), Pads<M, NS>::swz>(R.v, buf + K_BYTES + R_BYTES);
   }
 
   __device__ static F k_frag(const E* Kp, int r, int c0) { return lds_frag<M>(Kp + r * LDK + c0); }
@@ -136,7 +138,7 @@ struct Fwd {
   // accumulator registers st*KPL .. of 32-key atom t (see acc_key_col).
   __device__ static F v_frag(const E* Vp, int t, int st, int n0) {
     if constexpr (M::KPL == 8) {
-      return tr_frag_acc(Vp, LDV, t * 32 + st * 16, n0);
+      return tr_frag_acc_swz(Vp, LDV, t * 32 + st * 16, n0);
     } else {
       const int lane = threadIdx.x % kWave;
       const int key = t * 32 + 8 * (st / 4) + 4 * (lane / 32) + (st % 4);
@@ -228,10 +230,12 @@ struct Fwd {
 #pragma unroll
         for (int j = 0; j < M::KPL; ++j) ph[j] = M::from_f32(sc[t][st * M::KPL + j]);
         const F pf = *reinterpret_cast<F*>(ph);
+        // Plane-outer order: consecutive products go to different accumulators.
 #pragma unroll
-        for (int n = 0; n < NO; ++n) {
-          st_.o[n] = M::mma(v_frag(Vs, t, st, n * 32), pf, st_.o[n]);
-          if constexpr (NS == 2) st_.o[n] = M::mma(v_frag(Vs + BN * LDV, t, st, n * 32), pf, st_.o[n]);
+        for (int n = 0; n < NO; ++n) st_.o[n] = M::mma(v_frag(Vs, t, st, n * 32), pf, st_.o[n]);
+        if constexpr (NS == 2) {
+#pragma unroll
+          for (int n = 0; n < NO; ++n) st_.o[n] = M::mma(v_frag(Vs + BN * LDV, t, st, n * 32), pf, st_.o[n]);
         }
       }
   }
