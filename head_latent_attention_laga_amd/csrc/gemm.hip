@@ -139,7 +139,28 @@ struct SlabT {
 // written as an fp16 hi part in plane 0 and the fp16 rest in plane 1.
 template <class KvT, int NS>
 struct EpiKvUp {
+  static constexpr bool TRANS = true;  // takes 4 consecutive n of one row m
   KvT* kn; KvT* v; int64_t M; int N, C, dn, dv, h; int64_t plane_k, plane_v;
+  // n .. n+3 lie in one head and one part (C, dn multiples of 4).
+  __device__ void store4(int64_t m, int n, f32x4 val) const {
+    if (m >= M || n >= N) return;
+    const int i = n / C, c = n - i * C;
+    KvT* dst = c < dn ? kn + (m * h + i) * dn + c : v + (m * h + i) * dv + (c - dn);
+    const int64_t plane = c < dn ? plane_k : plane_v;
+    KvT part[NS][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      part[0][j] = static_cast<KvT>(val[j]);
+      if constexpr (NS == 2) part[1][j] = static_cast<KvT>(val[j] - static_cast<float>(part[0][j]));
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if constexpr (sizeof(KvT) == 2)
+        *reinterpret_cast<u16x4*>(dst + s * plane) = *reinterpret_cast<const u16x4*>(part[s]);
+      else
+        *reinterpret_cast<f32x4*>(dst + s * plane) = *reinterpret_cast<const f32x4*>(part[s]);
+    }
+  }
   __device__ void operator()(int64_t m, int n, float val) const {
     if (m >= M || n >= N) return;
     const int i = n / C, c = n - i * C;
@@ -159,6 +180,7 @@ struct EpiKvUp {
 };
 
 struct EpiStore {  // out[m * ld + n] (+ chunk offset)
+  static constexpr bool TRANS = false;
   float* p; int64_t M; int N; int64_t ld; int64_t chunk_stride;
   __device__ void operator()(int64_t m, int n, float val) const {
     if (m >= M || n >= N) return;
@@ -190,26 +212,16 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(Operand<typename SA::
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-  typename SA::Slab sa;
-  typename SB::Slab sb;
+  // Two register stages of operand slabs in flight: the loads for step k+2
+  // are issued while step k computes, so about two steps of products cover
+  // the global-memory latency.  The loop is unrolled by two so that each
+  // stage keeps its own registers.
+  typename SA::Slab sa0, sa1;
+  typename SB::Slab sb0, sb1;
   constexpr int NSA = SA::Slab::NS_, NSB = SB::Slab::NS_;
   constexpr int NSMAX = NSA > NSB ? NSA : NSB;
 
-  if (kbeg < kend) {
-    sa.load(A, m0, kbeg);
-    sb.load(B, n0, kbeg);
-  }
-  int buf = 0;
-  for (int64_t k0 = kbeg; k0 < kend; k0 += BK, buf ^= 1) {
-    E* as = reinterpret_cast<E*>(lds + buf * STAGE);
-    E* bs = reinterpret_cast<E*>(lds + buf * STAGE + SA::BYTES);
-    sa.store(as);
-    sb.store(bs);
-    __syncthreads();  // also orders the reads of this buffer two steps ago before the stores above
-    if (k0 + BK < kend) {
-      sa.load(A, m0, k0 + BK);
-      sb.load(B, n0, k0 + BK);
-    }
+  auto compute = [&](const E* as, const E* bs) {
 #pragma unroll
     for (int kk = 0; kk < BK; kk += M::K) {
       typename M::frag af[NSA][2], bfr[NSB][2];
@@ -229,22 +241,64 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(Operand<typename SA::
 #pragma unroll
           for (int a = 0; a < 2; ++a)
 #pragma unroll
-            for (int b = 0; b < 2; ++b) acc[a][b] = M::mma(af[s1][a], bfr[s2][b], acc[a][b]);
+            for (int b = 0; b < 2; ++b) {
+              // EPI::TRANS: the atom holds C^T (rows n, columns m).
+              if constexpr (EPI::TRANS) acc[a][b] = M::mma(bfr[s2][b], af[s1][a], acc[a][b]);
+              else acc[a][b] = M::mma(af[s1][a], bfr[s2][b], acc[a][b]);
+            }
         }
     }
+  };
+  // One step: publish the slabs of step k0 (held in sa/sb) into LDS buffer
+  // `buf`, refill sa/sb with step k0 + 2*BK, compute step k0.
+  auto step = [&](int64_t k0, int buf, typename SA::Slab& sa, typename SB::Slab& sb) {
+    E* as = reinterpret_cast<E*>(lds + buf * STAGE);
+    E* bs = reinterpret_cast<E*>(lds + buf * STAGE + SA::BYTES);
+    sa.store(as);
+    sb.store(bs);
+    __syncthreads();  // also orders the reads of this buffer two steps ago before the stores above
+    if (k0 + 2 * BK < kend) {
+      sa.load(A, m0, k0 + 2 * BK);
+      sb.load(B, n0, k0 + 2 * BK);
+    }
+    compute(as, bs);
+  };
+
+  if (kbeg < kend) {
+    sa0.load(A, m0, kbeg);
+    sb0.load(B, n0, kbeg);
+  }
+  if (kbeg + BK < kend) {
+    sa1.load(A, m0, kbeg + BK);
+    sb1.load(B, n0, kbeg + BK);
+  }
+  for (int64_t k0 = kbeg; k0 < kend; k0 += 2 * BK) {
+    step(k0, 0, sa0, sb0);
+    if (k0 + BK < kend) step(k0 + BK, 1, sa1, sb1);
   }
   // C[r]: row 8*(r/4) + 4*(lane/32) + r%4 of the atom, column lane%32.
   const int lane = threadIdx.x % kWave;
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 2; ++b) {
+      if constexpr (EPI::TRANS) {
+        const int64_t m = m0 + wm * 64 + a * 32 + (lane % 32);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + wm * 64 + a * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
-        const int n = static_cast<int>(n0 + wn * 64 + b * 32 + (lane % 32));
-        epi(m, n, acc[a][b][r]);
+        for (int g = 0; g < 4; ++g) {
+          const int n = static_cast<int>(n0 + wn * 64 + b * 32 + 8 * g + 4 * (lane / 32));
+          const f32x4 v4 = {acc[a][b][4 * g], acc[a][b][4 * g + 1], acc[a][b][4 * g + 2], acc[a][b][4 * g + 3]};
+          epi.store4(m, n, v4);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t m = m0 + wm * 64 + a * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+          const int n = static_cast<int>(n0 + wn * 64 + b * 32 + (lane % 32));
+          epi(m, n, acc[a][b][r]);
+        }
       }
+    }
 }
 
 // Operand description: MFMA type, planes, orientation, rows per tile, source element.
