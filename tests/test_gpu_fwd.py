@@ -59,7 +59,7 @@ def test_f32_shapes(B, S, n_h, P, r):
 
 @pytest.mark.parametrize("precision", [FP16, SPLIT])
 @pytest.mark.parametrize("B,S,n_h,P,r", [(1, 300, 16, 8, 3), (2, 130, 64, 8, 7), (1, 1, 16, 8, 0),
-                                         (1, 64, 128, 16, 2)])
+                                         (1, 64, 128, 16, 2), (1, 1000, 16, 8, 2)])
 def test_bf16_shapes(precision, B, S, n_h, P, r):
     _full_forward_check(_dims(B, S, n_h, P, r, li.BF16), precision, seed=S + P)
 
@@ -85,6 +85,28 @@ def test_full_size_workloads(name, precision):
     check("k_nope", kv_host(out["k_nope"]), kn, d.dtype)
     check("v", kv_host(out["v"]), vv, d.dtype)
     rows = sample_rows(d.S)
+    O, lse = oracle.attention_fwd_rows(v["q"], kn, v["k_pe"], vv, rows)
+    check("o[rows]", host(out["o"])[:, rows], O, d.dtype)
+    check("lse[rows]", host(out["lse"])[..., rows], lse, d.dtype)
+
+
+def test_long_sequence_sampled_rows():
+    """Twice the longest workload's sequence (16 local heads, fp16 operands):
+    index arithmetic of every kernel beyond the workload sizes, checked on
+    sampled query rows."""
+    d = _dims(1, 32768, 128, 8, 0, li.BF16)
+    announce(f"forward long sequence dims={d}")
+    inp = li.make_inputs(d, 11)
+    x = device_inputs(inp)
+    out = make_path(d, FP16).forward(x)
+    torch.cuda.synchronize()
+    v = {k: t.value for k, t in inp.items()}
+    del inp, x
+    heads = oracle.head_shard(d.n_h, d.sp_size, d.sp_rank)
+    L, _ = oracle.latent_rmsnorm(v["latent"], v["gamma"], d.eps)
+    kn, vv = oracle.kv_up(L, v["w_kv_b"], heads, d.d_nope)
+    del L
+    rows = sample_rows(d.S, n=24, seed=3)
     O, lse = oracle.attention_fwd_rows(v["q"], kn, v["k_pe"], vv, rows)
     check("o[rows]", host(out["o"])[:, rows], O, d.dtype)
     check("lse[rows]", host(out["lse"])[..., rows], lse, d.dtype)
