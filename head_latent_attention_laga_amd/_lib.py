@@ -18,6 +18,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "laga.h")
 LAGA_F32, LAGA_BF16 = 0, 1
 LAGA_OPERANDS_FP16, LAGA_OPERANDS_SPLIT = 0, 1
 LAGA_BWD_STAGES = 7
+LAGA_KV_LO_SHIFT = 12  # the #define of laga.h: scale exponent of the e4m3 low plane of split K/V
 BWD_STAGE_NAMES = ("bwd_delta", "attn_bwd_dkdv", "attn_bwd_dq", "dk_pe_head_sum", "fold_dL", "fold_dW",
                    "rmsnorm_bwd")
 STATUS = {0: "LAGA_OK", 1: "LAGA_ERR_INVALID", 2: "LAGA_ERR_UNSUPPORTED", 3: "LAGA_ERR_ALIGN",

@@ -82,7 +82,7 @@ extern "C" {
 size_t laga_kv_elem_bytes(const laga_dims* dims) {
   Shape s;
   if (check_dims(dims, &s) != LAGA_OK) return 0;
-  return (s.bf16 && !s.split) ? 2 : 4;
+  return !s.bf16 ? 4 : s.split ? 3 : 2;  // f32 | fp16 | fp16 + e4m3
 }
 
 laga_status laga_latent_norm(const laga_dims* dims, const void* latent, const void* gamma,

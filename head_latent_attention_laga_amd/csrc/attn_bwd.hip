@@ -304,25 +304,40 @@ struct Dkdv {
     E* klo = reinterpret_cast<E*>(lds + 2 * BUF_BYTES);
     E* vlo = reinterpret_cast<E*>(lds + 2 * BUF_BYTES + LO_B);
     if constexpr (NS == 2) {
-      // Lo planes of this workgroup's 128 keys -> LDS rows (published by the
-      // first barrier of the query loop).  Keys past the sequence read as zero.
+      // Low planes of this workgroup's 128 keys (e4m3 bytes scaled by
+      // 2^kLoShift after the fp16 planes) -> fp16 LDS rows, exactly, published
+      // by the first barrier of the query loop.  Keys past the sequence read as zero.
+      static_assert(sizeof(E) == 2, "low planes decode to fp16");
       const int nkw = static_cast<int>(a.S - k0 < BK ? a.S - k0 : BK);
-      const int krb = a.h * DN * static_cast<int>(sizeof(E)), vrb = a.h * DV * static_cast<int>(sizeof(E));
-      const E* kbase = static_cast<const E*>(a.k_nope) + a.plane_k + ((b * a.S + k0) * a.h + head) * DN;
-      const E* vbase = static_cast<const E*>(a.v) + a.plane_v + ((b * a.S + k0) * a.h + head) * DV;
+      const int krb = a.h * DN, vrb = a.h * DV;
+      const char* kbase = static_cast<const char*>(a.k_nope) + a.plane_k * sizeof(E) + ((b * a.S + k0) * a.h + head) * DN;
+      const char* vbase = static_cast<const char*>(a.v) + a.plane_v * sizeof(E) + ((b * a.S + k0) * a.h + head) * DV;
       const auto rk = rsrc(kbase, nkw * krb), rv = rsrc(vbase, nkw * vrb);
-      constexpr int EPC = 16 / sizeof(E);
+      constexpr float inv = 1.0f / static_cast<float>(1 << kLoShift);
+      auto decode = [&](u32x4 w, E* dst) {
+        E e[16];
 #pragma unroll
-      for (int i = 0; i < BK * DN / EPC / kThreads; ++i) {
+        for (int d = 0; d < 4; ++d) {
+          const f32x2 x = unpack_e4m3x2<false>(w[d]), y = unpack_e4m3x2<true>(w[d]);
+          e[4 * d] = static_cast<E>(x[0] * inv);
+          e[4 * d + 1] = static_cast<E>(x[1] * inv);
+          e[4 * d + 2] = static_cast<E>(y[0] * inv);
+          e[4 * d + 3] = static_cast<E>(y[1] * inv);
+        }
+        *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(e);
+        *reinterpret_cast<u32x4*>(dst + 8) = *reinterpret_cast<const u32x4*>(e + 8);
+      };
+#pragma unroll
+      for (int i = 0; i < BK * DN / 16 / kThreads; ++i) {
         const int c = i * kThreads + static_cast<int>(threadIdx.x);
-        const int r = c / (DN / EPC), j = c % (DN / EPC);
-        *reinterpret_cast<u32x4*>(klo + r * LLO + j * EPC) = __builtin_amdgcn_raw_buffer_load_b128(rk, r * krb + j * 16, 0, 0);
+        const int r = c / (DN / 16), j = c % (DN / 16);
+        decode(__builtin_amdgcn_raw_buffer_load_b128(rk, r * krb + j * 16, 0, 0), klo + r * LLO + j * 16);
       }
 #pragma unroll
-      for (int i = 0; i < BK * DV / EPC / kThreads; ++i) {
+      for (int i = 0; i < BK * DV / 16 / kThreads; ++i) {
         const int c = i * kThreads + static_cast<int>(threadIdx.x);
-        const int r = c / (DV / EPC), j = c % (DV / EPC);
-        *reinterpret_cast<u32x4*>(vlo + r * LLO + j * EPC) = __builtin_amdgcn_raw_buffer_load_b128(rv, r * vrb + j * 16, 0, 0);
+        const int r = c / (DV / 16), j = c % (DV / 16);
+        decode(__builtin_amdgcn_raw_buffer_load_b128(rv, r * vrb + j * 16, 0, 0), vlo + r * LLO + j * 16);
       }
     }
     K.klo_row = klo + (wv * 32 + col) * LLO + hf * M::KPL;  // this lane's key

@@ -78,6 +78,46 @@ __device__ __forceinline__ half8 tr_frag_acc_swz(const E* tile, int ld, int k0, 
   return __builtin_bit_cast(half8, r);
 }
 
+// 8-bit tiles of 128-byte rows read with ds_read_b64_tr_b8 (tr8_frag_acc64):
+// 8-byte word w of row r is stored at w ^ (4 * h(r)), h(r) = bit 1 of r | bit 3
+// of r << 1, i.e. 16-byte chunk c at c ^ (2 * h(r)).  The eight rows one
+// half-wavefront reads (4 consecutive, twice, 8 apart) then cover all 64 banks.
+__device__ __forceinline__ int swz8_h(int r) { return ((r >> 1) & 1) | (((r >> 3) & 1) << 1); }
+__device__ __forceinline__ int swz8_chunk(int r, int c) { return c ^ (2 * swz8_h(r)); }
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+// gfx950 transposing LDS read of 8-bit elements.  Within each group of 16
+// lanes, byte j (0..7) that lane i receives is element i % 8 of the 8-byte
+// word addressed by lane 2j + i/8 of the group.
+__device__ __forceinline__ i32x2 ds_read_tr8(const void* lds_ptr) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(reinterpret_cast<uintptr_t>(lds_ptr)));
+}
+
+// e4m3 A operand (K = 64) of a product against 32x32 accumulators fed as B:
+// from a swizzled [64 keys][128 bytes] tile, lane l gets column 32 n + l % 32
+// and as byte J = 16 t + r the key 32 t + 8 (r / 4) + 4 hf + r % 4, the key
+// that accumulator register r of atom t holds (hf = l / 32).  Read m covers
+// J = 8m .. 8m+7, i.e. keys 16m + {0..3, 8..11} + 4hf; source lane s of a
+// 16-lane group addresses key row 16m + 8 (s/8) + 4 hf + (s/2) % 4 and the
+// 8 columns from 32 n + 16 (g%2) + 8 (s%2) (g = l / 16).
+__device__ __forceinline__ i32x8 tr8_frag_acc64(const uint8_t* tile, int n) {
+  const int lane = threadIdx.x % kWave;
+  const int g = lane / 16, s = lane % 16, hf = lane / 32;
+  const int row = 8 * (s / 8) + 4 * hf + (s / 2) % 4;  // + 16 m; bits 1, 3 fixed by s
+  const int word = 4 * (n ^ swz8_h(row)) + 2 * (g % 2) + (s % 2);
+  const uint8_t* p = tile + row * 128 + 8 * word;
+  i32x8 out;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const i32x2 x = ds_read_tr8(p + m * 16 * 128);
+    out[2 * m] = x[0];
+    out[2 * m + 1] = x[1];
+  }
+  return out;
+}
+
 // One 16-byte chunk of a [rows x cols] tile copied from global memory:
 // row r of the source starts at src + r*ld (elements), rows >= nrows read as 0.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

@@ -27,10 +27,13 @@
 // only blocks crossing it are masked.
 //
 // Precision: NS == 1 uses single fp16 K, V and P.  NS == 2 reads K and V as
-// fp16 hi/lo planes (as laga_kv_up writes them): S = Q.K_hi + Q.K_lo with
-// fp32-class accuracy, and O = P.V_hi + P.V_lo with P in fp16, whose rounding
-// is independent from pair to pair and averages out in O and in the backward's
-// delta = sum dO o.
+// laga_kv_up writes them for split operands, an fp16 hi plane and an e4m3
+// plane of the rest scaled by 2^kLoShift: S = Q.K_hi + Q8.K_lo and
+// O = P.V_hi + P8.V_lo, where the low terms run as e4m3 matrix-core products
+// (K = 64 per instruction, half the cycles of fp16 per element) with q and P
+// rounded to e4m3 -- harmless, as those terms are 2^-11 of the result.  P in
+// fp16 rounds independently from pair to pair and averages out in O and in
+// the backward's delta = sum dO o.
 // The float32 instantiation uses fp32 MFMAs throughout.
 #include "attn_common.hpp"
 #include "launch.hpp"
@@ -67,22 +70,37 @@ struct Fwd {
   static constexpr int EPC = 16 / sizeof(E), RPC = 16 / sizeof(ER);
   static constexpr int CK = DN / EPC, CR = DR / RPC, CV = DV / EPC;
   static constexpr int LDK = DN + Pads<M, NS>::k, LDR = DR + Pads<M, NS>::r, LDV = DV + Pads<M, NS>::v;
-  // LDS buffer: NS K planes | rope band | NS V planes.
-  static constexpr int K_BYTES = NS * BN * LDK * sizeof(E);
+  // NS == 2: K and V also have an e4m3 low plane (see kLoShift).
+  static constexpr bool LO8 = NS == 2;
+  static_assert(!LO8 || sizeof(E) == 2, "low planes complement fp16 operands");
+  static constexpr int K8P = DN + 16;  // byte pitch of the e4m3 K rows (16-byte row reads)
+  // LDS buffer: K | K low | rope band | V | V low.
+  static constexpr int K_BYTES = BN * LDK * sizeof(E);
+  static constexpr int K8_BYTES = LO8 ? BN * K8P : 0;
   static constexpr int R_BYTES = BN * LDR * sizeof(ER);
-  static constexpr int V_BYTES = NS * BN * LDV * sizeof(E);
-  static constexpr int BUF_BYTES = K_BYTES + R_BYTES + V_BYTES;
+  static constexpr int V_BYTES = BN * LDV * sizeof(E);
+  static constexpr int V8_BYTES = LO8 ? BN * DV : 0;
+  static constexpr int OFF_K8 = K_BYTES, OFF_R = OFF_K8 + K8_BYTES, OFF_V = OFF_R + R_BYTES,
+                       OFF_V8 = OFF_V + V_BYTES;
+  static constexpr int BUF_BYTES = OFF_V8 + V8_BYTES;
+  static_assert(OFF_V % 256 == 0 && OFF_V8 % 128 == 0 && BUF_BYTES % 256 == 0, "swizzled tiles stay aligned");
   // 16-byte chunks of data per region (the padding is never loaded).
-  static constexpr int K_CH = NS * BN * CK, R_CH = BN * CR, V_CH = NS * BN * CV;
-  static_assert(K_CH % NT == 0 && R_CH % NT == 0 && V_CH % NT == 0, "staging passes");
+  static constexpr int K_CH = BN * CK, K8_CH = LO8 ? BN * DN / 16 : 0, R_CH = BN * CR, V_CH = BN * CV,
+                       V8_CH = LO8 ? BN * DV / 16 : 0;
+  static_assert(K_CH % NT == 0 && K8_CH % NT == 0 && R_CH % NT == 0 && V_CH % NT == 0 && V8_CH % NT == 0,
+                "staging passes");
   static constexpr int KS_N = DN / M::K, KS_R = DR / MR::K, NO = DV / 32, PV_STEPS = 32 / M::K;
-  static_assert(DN % M::K == 0 && DR % MR::K == 0 && DV % 32 == 0, "head dims");
+  static constexpr int KS_8 = DN / 64;  // e4m3 atoms (K = 64) over d_nope
+  static_assert(DN % M::K == 0 && DR % MR::K == 0 && DV % 32 == 0 && (!LO8 || (DN % 64 == 0 && DV == 128 && BN == 64)),
+                "head dims");
 
   // Staging: chunk c of a plane-major [planes][BN][CPR chunks] region, read
   // from global memory in order (coalesced) and written to its padded row.
   // Each region is a whole number of workgroup passes.
-  static constexpr int IK = K_CH / NT, IR = R_CH / NT, IV = V_CH / NT;
-  struct Regs { u32x4 k[IK]; u32x4 r[IR > 0 ? IR : 1]; u32x4 v[IV]; };
+  static constexpr int IK = K_CH / NT, IK8 = K8_CH / NT, IR = R_CH / NT, IV = V_CH / NT, IV8 = V8_CH / NT;
+  struct Regs {
+    u32x4 k[IK]; u32x4 k8[IK8 > 0 ? IK8 : 1]; u32x4 r[IR > 0 ? IR : 1]; u32x4 v[IV]; u32x4 v8[IV8 > 0 ? IV8 : 1];
+  };
 
   // Buffer loads: one scalar descriptor per (region, plane) and block, lane
   // offsets fixed for the whole kernel.  Rows past the end of the sequence
@@ -102,14 +120,17 @@ struct Fwd {
     }
   }
 
-  template <int CPR, int PER, int PITCH_BYTES, bool SWZ = false>
+  // SWZ: 0 plain rows, 1 swz_block (16-bit transposing reads), 2 swz8_chunk
+  // (8-bit transposing reads).
+  template <int CPR, int PER, int PITCH_BYTES, int SWZ = 0>
   __device__ static void store_region(const u32x4* in, char* lds_region) {
-    static_assert(!SWZ || (CPR >= 16 && PITCH_BYTES % 256 == 0), "swizzled rows span whole 256-byte windows");
+    static_assert(SWZ != 1 || (CPR >= 16 && PITCH_BYTES % 256 == 0), "swizzled rows span whole 256-byte windows");
+    static_assert(SWZ != 2 || (CPR == 8 && PITCH_BYTES == 128), "8-bit swizzle assumes 128-byte rows");
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int c = i * NT + static_cast<int>(threadIdx.x);
       const int plane = c / (BN * CPR), r = (c % (BN * CPR)) / CPR, lc = c % CPR;
-      const int pc = SWZ ? swz_block(r, lc) : lc;
+      const int pc = SWZ == 1 ? swz_block(r, lc) : SWZ == 2 ? swz8_chunk(r, lc) : lc;
       *reinterpret_cast<u32x4*>(lds_region + (plane * BN + r) * PITCH_BYTES + pc * 16) = in[i];
     }
   }
@@ -117,18 +138,26 @@ struct Fwd {
   __device__ static void load_block(const FwdArgs& a, int b, int head, int64_t key0, Regs& R) {
     const int nk = static_cast<int>(a.S - key0 < BN ? a.S - key0 : BN);
     const int64_t row0 = (b * a.S + key0) * a.h + head;
-    load_region<CK, IK>(static_cast<const char*>(a.k_nope) + row0 * DN * sizeof(E), a.plane_k * sizeof(E),
-                        a.h * DN * static_cast<int>(sizeof(E)), nk, R.k);
+    const char* kg = static_cast<const char*>(a.k_nope);
+    const char* vg = static_cast<const char*>(a.v);
+    load_region<CK, IK>(kg + row0 * DN * sizeof(E), 0, a.h * DN * static_cast<int>(sizeof(E)), nk, R.k);
     load_region<CR, IR>(static_cast<const char*>(a.k_pe) + (b * a.S + key0) * DR * sizeof(ER), 0,
                         DR * static_cast<int>(sizeof(ER)), nk, R.r);
-    load_region<CV, IV>(static_cast<const char*>(a.v) + row0 * DV * sizeof(E), a.plane_v * sizeof(E),
-                        a.h * DV * static_cast<int>(sizeof(E)), nk, R.v);
+    load_region<CV, IV>(vg + row0 * DV * sizeof(E), 0, a.h * DV * static_cast<int>(sizeof(E)), nk, R.v);
+    if constexpr (LO8) {  // byte planes after the fp16 planes
+      load_region<DN / 16, IK8>(kg + a.plane_k * sizeof(E) + row0 * DN, 0, a.h * DN, nk, R.k8);
+      load_region<DV / 16, IV8>(vg + a.plane_v * sizeof(E) + row0 * DV, 0, a.h * DV, nk, R.v8);
+    }
   }
 
   __device__ static void store_block(const Regs& R, char* buf) {
     store_region<CK, IK, LDK * sizeof(E)>(R.k, buf);
-    store_region<CR, IR, LDR * sizeof(ER)>(R.r, buf + K_BYTES);
-    store_region<CV, IV, LDV * sizeof(E), Pads<M, NS>::swz>(R.v, buf + K_BYTES + R_BYTES);
+    store_region<CR, IR, LDR * sizeof(ER)>(R.r, buf + OFF_R);
+    store_region<CV, IV, LDV * sizeof(E), Pads<M, NS>::swz ? 1 : 0>(R.v, buf + OFF_V);
+    if constexpr (LO8) {
+      store_region<DN / 16, IK8, K8P>(R.k8, buf + OFF_K8);
+      store_region<DV / 16, IV8, DV, 2>(R.v8, buf + OFF_V8);
+    }
   }
 
   __device__ static F k_frag(const E* Kp, int r, int c0) { return lds_frag<M>(Kp + r * LDK + c0); }
@@ -146,7 +175,17 @@ struct Fwd {
     }
   }
 
+  // A operand of S_lo^T += K_lo . Q^T, e4m3 atom s: key row krow, bytes
+  // 64 s + 32 hf + [0, 32) of the row.
+  __device__ static i32x8 k8_frag(const uint8_t* K8, int krow, int s, int hf) {
+    const uint8_t* p = K8 + krow * K8P + 64 * s + 32 * hf;
+    const u32x4 x = *reinterpret_cast<const u32x4*>(p), y = *reinterpret_cast<const u32x4*>(p + 16);
+    return i32x8{static_cast<int>(x[0]), static_cast<int>(x[1]), static_cast<int>(x[2]), static_cast<int>(x[3]),
+                 static_cast<int>(y[0]), static_cast<int>(y[1]), static_cast<int>(y[2]), static_cast<int>(y[3])};
+  }
+
   struct State {
+    i32x8 q8[LO8 ? KS_8 : 1];
     F qn[KS_N];
     FR qr[KS_R];
     f32x16 o[NO];
@@ -158,8 +197,10 @@ struct Fwd {
     const int lane = threadIdx.x % kWave;
     const int hf = lane / 32, col = lane % 32;
     const E* Ks = reinterpret_cast<const E*>(buf);
-    const ER* Kr = reinterpret_cast<const ER*>(buf + K_BYTES);
-    const E* Vs = reinterpret_cast<const E*>(buf + K_BYTES + R_BYTES);
+    const ER* Kr = reinterpret_cast<const ER*>(buf + OFF_R);
+    const E* Vs = reinterpret_cast<const E*>(buf + OFF_V);
+    const uint8_t* K8 = reinterpret_cast<const uint8_t*>(buf + OFF_K8);
+    const uint8_t* V8 = reinterpret_cast<const uint8_t*>(buf + OFF_V8);
 
     f32x16 sc[2];
 #pragma unroll
@@ -172,13 +213,18 @@ struct Fwd {
       for (int t = 0; t < 2; ++t) {
         const int krow = t * 32 + col;
         sc[t] = M::mma(k_frag(Ks, krow, s * M::K + hf * M::KPL), st_.qn[s], sc[t]);
-        if constexpr (NS == 2)
-          sc[t] = M::mma(k_frag(Ks + BN * LDK, krow, s * M::K + hf * M::KPL), st_.qn[s], sc[t]);
       }
 #pragma unroll
     for (int s = 0; s < KS_R; ++s)
 #pragma unroll
       for (int t = 0; t < 2; ++t) sc[t] = MR::mma(r_frag(Kr, t * 32 + col, s * MR::K + hf * MR::KPL), st_.qr[s], sc[t]);
+    if constexpr (LO8) {  // + Q . K_lo: e4m3 K_lo * 2^kLoShift against e4m3 q
+#pragma unroll
+      for (int s = 0; s < KS_8; ++s)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          sc[t] = mma_e4m3(k8_frag(K8, t * 32 + col, s, hf), st_.q8[s], sc[t], 127 - kLoShift, 127);
+    }
 
     // Causal mask, only on blocks that cross this wavefront's diagonal: key
     // key0 + t*32 + 8(r/4) + 4hf + r%4 is masked when it exceeds the query.
@@ -230,14 +276,22 @@ struct Fwd {
 #pragma unroll
         for (int j = 0; j < M::KPL; ++j) ph[j] = M::from_f32(sc[t][st * M::KPL + j]);
         const F pf = *reinterpret_cast<F*>(ph);
-        // Plane-outer order: consecutive products go to different accumulators.
 #pragma unroll
         for (int n = 0; n < NO; ++n) st_.o[n] = M::mma(v_frag(Vs, t, st, n * 32), pf, st_.o[n]);
-        if constexpr (NS == 2) {
-#pragma unroll
-          for (int n = 0; n < NO; ++n) st_.o[n] = M::mma(v_frag(Vs + BN * LDV, t, st, n * 32), pf, st_.o[n]);
-        }
       }
+    if constexpr (LO8) {
+      // + P . V_lo over the whole block in one e4m3 atom per 32 dv: byte
+      // 16 t + r of a lane's P operand is its probability sc[t][r].
+      i32x8 p8;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          p8[4 * t + g] = static_cast<int>(
+              pack_e4m3x4(sc[t][4 * g], sc[t][4 * g + 1], sc[t][4 * g + 2], sc[t][4 * g + 3]));
+#pragma unroll
+      for (int n = 0; n < NO; ++n) st_.o[n] = mma_e4m3(tr8_frag_acc64(V8, n), p8, st_.o[n], 127 - kLoShift, 127);
+    }
   }
 
   // One key block: publish the prefetched block, prefetch the next one, and
@@ -300,6 +354,19 @@ struct Fwd {
         for (int j = 0; j < M::KPL; ++j) tmp[j] = M::from_f32(qvalid ? to_f32(qp[s * M::K + hf * M::KPL + j]) : 0.f);
       }
       st_.qn[s] = *reinterpret_cast<F*>(tmp);
+    }
+    if constexpr (LO8) {  // e4m3 copy of q_nope for the low-plane products: dims 64 s + 32 hf + [0, 32)
+#pragma unroll
+      for (int s = 0; s < KS_8; ++s)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const u16x8 raw = qvalid ? *reinterpret_cast<const u16x8*>(qp + 64 * s + 32 * hf + 8 * c) : u16x8{};
+          float f[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) f[j] = to_f32(static_cast<InT>(raw[j]));
+          st_.q8[s][2 * c] = static_cast<int>(pack_e4m3x4(f[0], f[1], f[2], f[3]));
+          st_.q8[s][2 * c + 1] = static_cast<int>(pack_e4m3x4(f[4], f[5], f[6], f[7]));
+        }
     }
 #pragma unroll
     for (int s = 0; s < KS_R; ++s) {

@@ -16,6 +16,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "laga.h"
+
 namespace laga {
 
 typedef _Float16 half_t;
@@ -91,6 +93,39 @@ struct MmaF32 {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
   }
 };
+
+// ------------------------------------------------------------ fp8 (OCP e4m3)
+// The low part of a split K/V value (x - fp16(x), at most 2^-11 |x|) is kept
+// as e4m3 bytes scaled by 2^kLoShift: with |x| < 256 the scaled value stays
+// below e4m3's 448, and the 3-bit mantissa leaves x represented to ~2^-15.
+// Larger |x| saturate the low byte, which degrades gracefully towards fp16.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+constexpr int kLoShift = LAGA_KV_LO_SHIFT;
+constexpr float kE4m3Max = 448.f;
+
+// Four floats -> four e4m3 bytes, first value in the lowest byte (round to
+// nearest even; saturated at +-448 before conversion).
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+  a = fminf(fmaxf(a, -kE4m3Max), kE4m3Max);
+  b = fminf(fmaxf(b, -kE4m3Max), kE4m3Max);
+  c = fminf(fmaxf(c, -kE4m3Max), kE4m3Max);
+  d = fminf(fmaxf(d, -kE4m3Max), kE4m3Max);
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
+}
+
+// Bytes 2*HI .. 2*HI+1 of w (e4m3) -> two floats.
+template <bool HI>
+__device__ __forceinline__ f32x2 unpack_e4m3x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), HI);
+}
+
+// C += (A * 2^(ea-127)) . (B * 2^(eb-127)) with e4m3 operands, K = 64: lane l
+// supplies row / column l % 32 and k = (l / 32) * 32 + [0, 32) as 32 bytes.
+__device__ __forceinline__ f32x16 mma_e4m3(i32x8 a, i32x8 b, f32x16 c, int ea, int eb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, ea, 0, eb);
+}
 
 // Split a float into NS terms of the MMA element type: x ~= sum_s part[s].
 template <class M, int NS>

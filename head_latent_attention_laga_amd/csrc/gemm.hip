@@ -135,46 +135,34 @@ struct SlabT {
 };
 
 // ----------------------------------------------------------------- epilogues
-// n = i*C + c -> k_nope[t,i,c] or v[t,i,c-d_nope]; with NS == 2 the value is
-// written as an fp16 hi part in plane 0 and the fp16 rest in plane 1.
+// n = i*C + c -> k_nope[t,i,c] or v[t,i,c-d_nope].  With NS == 2 (fp16
+// storage) the value x is written as hi = fp16(x) in a first plane and the
+// rest as an e4m3 byte of (x - hi) * 2^kLoShift in a byte plane after it.
 template <class KvT, int NS>
 struct EpiKvUp {
+  static_assert(NS == 1 || sizeof(KvT) == 2, "the split form stores fp16 + e4m3");
   static constexpr bool TRANS = true;  // takes 4 consecutive n of one row m
   KvT* kn; KvT* v; int64_t M; int N, C, dn, dv, h; int64_t plane_k, plane_v;
   // n .. n+3 lie in one head and one part (C, dn multiples of 4).
   __device__ void store4(int64_t m, int n, f32x4 val) const {
     if (m >= M || n >= N) return;
     const int i = n / C, c = n - i * C;
-    KvT* dst = c < dn ? kn + (m * h + i) * dn + c : v + (m * h + i) * dv + (c - dn);
-    const int64_t plane = c < dn ? plane_k : plane_v;
-    KvT part[NS][4];
+    const bool isk = c < dn;
+    const int64_t e = isk ? (m * h + i) * dn + c : (m * h + i) * dv + (c - dn);
+    KvT* base = isk ? kn : v;
+    KvT hi[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      part[0][j] = static_cast<KvT>(val[j]);
-      if constexpr (NS == 2) part[1][j] = static_cast<KvT>(val[j] - static_cast<float>(part[0][j]));
-    }
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      if constexpr (sizeof(KvT) == 2)
-        *reinterpret_cast<u16x4*>(dst + s * plane) = *reinterpret_cast<const u16x4*>(part[s]);
-      else
-        *reinterpret_cast<f32x4*>(dst + s * plane) = *reinterpret_cast<const f32x4*>(part[s]);
-    }
-  }
-  __device__ void operator()(int64_t m, int n, float val) const {
-    if (m >= M || n >= N) return;
-    const int i = n / C, c = n - i * C;
-    KvT part[NS];
-    if constexpr (NS == 1) {
-      part[0] = static_cast<KvT>(val);
-    } else {
-      part[0] = static_cast<KvT>(val);
-      part[1] = static_cast<KvT>(val - static_cast<float>(part[0]));
-    }
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      if (c < dn) kn[s * plane_k + (m * h + i) * dn + c] = part[s];
-      else v[s * plane_v + (m * h + i) * dv + (c - dn)] = part[s];
+    for (int j = 0; j < 4; ++j) hi[j] = static_cast<KvT>(val[j]);
+    if constexpr (sizeof(KvT) == 2)
+      *reinterpret_cast<u16x4*>(base + e) = *reinterpret_cast<const u16x4*>(hi);
+    else
+      *reinterpret_cast<f32x4*>(base + e) = *reinterpret_cast<const f32x4*>(hi);
+    if constexpr (NS == 2) {
+      constexpr float sc = static_cast<float>(1 << kLoShift);
+      uint8_t* lo = reinterpret_cast<uint8_t*>(base + (isk ? plane_k : plane_v));
+      *reinterpret_cast<uint32_t*>(lo + e) =
+          pack_e4m3x4((val[0] - static_cast<float>(hi[0])) * sc, (val[1] - static_cast<float>(hi[1])) * sc,
+                      (val[2] - static_cast<float>(hi[2])) * sc, (val[3] - static_cast<float>(hi[3])) * sc);
     }
   }
 };

@@ -25,11 +25,27 @@ class LagaPath:
         kvb = _lib.kv_elem_bytes(self.dims)
         if kvb == 0:
             raise _lib.LagaError("laga_kv_elem_bytes", 2, "dims rejected")
-        # k_nope / v storage: [planes, B, S, h, d]; bf16 inputs store fp16 (two
-        # planes hi, lo with split operands), float32 inputs one float32 plane.
-        bf16 = dtype == "bf16"
-        self.kv_dtype = torch.float16 if bf16 else torch.float32
-        self.kv_planes = kvb // 2 if bf16 else 1
+        # k_nope / v storage (laga.h): float32, fp16, or an fp16 plane followed
+        # by an e4m3 low plane (kvb == 3); held here as flat byte tensors.
+        self.kv_bytes = kvb
+
+    def _kv_empty(self, width):
+        return torch.empty((self.B * self.S * self.h * width * self.kv_bytes,), dtype=torch.uint8,
+                           device=self.device)
+
+    def kv_value(self, t, width):
+        """The value a k_nope / v buffer of row width `width` holds, as a float64
+        [B, S, h, width] CPU tensor (decoding only; for checks and inspection)."""
+        shape = (self.B, self.S, self.h, width)
+        n = self.B * self.S * self.h * width
+        t = t.detach().cpu()
+        if self.kv_bytes == 4:
+            return t.view(torch.float32).double().view(shape)
+        hi = t[:2 * n].view(torch.float16).double().view(shape)
+        if self.kv_bytes == 2:
+            return hi
+        lo = t[2 * n:].view(torch.float8_e4m3fn).double().view(shape)
+        return hi + lo * 2.0 ** -_lib.LAGA_KV_LO_SHIFT
 
     def _empty(self, shape, dtype=torch.float32):
         return torch.empty(shape, dtype=dtype, device=self.device)
@@ -38,8 +54,7 @@ class LagaPath:
         B, S, h = self.B, self.S, self.h
         return dict(
             latent_n=self._empty((B, S, self.d_kv)), rstd=self._empty((B, S)),
-            k_nope=self._empty((self.kv_planes, B, S, h, self.d_nope), self.kv_dtype),
-            v=self._empty((self.kv_planes, B, S, h, self.d_v), self.kv_dtype),
+            k_nope=self._kv_empty(self.d_nope), v=self._kv_empty(self.d_v),
             o=self._empty((B, S, h, self.d_v)), lse=self._empty((B, h, S)))
 
     def forward(self, x, out=None, stream=None):
@@ -49,11 +64,6 @@ class LagaPath:
         _lib.kv_up(self.dims, out["latent_n"], x["w_kv_b"], out["k_nope"], out["v"], stream)
         _lib.attn_fwd(self.dims, x["q"], out["k_nope"], x["k_pe"], out["v"], out["o"], out["lse"], stream)
         return out
-
-    @staticmethod
-    def kv_value(t):
-        """The value a k_nope / v buffer holds: the sum of its planes, as float32."""
-        return t.float().sum(0)
 
     def alloc_backward(self):
         B, S, h = self.B, self.S, self.h

@@ -35,12 +35,14 @@
  *                                    then the d_v V rows; rows of H_r are read
  *   q        [B, S, h, d_qk] in      nope part first, rope part already rotated
  *   k_pe     [B, S, d_rope] in       one band shared by every head
- *   k_nope   [P, B, S, h, d_nope] kv  P value planes, see below
- *   v        [P, B, S, h, d_v]    kv
- * K/V storage ("kv"): float32 with P = 1 for LAGA_F32; fp16 with P = 1 for
- * LAGA_BF16 + LAGA_OPERANDS_FP16; fp16 with P = 2 for LAGA_BF16 +
- * LAGA_OPERANDS_SPLIT, where plane 0 holds hi = fp16(x) and plane 1 holds
- * fp16(x - hi), the value being their sum.
+ *   k_nope   [B, S, h, d_nope] kv  see below
+ *   v        [B, S, h, d_v]    kv
+ * K/V storage ("kv"): float32 for LAGA_F32; fp16 for LAGA_BF16 +
+ * LAGA_OPERANDS_FP16; for LAGA_BF16 + LAGA_OPERANDS_SPLIT an fp16 plane
+ * hi = fp16(x) [B, S, h, d] followed by a byte plane [B, S, h, d] of OCP e4m3
+ * values lo = e4m3((x - hi) * 2^LAGA_KV_LO_SHIFT) (round to nearest even,
+ * saturated at +-448), the value being hi + lo * 2^-LAGA_KV_LO_SHIFT: about
+ * 2^-15 relative for |x| < 256, fp16 accuracy beyond.
  *   o        [B, S, h, d_v]  float32
  *   lse      [B, h, S]       float32 natural-log sum of exp(scores) per query
  */
@@ -65,14 +67,19 @@ typedef enum {
 
 typedef enum { LAGA_F32 = 0, LAGA_BF16 = 1 } laga_dtype;
 
+/* Scale exponent of the e4m3 low plane of split K/V storage (see above). */
+#define LAGA_KV_LO_SHIFT 12
+
 /*
  * Operand precision of the matrix-core contractions for LAGA_BF16 inputs.
  *  LAGA_OPERANDS_FP16:  K/V are stored as fp16; scores, probabilities and V
  *                       enter the MFMAs as single fp16 values (fp32 accumulate).
- *  LAGA_OPERANDS_SPLIT: K/V are stored as fp16 hi/lo planes and every computed operand
- *                       (L, K, V, P, dS, and the fold operands) enters the
- *                       MFMAs as a hi+lo pair of fp16/bf16 values, giving
- *                       fp32-class results at 2-3x the matrix-core work.
+ *  LAGA_OPERANDS_SPLIT: K/V are stored as an fp16 hi plane plus an e4m3 low
+ *                       plane, and every computed operand (L, K, V, P, dS,
+ *                       and the fold operands) enters the MFMAs as a hi+lo
+ *                       pair (fp16/bf16 hi; the K/V low terms of the forward
+ *                       as e4m3 products), giving fp32-class results at
+ *                       1.4-3x the matrix-core work.
  * LAGA_F32 inputs always use float32 MFMAs and float32 K/V (field ignored).
  * The backward needs the K/V, o and lse of a LAGA_OPERANDS_SPLIT forward.
  */
@@ -103,8 +110,8 @@ typedef struct {
  */
 
 /* Bytes per logical element of k_nope / v for these dims, all planes counted:
- * 2 (one fp16 plane) or 4 (two fp16 planes, or one float32 plane).  Returns 0
- * when the dims are invalid or unsupported. */
+ * 2 (fp16), 3 (fp16 + e4m3 low plane) or 4 (float32).  Returns 0 when the
+ * dims are invalid or unsupported. */
 size_t laga_kv_elem_bytes(const laga_dims* dims);
 
 /*

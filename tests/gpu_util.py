@@ -35,9 +35,9 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def kv_host(t: torch.Tensor) -> np.ndarray:
-    """Value of a k_nope / v buffer ([planes, B, S, h, d]) in fp64."""
-    return t.detach().float().cpu().numpy().astype(np.float64).sum(0)
+def kv_host(path, t: torch.Tensor, width: int) -> np.ndarray:
+    """Value of a k_nope / v buffer (the storage laga.h documents) in fp64."""
+    return path.kv_value(t, width).numpy()
 
 
 def err(got: np.ndarray, ref: np.ndarray) -> tuple[float, float]:

@@ -52,10 +52,17 @@ def test_status_strings(lib):
         assert lib.laga_status_string(s).decode().startswith(_lib.STATUS[s])
 
 
+def test_kv_lo_shift_matches_header():
+    import re
+    text = open(_lib.HEADER).read()
+    m = re.search(r"#define\s+LAGA_KV_LO_SHIFT\s+(\d+)", text)
+    assert m and int(m.group(1)) == _lib.LAGA_KV_LO_SHIFT
+
+
 def test_kv_elem_bytes():
     assert _lib.kv_elem_bytes(tiny()) == 4
     assert _lib.kv_elem_bytes(v3(precision=_lib.LAGA_OPERANDS_FP16)) == 2
-    assert _lib.kv_elem_bytes(v3(precision=_lib.LAGA_OPERANDS_SPLIT)) == 4
+    assert _lib.kv_elem_bytes(v3(precision=_lib.LAGA_OPERANDS_SPLIT)) == 3
     assert _lib.kv_elem_bytes(v3(d_kv=256)) == 0
 
 

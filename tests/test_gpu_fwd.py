@@ -24,6 +24,22 @@ def _dims(B, S, n_h, sp_size, sp_rank, dtype):
                    d_rope=64, d_v=128, dtype=li.BF16)
 
 
+# Split K/V storage (fp16 + e4m3 low plane) holds the up-projection to ~2^-15
+# relative: |x| stays below ~8 on these inputs, so the stored value is within
+# 2^-12 * 2^-4 * 8 = 2^-13 of the exact one plus the fp32 GEMM's error.
+# Single fp16 storage would miss this bound (its error reaches 2^-9 at |x| = 4).
+SPLIT_KV_MAX = 2.0 ** -12
+
+
+def check_kv(path, name, buf, ref, d, precision):
+    width = d.d_nope if name == "k_nope" else d.d_v
+    got = kv_host(path, buf, width)
+    check(name, got, ref, d.dtype)
+    if d.dtype == li.BF16 and precision == SPLIT:
+        mx = float(np.abs(got - ref).max())
+        assert mx <= SPLIT_KV_MAX, f"{name}: split storage max-abs {mx:.3e} > {SPLIT_KV_MAX:.3e}"
+
+
 def _full_forward_check(d: li.Dims, precision: int, seed: int = 0):
     announce(f"forward full compare dims={d} precision={precision} seed={seed}")
     inp = li.make_inputs(d, seed)
@@ -39,8 +55,8 @@ def _full_forward_check(d: li.Dims, precision: int, seed: int = 0):
                          sp_size=d.sp_size, sp_rank=d.sp_rank, d_nope=d.d_nope, eps=d.eps)
     check("L", host(out["latent_n"]), ref["L"], d.dtype)
     check("rstd", host(out["rstd"]), ref["rstd"], li.F32 if d.dtype == li.F32 else d.dtype)
-    check("k_nope", kv_host(out["k_nope"]), ref["k_nope"], d.dtype)
-    check("v", kv_host(out["v"]), ref["v"], d.dtype)
+    check_kv(path, "k_nope", out["k_nope"], ref["k_nope"], d, precision)
+    check_kv(path, "v", out["v"], ref["v"], d, precision)
     check("o", host(out["o"]), ref["O"], d.dtype)
     check("lse", host(out["lse"]), ref["lse"], d.dtype)
     return out
@@ -82,8 +98,8 @@ def test_full_size_workloads(name, precision):
     check("rstd", host(out["rstd"]), rstd, d.dtype)
     kn, vv = oracle.kv_up(L, v["w_kv_b"], heads, d.d_nope)
     del L
-    check("k_nope", kv_host(out["k_nope"]), kn, d.dtype)
-    check("v", kv_host(out["v"]), vv, d.dtype)
+    check_kv(path, "k_nope", out["k_nope"], kn, d, precision)
+    check_kv(path, "v", out["v"], vv, d, precision)
     rows = sample_rows(d.S)
     O, lse = oracle.attention_fwd_rows(v["q"], kn, v["k_pe"], vv, rows)
     check("o[rows]", host(out["o"])[:, rows], O, d.dtype)
