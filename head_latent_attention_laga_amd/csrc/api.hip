@@ -49,7 +49,7 @@ laga_status from_hip(hipError_t e) {
 
 // Backward workspace regions, each 256-byte aligned, in float32 elements.
 struct BwdLayout {
-  size_t delta, cvt, dkv, dkpe, dL, lp, dw, dg, total;  // byte offsets, total bytes
+  size_t delta, cvt, lo8, dkv, dkpe, dL, lp, dw, dg, total;  // byte offsets, total bytes
 };
 
 size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
@@ -65,6 +65,8 @@ BwdLayout bwd_layout(const Shape& s) {
   L.delta = take(static_cast<size_t>(s.B) * s.h * s.S);
   // fp16 copies of q, dO and k_pe (bfloat16 inputs only), in float units.
   L.cvt = take(s.bf16 ? (static_cast<size_t>(s.T) * (s.h * (s.d_qk() + s.d_v) + s.d_rope) + 1) / 2 : 0);
+  // e4m3 rows of q_nope and dO and their per-row scale bytes (split operands).
+  L.lo8 = take(s.split ? (static_cast<size_t>(s.T) * s.h * (s.d_nope + s.d_v) + 3) / 4 + 2 * s.T * s.h : 0);
   L.dkv = take(static_cast<size_t>(s.T) * s.h * s.C());
   L.dkpe = take(static_cast<size_t>(s.h) * s.T * s.d_rope);
   L.dL = take(static_cast<size_t>(s.T) * s.d_kv);
@@ -160,18 +162,24 @@ laga_status laga_attn_bwd_traced(const laga_dims* dims, const void* q, const voi
   hipError_t e;
   if ((e = mark(0)) != hipSuccess) return from_hip(e);
   // bfloat16 inputs reach the attention kernels as exact fp16 copies.
+  laga::BwdCopies cp;
   uint16_t* q16 = reinterpret_cast<uint16_t*>(ws + L.cvt);
   uint16_t* do16 = q16 + static_cast<size_t>(s.T) * s.h * s.d_qk();
-  uint16_t* kpe16 = do16 + static_cast<size_t>(s.T) * s.h * s.d_v;
-  if ((e = laga::launch_bwd_prep(s, o, q, d_o, k_pe, delta, q16, do16, kpe16, hs)) != hipSuccess)
-    return from_hip(e);
+  cp.q16 = q16;
+  cp.do16 = do16;
+  cp.kpe16 = do16 + static_cast<size_t>(s.T) * s.h * s.d_v;
+  cp.q8 = ws + L.lo8;
+  cp.do8 = ws + L.lo8 + static_cast<size_t>(s.T) * s.h * s.d_nope;
+  cp.qsc = reinterpret_cast<int*>(ws + L.lo8 + static_cast<size_t>(s.T) * s.h * (s.d_nope + s.d_v));
+  cp.osc = cp.qsc + s.T * s.h;
+  if ((e = laga::launch_bwd_prep(s, o, q, d_o, k_pe, delta, cp, hs)) != hipSuccess) return from_hip(e);
   if (s.bf16) {
-    q = q16;
-    d_o = do16;
-    k_pe = kpe16;
+    q = cp.q16;
+    d_o = cp.do16;
+    k_pe = cp.kpe16;
   }
   if ((e = mark(1)) != hipSuccess) return from_hip(e);
-  if ((e = laga::launch_attn_bwd_dkdv(s, q, k_nope, k_pe, v, lse, delta, d_o, dkv, dkpe, hs)) != hipSuccess)
+  if ((e = laga::launch_attn_bwd_dkdv(s, q, k_nope, k_pe, v, lse, delta, d_o, cp, dkv, dkpe, hs)) != hipSuccess)
     return from_hip(e);
   if ((e = mark(2)) != hipSuccess) return from_hip(e);
   if ((e = laga::launch_attn_bwd_dq(s, q, k_nope, k_pe, v, lse, delta, d_o, dq, hs)) != hipSuccess)

@@ -28,8 +28,11 @@
 // order (deterministic, no atomics).
 //
 // Precision (LAGA_OPERANDS_SPLIT): the products that feed dK, dV and hence
-// dW_kv_b, dLatent and dgamma use K, V, P and dS as fp16 hi + lo pairs (q and
-// dO are exact in fp16); dq uses the hi parts of K and V and single fp16 dS.
+// dW_kv_b, dLatent and dgamma use K, V, P and dS as hi + lo pairs (q and dO
+// are exact in fp16): S and dP add the low planes of K and V as e4m3 products
+// against e4m3 copies of q_nope and dO, each query row scaled by its own power
+// of two (the row's E8M0 byte is the A operand's scale), and dK, dV take P and
+// dS as fp16 hi + lo.  dq uses the hi parts of K and V and single fp16 dS.
 // The float32 instantiation uses fp32 MFMAs.
 #include "attn_bwd_common.hpp"
 
@@ -48,13 +51,19 @@ struct Dkdv {
   // One q tile and one dO tile per block, read both as rows and transposed.
   static constexpr int LQR = DQK + TilePad<M>::both, LOR = DV + TilePad<M>::both;
   static constexpr int QR_B = BQ * LQR * sizeof(E), OR_B = BQ * LOR * sizeof(E);
-  static constexpr int BUF_BYTES = QR_B + OR_B + 2 * BQ * 4;
-  // The lo planes of the workgroup's K and V (split operands) stay in LDS for
-  // the whole kernel; the hi parts live in registers.
-  static constexpr int LLO = (DN > DV ? DN : DV) + TilePad<M>::row;
-  static constexpr int LO_B = NS == 2 ? BK * LLO * sizeof(E) : 0;
-  static constexpr int LDS_BYTES = 2 * BUF_BYTES + 2 * LO_B;
+  // Split operands: the low terms S_lo = q8 K_lo^T and dP_lo = dO8 V_lo^T run
+  // as e4m3 products; e4m3 q_nope / dO rows (16-byte row reads, 16-byte pad)
+  // and their per-query E8M0 scales are staged with each block.
+  static constexpr bool LO8 = NS == 2;
+  static constexpr int P8 = 16;  // row padding (bytes) of the e4m3 tiles
+  static constexpr int Q8_B = LO8 ? BQ * (DN + P8) : 0, O8_B = LO8 ? BQ * (DV + P8) : 0;
+  static constexpr int OFF_Q8 = QR_B + OR_B, OFF_O8 = OFF_Q8 + Q8_B, OFF_ST = OFF_O8 + O8_B;
+  static constexpr int BUF_BYTES = OFF_ST + (LO8 ? 4 : 2) * BQ * 4;  // lse, delta [, q / dO scales]
+  static constexpr int LDS_BYTES = 2 * BUF_BYTES;
   static constexpr int KS_QK = DQK / M::K, KS_N = DN / M::K, KS_V = DV / M::K;
+  static constexpr int KS8_N = DN / 64, KS8_V = DV / 64;  // e4m3 atoms (K = 64)
+  static_assert(!LO8 || (sizeof(E) == 2 && DN % 64 == 0 && DV % 64 == 0 && BQ * DN / 16 == kThreads &&
+                         BQ * DV / 16 == kThreads), "e4m3 staging: one 16-byte chunk per thread");
   static constexpr int STEPS = BQ / M::K;
   static constexpr int NKT = (DQK + 31) / 32, NVT = DV / 32;
   // Staging: 16-byte chunks of the input rows.
@@ -63,13 +72,17 @@ struct Dkdv {
   static constexpr int IQ = (QCH + kThreads - 1) / kThreads, IO = (OCH + kThreads - 1) / kThreads;
   static_assert(DQK % IPC == 0 && DV % IPC == 0, "rows of whole chunks");
 
-  struct Regs { u32x4 q[IQ]; u32x4 o[IO]; float lse2, dlt; };  // lse2: natural-log lse until stored
+  struct Regs {
+    u32x4 q[IQ]; u32x4 o[IO]; float lse2, dlt;  // lse2: natural-log lse until stored
+    u32x4 q8, o8; int qs, os;                    // split operands only
+  };
 
   // Stationary operands of one wavefront: its 32 keys' K (nope hi plane, rope)
-  // and V (hi plane) fragments in registers; the lo planes are read from LDS.
+  // and V (hi plane) fragments, and for split operands the e4m3 low planes
+  // of K_nope and V (B operands of the e4m3 products), all in registers.
   struct Stat {
     F kf[KS_N], kr[KS_QK - KS_N], vf[KS_V];
-    const E* klo_row; const E* vlo_row;
+    i32x8 k8[LO8 ? KS8_N : 1], v8[LO8 ? KS8_V : 1];
   };
   struct Acc { f32x16 dk[NKT], dvt[NVT]; };
 
@@ -98,12 +111,21 @@ struct Dkdv {
     const int64_t si0 = (static_cast<int64_t>(b) * a.h + head) * a.S + q0;
     R.lse2 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.lse + si0, nq * 4), t * 4, 0, 0));
     R.dlt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.delta + si0, nq * 4), t * 4, 0, 0));
+    if constexpr (LO8) {
+      const int r = tid / (DN / 16), j = tid % (DN / 16);
+      R.q8 = __builtin_amdgcn_raw_buffer_load_b128(rsrc(a.q8 + row0 * DN, nq * a.h * DN), r * a.h * DN + j * 16, 0, 0);
+      const int ro8 = tid / (DV / 16), jo8 = tid % (DV / 16);
+      R.o8 = __builtin_amdgcn_raw_buffer_load_b128(rsrc(a.do8 + row0 * DV, nq * a.h * DV), ro8 * a.h * DV + jo8 * 16,
+                                                   0, 0);
+      R.qs = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.qsc + si0, nq * 4), t * 4, 0, 0));
+      R.os = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.osc + si0, nq * 4), t * 4, 0, 0));
+    }
   }
 
   __device__ static void store(const Regs& R, char* buf) {
     E* Qr = reinterpret_cast<E*>(buf);
     E* Or = reinterpret_cast<E*>(buf + QR_B);
-    float* st = reinterpret_cast<float*>(buf + QR_B + OR_B);
+    float* st = reinterpret_cast<float*>(buf + OFF_ST);
     const int tid = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < IQ; ++i) {
@@ -133,6 +155,23 @@ struct Dkdv {
       st[tid] = R.lse2 * kLog2e;
       st[BQ + tid] = R.dlt;
     }
+    if constexpr (LO8) {
+      const int r = tid / (DN / 16), j = tid % (DN / 16);
+      *reinterpret_cast<u32x4*>(buf + OFF_Q8 + r * (DN + P8) + j * 16) = R.q8;
+      const int ro8 = tid / (DV / 16), jo8 = tid % (DV / 16);
+      *reinterpret_cast<u32x4*>(buf + OFF_O8 + ro8 * (DV + P8) + jo8 * 16) = R.o8;
+      if (tid < BQ) {
+        reinterpret_cast<int*>(st)[2 * BQ + tid] = R.qs;
+        reinterpret_cast<int*>(st)[3 * BQ + tid] = R.os;
+      }
+    }
+  }
+
+  // 32 e4m3 bytes of an LDS row (the A or B operand of one e4m3 atom).
+  __device__ static i32x8 frag8(const char* p) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(p), y = *reinterpret_cast<const u32x4*>(p + 16);
+    return i32x8{static_cast<int>(x[0]), static_cast<int>(x[1]), static_cast<int>(x[2]), static_cast<int>(x[3]),
+                 static_cast<int>(y[0]), static_cast<int>(y[1]), static_cast<int>(y[2]), static_cast<int>(y[3])};
   }
 
   // A operand of a product whose k index runs over the queries of the block:
@@ -173,7 +212,7 @@ struct Dkdv {
     if (MASK && q0 + BQ - 1 < wk0) return;  // every query of the block precedes these keys
     const E* Qr = reinterpret_cast<const E*>(buf);
     const E* Or = reinterpret_cast<const E*>(buf + QR_B);
-    const float* st = reinterpret_cast<const float*>(buf + QR_B + OR_B);
+    const float* st = reinterpret_cast<const float*>(buf + OFF_ST);
 
     // S[q, key], dP[q, key]: rows = queries 8g + 4hf + i, column = key.  The
     // chains run one after the other so that the vector work on each result
@@ -185,18 +224,22 @@ struct Dkdv {
 #pragma unroll
     for (int r = 0; r < 16; ++r) { sc[r] = 0.f; dp[r] = 0.f; }
 #pragma unroll
-    for (int s = 0; s < KS_N; ++s) {
-      const F qa = lds_frag<M>(qrow + s * M::K);
-      sc = M::mma(qa, K.kf[s], sc);
-      if constexpr (NS == 2) sc = M::mma(qa, lds_frag<M>(K.klo_row + s * M::K), sc);
-    }
+    for (int s = 0; s < KS_N; ++s) sc = M::mma(lds_frag<M>(qrow + s * M::K), K.kf[s], sc);
 #pragma unroll
     for (int s = KS_N; s < KS_QK; ++s) sc = M::mma(lds_frag<M>(qrow + s * M::K), K.kr[s - KS_N], sc);
+    if constexpr (LO8) {  // + (q8 * 2^-s_q) . (K_lo * 2^-kLoShift)^T, per-query scale in the A operand
+      const int qs = reinterpret_cast<const int*>(st)[2 * BQ + col];
+      const char* q8row = buf + OFF_Q8 + col * (DN + P8) + 32 * hf;
 #pragma unroll
-    for (int s = 0; s < KS_V; ++s) {
-      const F oa = lds_frag<M>(orow + s * M::K);
-      dp = M::mma(oa, K.vf[s], dp);
-      if constexpr (NS == 2) dp = M::mma(oa, lds_frag<M>(K.vlo_row + s * M::K), dp);
+      for (int s = 0; s < KS8_N; ++s) sc = mma_e4m3(frag8(q8row + 64 * s), K.k8[s], sc, qs, 127 - kLoShift);
+    }
+#pragma unroll
+    for (int s = 0; s < KS_V; ++s) dp = M::mma(lds_frag<M>(orow + s * M::K), K.vf[s], dp);
+    if constexpr (LO8) {
+      const int os = reinterpret_cast<const int*>(st)[3 * BQ + col];
+      const char* o8row = buf + OFF_O8 + col * (DV + P8) + 32 * hf;
+#pragma unroll
+      for (int s = 0; s < KS8_V; ++s) dp = mma_e4m3(frag8(o8row + 64 * s), K.v8[s], dp, os, 127 - kLoShift);
     }
 
     // P = exp(s - lse) per query row of the block, split into NS terms
@@ -301,47 +344,18 @@ struct Dkdv {
     for (int s = 0; s < KS_V; ++s) K.vf[s] = row_frag(vg + s * M::K + hf * M::KPL);
 #pragma unroll
     for (int s = 0; s < KS_QK - KS_N; ++s) K.kr[s] = row_frag(kp + s * M::K + hf * M::KPL);
-    E* klo = reinterpret_cast<E*>(lds + 2 * BUF_BYTES);
-    E* vlo = reinterpret_cast<E*>(lds + 2 * BUF_BYTES + LO_B);
-    if constexpr (NS == 2) {
-      // Low planes of this workgroup's 128 keys (e4m3 bytes scaled by
-      // 2^kLoShift after the fp16 planes) -> fp16 LDS rows, exactly, published
-      // by the first barrier of the query loop.  Keys past the sequence read as zero.
-      static_assert(sizeof(E) == 2, "low planes decode to fp16");
-      const int nkw = static_cast<int>(a.S - k0 < BK ? a.S - k0 : BK);
-      const int krb = a.h * DN, vrb = a.h * DV;
-      const char* kbase = static_cast<const char*>(a.k_nope) + a.plane_k * sizeof(E) + ((b * a.S + k0) * a.h + head) * DN;
-      const char* vbase = static_cast<const char*>(a.v) + a.plane_v * sizeof(E) + ((b * a.S + k0) * a.h + head) * DV;
-      const auto rk = rsrc(kbase, nkw * krb), rv = rsrc(vbase, nkw * vrb);
-      constexpr float inv = 1.0f / static_cast<float>(1 << kLoShift);
-      auto decode = [&](u32x4 w, E* dst) {
-        E e[16];
+    if constexpr (LO8) {
+      // e4m3 low planes (after the fp16 planes) of this lane's key: bytes
+      // 64 s + 32 hf + [0, 32) of its K_nope and V rows.
+      const uint8_t* k8 = static_cast<const uint8_t*>(a.k_nope) + a.plane_k * sizeof(E) +
+                          ((b * a.S + kc) * a.h + head) * DN + 32 * hf;
+      const uint8_t* v8 = static_cast<const uint8_t*>(a.v) + a.plane_v * sizeof(E) +
+                          ((b * a.S + kc) * a.h + head) * DV + 32 * hf;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const f32x2 x = unpack_e4m3x2<false>(w[d]), y = unpack_e4m3x2<true>(w[d]);
-          e[4 * d] = static_cast<E>(x[0] * inv);
-          e[4 * d + 1] = static_cast<E>(x[1] * inv);
-          e[4 * d + 2] = static_cast<E>(y[0] * inv);
-          e[4 * d + 3] = static_cast<E>(y[1] * inv);
-        }
-        *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(e);
-        *reinterpret_cast<u32x4*>(dst + 8) = *reinterpret_cast<const u32x4*>(e + 8);
-      };
+      for (int s = 0; s < KS8_N; ++s) K.k8[s] = *reinterpret_cast<const i32x8*>(k8 + 64 * s);
 #pragma unroll
-      for (int i = 0; i < BK * DN / 16 / kThreads; ++i) {
-        const int c = i * kThreads + static_cast<int>(threadIdx.x);
-        const int r = c / (DN / 16), j = c % (DN / 16);
-        decode(__builtin_amdgcn_raw_buffer_load_b128(rk, r * krb + j * 16, 0, 0), klo + r * LLO + j * 16);
-      }
-#pragma unroll
-      for (int i = 0; i < BK * DV / 16 / kThreads; ++i) {
-        const int c = i * kThreads + static_cast<int>(threadIdx.x);
-        const int r = c / (DV / 16), j = c % (DV / 16);
-        decode(__builtin_amdgcn_raw_buffer_load_b128(rv, r * vrb + j * 16, 0, 0), vlo + r * LLO + j * 16);
-      }
+      for (int s = 0; s < KS8_V; ++s) K.v8[s] = *reinterpret_cast<const i32x8*>(v8 + 64 * s);
     }
-    K.klo_row = klo + (wv * 32 + col) * LLO + hf * M::KPL;  // this lane's key
-    K.vlo_row = vlo + (wv * 32 + col) * LLO + hf * M::KPL;
 
     Acc acc;
 #pragma unroll
@@ -448,14 +462,17 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(const float* __restrict__ 
 // with plain 16-byte copies.  One wavefront per (b, t, i) row: the first DV/8
 // lanes take 8 elements of dO and o each, the next DQK/8 lanes 8 elements of
 // q, and on the i == 0 row the next DR/8 lanes 8 elements of k_pe.
-template <int DQK, int DV, int DR>
+template <int DN, int DR, int DV>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__ o, const bf16_t* __restrict__ q,
                                                        const bf16_t* __restrict__ d_o,
                                                        const bf16_t* __restrict__ k_pe, float* __restrict__ delta,
                                                        half_t* __restrict__ q16, half_t* __restrict__ do16,
-                                                       half_t* __restrict__ kpe16, int64_t rows, int h, int64_t S) {
-  constexpr int NO = DV / 8, NQ = DQK / 8, NR = DR / 8;
+                                                       half_t* __restrict__ kpe16, uint8_t* __restrict__ q8,
+                                                       uint8_t* __restrict__ do8, int* __restrict__ qsc,
+                                                       int* __restrict__ osc, int64_t rows, int h, int64_t S) {
+  constexpr int DQK = DN + DR, NO = DV / 8, NQ = DQK / 8, NR = DR / 8;
   static_assert(NO + NQ + NR <= kWave && DV % 8 == 0 && DQK % 8 == 0 && DR % 8 == 0, "one chunk per lane");
+  static_assert(NO == 16 && DN / 8 == 16, "dO and q_nope fill one 16-lane group each");
   const int lane = threadIdx.x % kWave;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;  // (b, t, i)
   if (row >= rows) return;
@@ -471,7 +488,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
     return r;
   };
   float acc = 0.f;
-  float f[8];
+  float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (lane < NO) {
     const int64_t at = row * DV + lane * 8;
     *reinterpret_cast<half8*>(do16 + at) = to_half8(*reinterpret_cast<const u16x8*>(d_o + at), f);
@@ -485,11 +502,27 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
     const int64_t at = bt * DR + (lane - NO - NQ) * 8;
     *reinterpret_cast<half8*>(kpe16 + at) = to_half8(*reinterpret_cast<const u16x8*>(k_pe + at), f);
   }
-  acc = wave_sum(acc);
-  if (lane == 0) {
-    const int64_t b = bt / S, t = bt % S;
-    delta[(b * h + i) * S + t] = acc;
+  // e4m3 copies of the dO row (lanes 0..15) and the q_nope row (lanes 16..31),
+  // each scaled by the power of two 2^s that brings its largest magnitude into
+  // [128, 256); the E8M0 byte 127 - s undoes it inside the matrix-core product.
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[j]));
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, kWave));
+  const int s = e4m3_row_shift(amax);
+  const float sc = __uint_as_float(static_cast<uint32_t>(127 + s) << 23);
+  const int64_t b = bt / S, t = bt % S;
+  const int64_t si = (b * h + i) * S + t;
+  if (lane < NO + DN / 8) {
+    uint8_t* dst = lane < NO ? do8 + row * DV + lane * 8 : q8 + row * DN + (lane - NO) * 8;
+    *reinterpret_cast<uint2*>(dst) = make_uint2(pack_e4m3x4(f[0] * sc, f[1] * sc, f[2] * sc, f[3] * sc),
+                                                pack_e4m3x4(f[4] * sc, f[5] * sc, f[6] * sc, f[7] * sc));
+    if (lane == 0) osc[si] = 127 - s;
+    if (lane == NO) qsc[si] = 127 - s;
   }
+  acc = wave_sum(acc);
+  if (lane == 0) delta[si] = acc;
 }
 
 // out[t, c] = sum_i part[i, t, c] in increasing i (deterministic head sum).
@@ -505,14 +538,15 @@ __global__ __launch_bounds__(256) void head_sum_kernel(const float* __restrict__
 }  // namespace
 
 hipError_t launch_bwd_prep(const Shape& s, const float* o, const void* q, const void* d_o, const void* k_pe,
-                           float* delta, void* q16, void* do16, void* kpe16, hipStream_t st) {
+                           float* delta, const BwdCopies& c, hipStream_t st) {
   const int64_t rows = s.T * s.h;
   const unsigned blocks = static_cast<unsigned>((rows + 3) / 4);
   if (s.bf16 && s.d_nope == 128 && s.d_rope == 64 && s.d_v == 128)
-    hipLaunchKernelGGL((bwd_prep_kernel<192, 128, 64>), dim3(blocks), dim3(256), 0, st, o,
+    hipLaunchKernelGGL((bwd_prep_kernel<128, 64, 128>), dim3(blocks), dim3(256), 0, st, o,
                        static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(d_o),
-                       static_cast<const bf16_t*>(k_pe), delta, static_cast<half_t*>(q16),
-                       static_cast<half_t*>(do16), static_cast<half_t*>(kpe16), rows, s.h, s.S);
+                       static_cast<const bf16_t*>(k_pe), delta, static_cast<half_t*>(c.q16),
+                       static_cast<half_t*>(c.do16), static_cast<half_t*>(c.kpe16), static_cast<uint8_t*>(c.q8),
+                       static_cast<uint8_t*>(c.do8), c.qsc, c.osc, rows, s.h, s.S);
   else if (!s.bf16 && s.d_v == 32)
     hipLaunchKernelGGL((bwd_dot_kernel<float, 32>), dim3(blocks), dim3(256), 0, st, o,
                        static_cast<const float*>(d_o), delta, rows, s.h, s.S);
@@ -529,9 +563,13 @@ hipError_t launch_head_sum(const Shape& s, const float* part, float* out, hipStr
 }
 
 hipError_t launch_attn_bwd_dkdv(const Shape& s, const void* q, const void* kn, const void* kp, const void* v,
-                                const float* lse, const float* delta, const void* d_o, void* dkv,
-                                float* dk_pe_part, hipStream_t st) {
+                                const float* lse, const float* delta, const void* d_o, const BwdCopies& c,
+                                void* dkv, float* dk_pe_part, hipStream_t st) {
   BwdArgs a = make_args(s, q, kn, kp, v, lse, delta, d_o);
+  a.q8 = static_cast<const uint8_t*>(c.q8);
+  a.do8 = static_cast<const uint8_t*>(c.do8);
+  a.qsc = c.qsc;
+  a.osc = c.osc;
   a.dkv = dkv;
   a.dk_pe_part = dk_pe_part;
   const unsigned grid = static_cast<unsigned>(((s.S + 127) / 128) * s.B * s.h);

@@ -20,6 +20,8 @@ struct BwdArgs {
   const void* q; const void* k_nope; const void* k_pe; const void* v;
   const float* lse; const float* delta; const void* d_o;
   void* dkv; float* dk_pe_part; float* dq;
+  // e4m3 q_nope / dO rows and their E8M0 row scales (split operands, dK/dV).
+  const uint8_t* q8; const uint8_t* do8; const int* qsc; const int* osc;
   int64_t S, plane_k, plane_v, plane_dkv; int B, h; float scale_log2, scale;
 };
 
@@ -58,6 +60,7 @@ inline BwdArgs make_args(const Shape& s, const void* q, const void* kn, const vo
   BwdArgs a;
   a.q = q; a.k_nope = kn; a.k_pe = kp; a.v = v; a.lse = lse; a.delta = delta; a.d_o = d_o;
   a.dkv = nullptr; a.dk_pe_part = nullptr; a.dq = nullptr;
+  a.q8 = nullptr; a.do8 = nullptr; a.qsc = nullptr; a.osc = nullptr;
   a.S = s.S; a.B = static_cast<int>(s.B); a.h = s.h;
   a.plane_k = s.T * s.h * s.d_nope;
   a.plane_v = s.T * s.h * s.d_v;

@@ -115,6 +115,16 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
   return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
 }
 
+// Power-of-two shift s for a row of e4m3 values with largest magnitude m:
+// m * 2^s lies in [128, 256) (below e4m3's 448 with room for rounding); 0 for
+// an all-zero row.  Clamped so that 127 - s stays a valid E8M0 scale byte.
+__device__ __forceinline__ int e4m3_row_shift(float m) {
+  const int e = static_cast<int>((__float_as_uint(m) >> 23) & 0xff);  // m = 1.f * 2^(e - 127)
+  if (e == 0) return 0;
+  const int s = 134 - e;  // 2^(e - 127) * 2^s = 2^7
+  return s < -120 ? -120 : (s > 120 ? 120 : s);
+}
+
 // Bytes 2*HI .. 2*HI+1 of w (e4m3) -> two floats.
 template <bool HI>
 __device__ __forceinline__ f32x2 unpack_e4m3x2(uint32_t w) {

@@ -27,14 +27,21 @@ hipError_t launch_attn_fwd(const Shape& s, const void* q, const void* k_nope, co
                            const void* v, float* o, float* lse, hipStream_t st);
 
 // Backward pieces.  Workspace carving lives in the API layer.
-// delta = rowsum(dO * o); for bfloat16 inputs also fp16 copies of q, dO and
-// k_pe (q16 [T,h,d_qk], do16 [T,h,d_v], kpe16 [T,d_rope]), which the two
-// attention-backward launchers then take in place of the inputs.
+// Copies of the bfloat16 inputs that the backward kernels read: exact fp16
+// q16 [T,h,d_qk], do16 [T,h,d_v], kpe16 [T,d_rope] (taken in place of the
+// inputs), and for split operands e4m3 rows q8 = e4m3(q_nope * 2^s)
+// [T,h,d_nope], do8 = e4m3(dO * 2^s) [T,h,d_v] with one shift per row, whose
+// E8M0 bytes 127 - s are qsc / osc [B,h,S] (int32).
+struct BwdCopies {
+  void* q16; void* do16; void* kpe16;
+  void* q8; void* do8; int* qsc; int* osc;
+};
+// delta = rowsum(dO * o) and, for bfloat16 inputs, the copies above.
 hipError_t launch_bwd_prep(const Shape& s, const float* o, const void* q, const void* d_o, const void* k_pe,
-                           float* delta, void* q16, void* do16, void* kpe16, hipStream_t st);
+                           float* delta, const BwdCopies& c, hipStream_t st);
 hipError_t launch_attn_bwd_dkdv(const Shape& s, const void* q, const void* k_nope,
                                 const void* k_pe, const void* v, const float* lse,
-                                const float* delta, const void* d_o, void* dkv,
+                                const float* delta, const void* d_o, const BwdCopies& c, void* dkv,
                                 float* dk_pe_part, hipStream_t st);
 hipError_t launch_attn_bwd_dq(const Shape& s, const void* q, const void* k_nope, const void* k_pe,
                               const void* v, const float* lse, const float* delta,
