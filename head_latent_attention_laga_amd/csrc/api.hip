@@ -49,7 +49,7 @@ laga_status from_hip(hipError_t e) {
 
 // Backward workspace regions, each 256-byte aligned, in float32 elements.
 struct BwdLayout {
-  size_t delta, cvt, lo8, dkv, dkpe, dL, lp, dw, dg, total;  // byte offsets, total bytes
+  size_t delta, cvt, lo8, dos, dkv, dkpe, dL, lp, dw, dg, total;  // byte offsets, total bytes
 };
 
 size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
@@ -67,6 +67,8 @@ BwdLayout bwd_layout(const Shape& s) {
   L.cvt = take(s.bf16 ? (static_cast<size_t>(s.T) * (s.h * (s.d_qk() + s.d_v) + s.d_rope) + 1) / 2 : 0);
   // e4m3 rows of q_nope and dO and their per-row scale bytes (split operands).
   L.lo8 = take(s.split ? (static_cast<size_t>(s.T) * s.h * (s.d_nope + s.d_v) + 3) / 4 + 2 * s.T * s.h : 0);
+  // Maxima of |dO| per delta workgroup (4 rows) and the dO scale shift (bfloat16 inputs).
+  L.dos = take(s.bf16 ? (static_cast<size_t>(s.T) * s.h + 3) / 4 + 64 : 0);
   L.dkv = take(static_cast<size_t>(s.T) * s.h * s.C());
   L.dkpe = take(static_cast<size_t>(s.h) * s.T * s.d_rope);
   L.dL = take(static_cast<size_t>(s.T) * s.d_kv);
@@ -172,6 +174,8 @@ laga_status laga_attn_bwd_traced(const laga_dims* dims, const void* q, const voi
   cp.do8 = ws + L.lo8 + static_cast<size_t>(s.T) * s.h * s.d_nope;
   cp.qsc = reinterpret_cast<int*>(ws + L.lo8 + static_cast<size_t>(s.T) * s.h * (s.d_nope + s.d_v));
   cp.osc = cp.qsc + s.T * s.h;
+  cp.do_row_max = s.bf16 ? reinterpret_cast<float*>(ws + L.dos) : nullptr;
+  cp.do_shift = s.bf16 ? reinterpret_cast<int*>(ws + L.dos) + (s.T * s.h + 3) / 4 : nullptr;
   if ((e = laga::launch_bwd_prep(s, o, q, d_o, k_pe, delta, cp, hs)) != hipSuccess) return from_hip(e);
   if (s.bf16) {
     q = cp.q16;
@@ -182,7 +186,7 @@ laga_status laga_attn_bwd_traced(const laga_dims* dims, const void* q, const voi
   if ((e = laga::launch_attn_bwd_dkdv(s, q, k_nope, k_pe, v, lse, delta, d_o, cp, dkv, dkpe, hs)) != hipSuccess)
     return from_hip(e);
   if ((e = mark(2)) != hipSuccess) return from_hip(e);
-  if ((e = laga::launch_attn_bwd_dq(s, q, k_nope, k_pe, v, lse, delta, d_o, dq, hs)) != hipSuccess)
+  if ((e = laga::launch_attn_bwd_dq(s, q, k_nope, k_pe, v, lse, delta, d_o, cp.do_shift, dq, hs)) != hipSuccess)
     return from_hip(e);
   if ((e = mark(3)) != hipSuccess) return from_hip(e);
   if ((e = laga::launch_head_sum(s, dkpe, d_k_pe, hs)) != hipSuccess) return from_hip(e);

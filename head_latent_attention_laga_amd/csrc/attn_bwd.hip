@@ -75,6 +75,7 @@ struct Dkdv {
   struct Regs {
     u32x4 q[IQ]; u32x4 o[IO]; float lse2, dlt;  // lse2: natural-log lse until stored
     u32x4 q8, o8; int qs, os;                    // split operands only
+    float dsc; int dsh;                          // 2^g and g of the dO scale (set once)
   };
 
   // Stationary operands of one wavefront: its 32 keys' K (nope hi plane, rope)
@@ -153,7 +154,7 @@ struct Dkdv {
     }
     if (tid < BQ) {
       st[tid] = R.lse2 * kLog2e;
-      st[BQ + tid] = R.dlt;
+      st[BQ + tid] = R.dlt * R.dsc;  // delta in the units of the scaled dO
     }
     if constexpr (LO8) {
       const int r = tid / (DN / 16), j = tid % (DN / 16);
@@ -162,7 +163,9 @@ struct Dkdv {
       *reinterpret_cast<u32x4*>(buf + OFF_O8 + ro8 * (DV + P8) + jo8 * 16) = R.o8;
       if (tid < BQ) {
         reinterpret_cast<int*>(st)[2 * BQ + tid] = R.qs;
-        reinterpret_cast<int*>(st)[3 * BQ + tid] = R.os;
+        // dO8 * 2^-s_row feeds dP in the scaled units of the fp16 part: 2^(g - s_row).
+        const int e = R.os + R.dsh;
+        reinterpret_cast<int*>(st)[3 * BQ + tid] = e < 0 ? 0 : (e > 254 ? 254 : e);
       }
     }
   }
@@ -375,6 +378,8 @@ struct Dkdv {
     const int nfull = static_cast<int>((a.S - k0) / BQ);
     const int nmid = nfull > ndiag ? nfull : ndiag;
     Regs R;
+    R.dsh = do_shift_of(a);
+    R.dsc = pow2i(R.dsh);
     load(a, b, head, k0, R);
     int it = 0;
     for (; it < ndiag; ++it) step<true>(a, lds, it, nqb, b, head, k0, wk0, R, K, acc);
@@ -385,15 +390,16 @@ struct Dkdv {
 
     if (!kvalid) return;
     // Lane holds column `key`; accumulator r is row 8(r/4) + 4hf + r%4 of its 32-row atom.
+    // dK and dV come out in the units of the scaled dO: multiply by 2^-g.
     const int64_t orow = ((b * a.S + key) * a.h + head) * C;
+    const float vsc = pow2i(-R.dsh), ksc = a.scale * vsc;
 #pragma unroll
     for (int n = 0; n < NKT; ++n)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = n * 32 + 8 * g + 4 * hf;
         if (d >= DQK) continue;
-        f32x4 w = {dk[n][4 * g] * a.scale, dk[n][4 * g + 1] * a.scale, dk[n][4 * g + 2] * a.scale,
-                   dk[n][4 * g + 3] * a.scale};
+        f32x4 w = {dk[n][4 * g] * ksc, dk[n][4 * g + 1] * ksc, dk[n][4 * g + 2] * ksc, dk[n][4 * g + 3] * ksc};
         if (d < DN)
           store_dkv(a, orow + d, w);
         else
@@ -405,7 +411,7 @@ struct Dkdv {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = n * 32 + 8 * g + 4 * hf;
-        f32x4 w = {dvt[n][4 * g], dvt[n][4 * g + 1], dvt[n][4 * g + 2], dvt[n][4 * g + 3]};
+        f32x4 w = {dvt[n][4 * g] * vsc, dvt[n][4 * g + 1] * vsc, dvt[n][4 * g + 2] * vsc, dvt[n][4 * g + 3] * vsc};
         store_dkv(a, orow + DN + d, w);
       }
   }
@@ -466,18 +472,19 @@ template <int DN, int DR, int DV>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__ o, const bf16_t* __restrict__ q,
                                                        const bf16_t* __restrict__ d_o,
                                                        const bf16_t* __restrict__ k_pe, float* __restrict__ delta,
-                                                       half_t* __restrict__ q16, half_t* __restrict__ do16,
-                                                       half_t* __restrict__ kpe16, uint8_t* __restrict__ q8,
-                                                       uint8_t* __restrict__ do8, int* __restrict__ qsc,
-                                                       int* __restrict__ osc, int64_t rows, int h, int64_t S) {
+                                                       half_t* __restrict__ q16, half_t* __restrict__ kpe16,
+                                                       uint8_t* __restrict__ q8, uint8_t* __restrict__ do8,
+                                                       int* __restrict__ qsc, int* __restrict__ osc,
+                                                       float* __restrict__ do_max, int64_t rows, int h, int64_t S) {
   constexpr int DQK = DN + DR, NO = DV / 8, NQ = DQK / 8, NR = DR / 8;
   static_assert(NO + NQ + NR <= kWave && DV % 8 == 0 && DQK % 8 == 0 && DR % 8 == 0, "one chunk per lane");
   static_assert(NO == 16 && DN / 8 == 16, "dO and q_nope fill one 16-lane group each");
   const int lane = threadIdx.x % kWave;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;  // (b, t, i)
-  if (row >= rows) return;
-  const int64_t bt = row / h;
-  const int i = static_cast<int>(row % h);
+  // Rows past the end still reach the workgroup barrier below; they touch no memory.
+  const bool live = row < rows;
+  const int64_t bt = (live ? row : 0) / h;
+  const int i = static_cast<int>((live ? row : 0) % h);
   auto to_half8 = [](u16x8 v, float* f) {
     half8 r;
 #pragma unroll
@@ -489,9 +496,11 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
   };
   float acc = 0.f;
   float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (lane < NO) {
+  if (!live) {
+    // no memory: f stays 0
+  } else if (lane < NO) {
     const int64_t at = row * DV + lane * 8;
-    *reinterpret_cast<half8*>(do16 + at) = to_half8(*reinterpret_cast<const u16x8*>(d_o + at), f);
+    to_half8(*reinterpret_cast<const u16x8*>(d_o + at), f);  // dO's fp16 copy follows the global scale
     const f32x4 o0 = *reinterpret_cast<const f32x4*>(o + at), o1 = *reinterpret_cast<const f32x4*>(o + at + 4);
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc += f[j] * o0[j] + f[4 + j] * o1[j];
@@ -514,7 +523,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
   const float sc = __uint_as_float(static_cast<uint32_t>(127 + s) << 23);
   const int64_t b = bt / S, t = bt % S;
   const int64_t si = (b * h + i) * S + t;
-  if (lane < NO + DN / 8) {
+  if (live && lane < NO + DN / 8) {
     uint8_t* dst = lane < NO ? do8 + row * DV + lane * 8 : q8 + row * DN + (lane - NO) * 8;
     *reinterpret_cast<uint2*>(dst) = make_uint2(pack_e4m3x4(f[0] * sc, f[1] * sc, f[2] * sc, f[3] * sc),
                                                 pack_e4m3x4(f[4] * sc, f[5] * sc, f[6] * sc, f[7] * sc));
@@ -522,7 +531,50 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
     if (lane == NO) qsc[si] = 127 - s;
   }
   acc = wave_sum(acc);
-  if (lane == 0) delta[si] = acc;
+  if (live && lane == 0) delta[si] = acc;
+  // Largest |dO| of the workgroup's rows (lane 0's group holds dO), one value per workgroup.
+  __shared__ float wmax[4];
+  if (lane == 0) wmax[threadIdx.x / kWave] = amax;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int nw = static_cast<int>(rows - static_cast<int64_t>(blockIdx.x) * 4 < 4 ? rows - blockIdx.x * 4 : 4);
+    float m = wmax[0];
+    for (int w = 1; w < nw; ++w) m = fmaxf(m, wmax[w]);
+    do_max[blockIdx.x] = m;
+  }
+}
+
+// g = the shift that brings max |dO| into [8, 16) (0 for an all-zero dO),
+// from the per-workgroup maxima of the delta kernel: one workgroup (a max is
+// independent of the reduction order).
+__global__ __launch_bounds__(1024) void do_shift_kernel(const float* __restrict__ part_max, int64_t n,
+                                                        int* __restrict__ shift) {
+  __shared__ float part[1024 / kWave];
+  float m = 0.f;
+  for (int64_t i = threadIdx.x; i < n; i += 1024) m = fmaxf(m, part_max[i]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+  if (threadIdx.x % kWave == 0) part[threadIdx.x / kWave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 1024 / kWave; ++w) m = fmaxf(m, part[w]);
+    const int e = static_cast<int>((__float_as_uint(m) >> 23) & 0xff);  // m = 1.f * 2^(e - 127)
+    int g = e == 0 ? 0 : 130 - e;                                       // m * 2^g in [8, 16)
+    shift[0] = g < -100 ? -100 : (g > 100 ? 100 : g);
+  }
+}
+
+// dO's fp16 copy, scaled by 2^g (exact: a power of two).
+__global__ __launch_bounds__(256) void do_convert_kernel(const bf16_t* __restrict__ d_o, const int* __restrict__ shift,
+                                                         half_t* __restrict__ do16, int64_t n8) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const float sc = __uint_as_float(static_cast<uint32_t>(127 + shift[0]) << 23);
+  const u16x8 v = *reinterpret_cast<const u16x8*>(d_o + i * 8);
+  half8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = static_cast<half_t>(bf16_to_f32(v[j]) * sc);
+  *reinterpret_cast<half8*>(do16 + i * 8) = r;
 }
 
 // out[t, c] = sum_i part[i, t, c] in increasing i (deterministic head sum).
@@ -541,12 +593,18 @@ hipError_t launch_bwd_prep(const Shape& s, const float* o, const void* q, const 
                            float* delta, const BwdCopies& c, hipStream_t st) {
   const int64_t rows = s.T * s.h;
   const unsigned blocks = static_cast<unsigned>((rows + 3) / 4);
-  if (s.bf16 && s.d_nope == 128 && s.d_rope == 64 && s.d_v == 128)
+  if (s.bf16 && s.d_nope == 128 && s.d_rope == 64 && s.d_v == 128) {
     hipLaunchKernelGGL((bwd_prep_kernel<128, 64, 128>), dim3(blocks), dim3(256), 0, st, o,
                        static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(d_o),
                        static_cast<const bf16_t*>(k_pe), delta, static_cast<half_t*>(c.q16),
-                       static_cast<half_t*>(c.do16), static_cast<half_t*>(c.kpe16), static_cast<uint8_t*>(c.q8),
-                       static_cast<uint8_t*>(c.do8), c.qsc, c.osc, rows, s.h, s.S);
+                       static_cast<half_t*>(c.kpe16), static_cast<uint8_t*>(c.q8), static_cast<uint8_t*>(c.do8),
+                       c.qsc, c.osc, c.do_row_max, rows, s.h, s.S);
+    hipLaunchKernelGGL(do_shift_kernel, dim3(1), dim3(1024), 0, st, c.do_row_max, static_cast<int64_t>(blocks),
+                       c.do_shift);
+    const int64_t n8 = rows * s.d_v / 8;
+    hipLaunchKernelGGL(do_convert_kernel, dim3(static_cast<unsigned>((n8 + 255) / 256)), dim3(256), 0, st,
+                       static_cast<const bf16_t*>(d_o), c.do_shift, static_cast<half_t*>(c.do16), n8);
+  }
   else if (!s.bf16 && s.d_v == 32)
     hipLaunchKernelGGL((bwd_dot_kernel<float, 32>), dim3(blocks), dim3(256), 0, st, o,
                        static_cast<const float*>(d_o), delta, rows, s.h, s.S);
@@ -566,6 +624,7 @@ hipError_t launch_attn_bwd_dkdv(const Shape& s, const void* q, const void* kn, c
                                 const float* lse, const float* delta, const void* d_o, const BwdCopies& c,
                                 void* dkv, float* dk_pe_part, hipStream_t st) {
   BwdArgs a = make_args(s, q, kn, kp, v, lse, delta, d_o);
+  a.do_shift = c.do_shift;
   a.q8 = static_cast<const uint8_t*>(c.q8);
   a.do8 = static_cast<const uint8_t*>(c.do8);
   a.qsc = c.qsc;

@@ -225,6 +225,7 @@ struct Dq {
 
     // q / dO rows of the wavefront; rows past the sequence read as zero, which
     // with zero statistics makes their dS zero.
+    const int g = do_shift_of(a);
     Stat Q;
     {
       const int nq = static_cast<int>(a.S - qw < 32 ? (a.S - qw > 0 ? a.S - qw : 0) : 32);
@@ -240,7 +241,8 @@ struct Dq {
         Q.of[s] = frag_from(ro, col * orb + (s * M::K + hf * M::KPL) * static_cast<int>(sizeof(InT)));
       const int64_t si0 = (static_cast<int64_t>(b) * a.h + head) * a.S + qw;
       Q.lse2 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.lse + si0, nq * 4), col * 4, 0, 0)) * kLog2e;
-      Q.dl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.delta + si0, nq * 4), col * 4, 0, 0));
+      Q.dl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.delta + si0, nq * 4), col * 4, 0, 0)) *
+             pow2i(g);  // dO enters scaled by 2^g
     }
     const int64_t qrow = (b * a.S + (qvalid ? tq : 0)) * a.h + head;
 
@@ -263,14 +265,14 @@ struct Dq {
     for (; kb < nkb; ++kb) step<true>(a, lds, kb, nkb, b, head, qw, R, Q, dq);
     if (!qvalid) return;
     float* out = a.dq + qrow * DQK;
+    const float osc = a.scale * pow2i(-g);
 #pragma unroll
     for (int n = 0; n < NQT; ++n)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        if (n * 32 + 8 * g + 4 * hf >= DQK) continue;
-        f32x4 w = {dq[n][4 * g] * a.scale, dq[n][4 * g + 1] * a.scale, dq[n][4 * g + 2] * a.scale,
-                   dq[n][4 * g + 3] * a.scale};
-        *reinterpret_cast<f32x4*>(out + n * 32 + 8 * g + 4 * hf) = w;
+      for (int j = 0; j < 4; ++j) {
+        if (n * 32 + 8 * j + 4 * hf >= DQK) continue;
+        f32x4 w = {dq[n][4 * j] * osc, dq[n][4 * j + 1] * osc, dq[n][4 * j + 2] * osc, dq[n][4 * j + 3] * osc};
+        *reinterpret_cast<f32x4*>(out + n * 32 + 8 * j + 4 * hf) = w;
       }
   }
 };
@@ -286,9 +288,11 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(BwdArgs a) {
 }  // namespace
 
 hipError_t launch_attn_bwd_dq(const Shape& s, const void* q, const void* kn, const void* kp, const void* v,
-                              const float* lse, const float* delta, const void* d_o, float* dq, hipStream_t st) {
+                              const float* lse, const float* delta, const void* d_o, const int* do_shift, float* dq,
+                              hipStream_t st) {
   BwdArgs a = make_args(s, q, kn, kp, v, lse, delta, d_o);
   a.dq = dq;
+  a.do_shift = do_shift;
   const unsigned grid = static_cast<unsigned>(((s.S + 127) / 128) * s.B * s.h);
   if (s.bf16 && s.split && s.d_nope == 128 && s.d_rope == 64 && s.d_v == 128)
     hipLaunchKernelGGL((dq_kernel<half_t, MmaF16, 2, 128, 64, 128>), dim3(grid), dim3(kThreads), 0, st, a);

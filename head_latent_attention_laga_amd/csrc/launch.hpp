@@ -32,9 +32,15 @@ hipError_t launch_attn_fwd(const Shape& s, const void* q, const void* k_nope, co
 // inputs), and for split operands e4m3 rows q8 = e4m3(q_nope * 2^s)
 // [T,h,d_nope], do8 = e4m3(dO * 2^s) [T,h,d_v] with one shift per row, whose
 // E8M0 bytes 127 - s are qsc / osc [B,h,S] (int32).
+// do16 holds dO * 2^g, with g (do_shift, one int) chosen from the maxima
+// do_row_max [ceil(T*h / 4)] (one per delta workgroup of 4 rows) so that
+// max |dO| * 2^g lies in [8, 16): the fp16
+// copy keeps dO's relative precision at any gradient magnitude, and the
+// attention-backward kernels undo the factor on their outputs.
 struct BwdCopies {
   void* q16; void* do16; void* kpe16;
   void* q8; void* do8; int* qsc; int* osc;
+  float* do_row_max; int* do_shift;
 };
 // delta = rowsum(dO * o) and, for bfloat16 inputs, the copies above.
 hipError_t launch_bwd_prep(const Shape& s, const float* o, const void* q, const void* d_o, const void* k_pe,
@@ -45,7 +51,7 @@ hipError_t launch_attn_bwd_dkdv(const Shape& s, const void* q, const void* k_nop
                                 float* dk_pe_part, hipStream_t st);
 hipError_t launch_attn_bwd_dq(const Shape& s, const void* q, const void* k_nope, const void* k_pe,
                               const void* v, const float* lse, const float* delta,
-                              const void* d_o, float* dq, hipStream_t st);
+                              const void* d_o, const int* do_shift, float* dq, hipStream_t st);
 hipError_t launch_head_sum(const Shape& s, const float* part, float* out, hipStream_t st);
 // dkv: [T, h, d_nope + d_v] as bf16 hi/lo planes (bf16 inputs) or one fp32 plane.
 hipError_t launch_fold_dl(const Shape& s, const void* dkv, const void* w, float* dL, hipStream_t st);

@@ -96,3 +96,31 @@ def test_backward_is_deterministic():
     torch.cuda.synchronize()
     for k in g1:
         assert torch.equal(g1[k], g2[k]), k
+
+
+@pytest.mark.parametrize("scale_exp", [-20, 12])
+def test_backward_gradient_magnitude(scale_exp):
+    """dO scaled by 2^scale_exp (exact in bf16): at 2^-20 its values sit deep in
+    fp16's subnormal range, at 2^12 the score gradients would overflow fp16.
+    The gradients are linear in dO, so both sides are divided by the scale and
+    held to the usual bars, i.e. the same relative accuracy as at unit scale."""
+    d = _dims(1, 300, 16, 8, 3, li.BF16)
+    announce(f"backward with dO * 2^{scale_exp} dims={d}")
+    inp = li.make_inputs(d, 29, backward=True)
+    x = device_inputs(inp)
+    sc = 2.0 ** scale_exp
+    x["d_o"] = (x["d_o"].float() * sc).to(torch.bfloat16)
+    path = make_path(d, SPLIT)
+    fwd = path.forward(x)
+    g = path.backward(x, fwd, x["d_o"])
+    torch.cuda.synchronize()
+    v = {k: t.value for k, t in inp.items()}
+    assert np.array_equal(host(x["d_o"]), v["d_o"] * sc), "scaling dO by a power of two must be exact"
+    ref = oracle.backward(v["q"], v["latent"], v["k_pe"], v["w_kv_b"], v["gamma"], v["d_o"] * sc, n_h=d.n_h,
+                          sp_size=d.sp_size, sp_rank=d.sp_rank, d_nope=d.d_nope, eps=d.eps)
+    heads = oracle.head_shard(d.n_h, d.sp_size, d.sp_rank)
+    check("dq/s", host(g["dq"]) / sc, ref["dq"] / sc, d.dtype)
+    check("d_latent/s", host(g["d_latent"]) / sc, ref["d_latent"] / sc, d.dtype)
+    check("dk_pe/s", host(g["d_k_pe"]) / sc, ref["dk_pe"] / sc, d.dtype)
+    check("d_gamma/s", host(g["d_gamma"]) / sc, ref["d_gamma"] / sc, d.dtype)
+    check("d_w/s", host(g["d_w_kv_b"])[heads] / sc, ref["d_w_kv_b"][heads] / sc, d.dtype)
