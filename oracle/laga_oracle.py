@@ -278,3 +278,41 @@ def explicit_scores(q, k_nope, k_pe):
             s = (q[b, :, i] @ _keys(k_nope[b, :, i], k_pe[b]).T) / np.sqrt(d_qk)
             out[b, i] = np.where(allowed, s, -np.inf)
     return out
+
+
+# ----------------------------------------------------------------------------
+# Absorbed form (B2 of §3.2) as a forward path of its own, with the two
+# n_h * d_kv-wide intermediates whose memory §3.2 / §4.3 measure
+# ----------------------------------------------------------------------------
+def absorbed_forward_rows(q, L, k_pe, w_kv_b, heads, d_nope, rows):
+    """B2's per-rank forward for the query positions `rows` [LAGA §3.2 (B2), Fig. 2].
+
+    Absorb: q_abs[t,i] = W^k[i]^T q_nope[t,i] (d_kv wide).  Latent attention
+    over the shared latent L (keys L || k_pe, values L): scores
+    (q_abs . L[u] + q_rope . k_pe[u]) / sqrt(d_nope + d_rope), causal softmax,
+    acc[t,i] = sum_u p L[u] (d_kv wide).  Un-absorb: O[t,i] = W^v[i] acc.
+    The softmax scale is that of the explicit scores, which these equal.
+    Returns q_abs, acc [B,len(rows),h,d_kv], O [B,len(rows),h,d_v], lse [B,h,len(rows)].
+    """
+    W = np.asarray(w_kv_b, dtype=np.float64)[heads]
+    B, S, h, d_qk = q.shape
+    d_kv = L.shape[-1]
+    rows = np.asarray(rows)
+    q_abs = np.empty((B, len(rows), h, d_kv))
+    acc = np.empty((B, len(rows), h, d_kv))
+    O = np.empty((B, len(rows), h, W.shape[1] - d_nope))
+    lse = np.empty((B, h, len(rows)))
+    for b in range(B):
+        for i in range(h):
+            Wk, Wv = W[i, :d_nope], W[i, d_nope:]
+            for j, t in enumerate(rows):
+                qa = q[b, t, i, :d_nope] @ Wk
+                s = (L[b, : t + 1] @ qa + k_pe[b, : t + 1] @ q[b, t, i, d_nope:]) / np.sqrt(d_qk)
+                m = np.max(s)
+                e = np.exp(s - m)
+                l = np.sum(e)
+                a = (e / l) @ L[b, : t + 1]
+                q_abs[b, j, i], acc[b, j, i] = qa, a
+                O[b, j, i] = Wv @ a
+                lse[b, i, j] = m + np.log(l)
+    return q_abs, acc, O, lse

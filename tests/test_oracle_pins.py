@@ -192,6 +192,34 @@ def test_absorbed_identity():
     np.testing.assert_allclose(O_abs, f["O"], rtol=1e-10, atol=1e-12)
 
 
+def test_absorbed_forward_matches_explicit_and_definitions():
+    """B2's forward (with its intermediates) against the explicit forward, which
+    the absorbed identity equates, and against the intermediates' definitions."""
+    d, kw = tiny(S=9, n_h=6, sp_size=3, sp_rank=2, d_kv=7, d_nope=4, d_rope=3, d_v=5, B=2, seed=3)
+    f = fwd(d, kw)
+    heads = oracle.head_shard(kw["n_h"], kw["sp_size"], kw["sp_rank"])
+    rows = np.arange(9)
+    q_abs, acc, O, lse = oracle.absorbed_forward_rows(d["q"], f["L"], d["k_pe"], d["w_kv_b"], heads,
+                                                      kw["d_nope"], rows)
+    np.testing.assert_allclose(O, f["O"], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(lse, f["lse"], rtol=1e-12, atol=1e-12)
+    # q_abs against its contraction written as plain loops, and the un-absorb
+    # O[t,i,j] = sum_c W[h_i, d_nope + j, c] acc[t,i,c] likewise.
+    W = d["w_kv_b"]
+    for b in range(2):
+        for t in (0, 4, 8):
+            for i, hg in enumerate(heads):
+                for c in range(7):
+                    ref = sum(d["q"][b, t, i, n] * W[hg, n, c] for n in range(4))
+                    assert abs(q_abs[b, t, i, c] - ref) < 1e-12
+                for j in range(5):
+                    ref = sum(W[hg, 4 + j, c] * acc[b, t, i, c] for c in range(7))
+                    assert abs(O[b, t, i, j] - ref) < 1e-12
+    # the first query attends only to key 0: acc = L[0]
+    np.testing.assert_allclose(acc[:, 0], np.broadcast_to(f["L"][:, 0, None, :], acc[:, 0].shape), rtol=0,
+                               atol=1e-13)
+
+
 # ------------------------------------------------------------ softmax and lse
 def test_softmax_rows_sum_to_one():
     d, kw = tiny(S=11, d_kv=6)
