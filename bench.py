@@ -48,6 +48,15 @@ def alg_flops(d) -> dict:
                 fold=2 * kv_up, fwd=attn_fwd + kv_up, step=3 * attn_fwd + 3 * kv_up)
 
 
+def absorbed_flops(d) -> float:
+    """The absorbed form's (B2) own forward FLOPs: absorb GEMM, latent attention (score
+    width d_kv + d_rope, value width d_kv, causal pairs only), un-absorb GEMM."""
+    pairs = d.S * (d.S + 1) / 2
+    T = d.B * d.S
+    return (2 * T * d.h * d.d_nope * d.d_kv + 2 * pairs * (2 * d.d_kv + d.d_rope) * d.h * d.B
+            + 2 * T * d.h * d.d_kv * d.d_v)
+
+
 def activation_bytes(d, kv_bytes: int) -> dict:
     """Bytes one rank keeps for the backward: LAGA vs the explicit (B1) and absorbed (B2) forms."""
     T, h = d.B * d.S, d.h
@@ -205,6 +214,33 @@ def main():
     fper = {n: statistics.mean(fe[i][k].elapsed_time(fe[i][k + 1]) for i in range(args.steps))
             for k, n in enumerate(["rmsnorm_fwd", "kv_up", "attn_fwd"])}
 
+    # The absorbed form (B2) on the same inputs, forward only, and the device memory
+    # each form's forward allocates for its outputs and kept intermediates (what a
+    # training step holds until the backward), read from torch's allocator.
+    m0 = torch.cuda.memory_allocated()
+    mem_laga_split = path.alloc_forward()
+    m1 = torch.cuda.memory_allocated()
+    absb = fast.alloc_absorbed()
+    m2 = torch.cuda.memory_allocated()
+    del mem_laga_split
+    ae = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for _ in range(args.warmup):
+        fast.absorbed_forward(x, absb)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        ae[i][0].record()
+        fast.absorbed_forward(x, absb)
+        ae[i][1].record()
+    torch.cuda.synchronize()
+    abs_ms = statistics.mean(ae[i][0].elapsed_time(ae[i][1]) for i in range(args.steps))
+    del absb
+    absorbed = {
+        "ms": round(abs_ms, 4), "tokens_s": round(d.B * d.S / (abs_ms / 1e3), 1),
+        "tflops_own": round(absorbed_flops(d) / (abs_ms / 1e3) / 1e12, 2),
+        "time_vs_laga_fwd_fp16": round(abs_ms / (fper["rmsnorm_fwd"] + fper["kv_up"] + fper["attn_fwd"]), 3),
+        "forward_buffers_mb": {"laga_split": round((m1 - m0) / 2**20, 1), "absorbed": round((m2 - m1) / 2**20, 1)},
+    }
+
     # Roofline of the dominant kernel of the step.
     work = {"rmsnorm_fwd": ("hbm", d.B * d.S * d.d_kv * (2 + 4) + 4 * d.B * d.S + 2 * d.d_kv),
             "kv_up": ("mfma", fl["kv_up"]), "attn_fwd": ("mfma", fl["attn_fwd"]),
@@ -241,6 +277,7 @@ def main():
         "kernels_ms": {k: round(v, 4) for k, v in per.items()},
         "roofline": roofline,
         "activation_mb": act,
+        "absorbed_form_fwd": absorbed,
         "gpu": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline:

@@ -48,6 +48,7 @@ _SIGS = {
     "laga_latent_norm": (ctypes.c_int, [ctypes.POINTER(laga_dims), _P, _P, _P, _P, _P]),
     "laga_kv_up": (ctypes.c_int, [ctypes.POINTER(laga_dims), _P, _P, _P, _P, _P]),
     "laga_attn_fwd": (ctypes.c_int, [ctypes.POINTER(laga_dims), _P, _P, _P, _P, _P, _P, _P]),
+    "laga_absorbed_fwd": (ctypes.c_int, [ctypes.POINTER(laga_dims)] + [_P] * 10),
     "laga_attn_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(laga_dims)]),
     "laga_attn_bwd": (ctypes.c_int, [ctypes.POINTER(laga_dims)] + [_P] * 17 + [ctypes.c_size_t, _P]),
     "laga_attn_bwd_traced": (ctypes.c_int, [ctypes.POINTER(laga_dims)] + [_P] * 17
@@ -122,6 +123,12 @@ def attn_fwd(dims, q, k_nope, k_pe, v, o, lse, stream=None):
     _check("laga_attn_fwd", load().laga_attn_fwd(
         ctypes.byref(dims), _ptr(q), _ptr(k_nope), _ptr(k_pe), _ptr(v), _ptr(o), _ptr(lse),
         _stream(stream)))
+
+
+def absorbed_fwd(dims, q, latent_n, k_pe, w_kv_b, q_abs, kx, acc, o, lse, stream=None):
+    _check("laga_absorbed_fwd", load().laga_absorbed_fwd(
+        ctypes.byref(dims), _ptr(q), _ptr(latent_n), _ptr(k_pe), _ptr(w_kv_b), _ptr(q_abs), _ptr(kx), _ptr(acc),
+        _ptr(o), _ptr(lse), _stream(stream)))
 
 
 def attn_bwd_workspace_bytes(dims) -> int:

@@ -1,0 +1,343 @@
+// Absorbed form (B2) of one rank's attention: latent-space attention over the
+// shared latent [LAGA §3.2 (B2), Fig. 2; the scores equal the explicit ones of
+// §2.1 / Algorithm 1].
+//
+//   kx[u]      = L[u] || k_pe[u]                           (fp16, d_kv + d_rope)
+//   s[t,i,u]   = (q_abs[t,i] || q_rope[t,i]) . kx[u] / sqrt(d_nope + d_rope),  u <= t
+//   acc[t,i]   = sum_u softmax_u(s) L[u]                   (fp32, d_kv wide)
+//   lse[i,t]   = ln sum_u exp(s[t,i,u])
+//
+// q_abs (= W^k^T q_nope, d_kv wide) comes from the batched absorb GEMM and the
+// output o = W^v acc from the un-absorb GEMM (gemm.hip).  This is the pages'
+// B2 baseline, built to measure its cost next to LAGA's path: both n_h * d_kv
+// intermediates (q_abs, acc) live in HBM, as a training forward keeps them.
+//
+// Every head reads the same keys and values (the latent), so a workgroup
+// takes 64 consecutive (token, head) query rows - 64 / h tokens of every head -
+// and streams key blocks of 32 rows of kx through LDS once for all of them.
+// Two wavefronts share 32 query rows: each keeps half of the 576 score
+// dimensions of its queries in registers (18 fp16 B-operand fragments of
+// S^T = K . Q^T) and accumulates half of the 512 latent output columns
+// (O^T[dv, query] += V^T . P^T, 8 accumulator tiles, V^T from transposing
+// reads of the same tile: the score and value sides share one copy of L in
+// LDS).  The two partial score tiles meet through LDS: each lane adds its
+// partner's same-lane values, so both wavefronts hold bitwise the same scores
+// and the same softmax.  One wavefront per SIMD.
+//
+// Key blocks move HBM -> LDS with buffer loads straight into LDS (16 bytes per
+// lane, no staging registers) into two separate shared arrays, the next block
+// in flight while the current one is computed.  Rows are 1152 bytes, so row r
+// starts at bank 32 (r & 1); 16-byte chunk c of row r is stored at c ^ f(r),
+// f(r) = bit 1 of r << 2 | bits 2..3 of r (< 8): the 16 rows of a row-read
+// pass and the 4 rows of a transposing read fall on different banks, and with
+// 128-byte aligned rows every read is a per-lane base XOR a constant plus an
+// immediate offset.
+#include "attn_common.hpp"
+#include "launch.hpp"
+
+namespace laga {
+namespace {
+
+constexpr int DL = 512, DR = 64, DNQ = 128, DQ = DL + DR;  // latent, rope band, q_nope, score width
+constexpr int BN = 32;                                      // keys per block
+constexpr int NW = 4, NT = NW * kWave, ROWS = 16 * NW;      // query rows per workgroup (32 per pair)
+constexpr int PITCH = DQ * 2;                               // bytes per kx row in LDS (1152)
+constexpr int CPR = PITCH / 16;                             // 16-byte chunks per row (72)
+constexpr int TILE = BN * PITCH;                            // bytes per key block (36864)
+constexpr int PASSES = TILE / (NT * 16);                    // 1 KB windows per wavefront per block
+constexpr int KSH = DQ / 32, NOH = DL / 64;                 // score steps (18), output tiles (8) per wavefront
+constexpr int XCH = NW * kWave * 16 * 4;                    // partial-score exchange area (bytes)
+constexpr float kRescale = 8.f;                             // lazy-rescale threshold (log2 units)
+static_assert(TILE % (NT * 16) == 0 && CPR % 8 == 0 && PITCH % 128 == 0, "layout");
+
+struct AbsArgs {
+  const half_t* q_abs;  // [B, S, h, DL]
+  const bf16_t* q;      // [B, S, h, DNQ + DR] (rope part used)
+  const half_t* kx;     // [B, S, DQ]
+  float* acc;           // [B, S, h, DL]
+  float* lse;           // [B, h, S]
+  int64_t S;
+  int B, h, n_rt;
+  float scale_log2;
+};
+
+__device__ __forceinline__ int swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+
+// Workgroup barrier for LDS data written by ds_write only: wait for this
+// wave's LDS operations, then s_barrier, with a compiler memory barrier so no
+// LDS access moves across it.  Unlike __syncthreads it does not wait for the
+// global->LDS loads in flight into the other buffer (those are not read until
+// the next __syncthreads).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt left at their maximum
+  asm volatile("s_barrier" ::: "memory");
+}
+
+struct Abs {
+  // Issue one key block (rows key0 ..) into `buf`; rows past the sequence read as zero.
+  __device__ static void issue(const AbsArgs& a, int b, int64_t key0, char* buf) {
+    const int64_t left = a.S - key0;
+    const int nk = static_cast<int>(left < BN ? (left > 0 ? left : 0) : BN);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<half_t*>(a.kx + (static_cast<int64_t>(b) * a.S + key0) * DQ), 0, nk * PITCH, 0x00020000);
+    const int lane = threadIdx.x % kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int w = p * NW + wv;
+      const int P = w * kWave + lane;  // physical chunk of the tile
+      const int r = P / CPR, pc = P % CPR;
+      load_lds16(rs, buf + w * 1024, r * PITCH + (pc ^ swz(r)) * 16);
+    }
+  }
+
+  struct State {
+    half8 qf[KSH];   // score dims 288 hw + 16 j + 8 hf + [0, 8)
+    f32x16 o[NOH];   // latent columns 256 hw + 32 n + ...
+    float m_run, l_run;
+  };
+
+  // Per-lane byte offsets: row fragment of key row col, score step s = 4m + u
+  // at (rb ^ 32u) + 128m; transposing fragment (st, n) at
+  // (tb ^ 64 (n&1) [^ 32 for rows + 8]) + (16 st [+ 8]) * PITCH + 128 (n >> 1).
+  struct Offs { uint32_t rb, tb; };
+
+  __device__ static void compute(const AbsArgs& a, const char* buf, float* xch, int64_t key0, int64_t t_lo,
+                                 int64_t tq, int hw, const Offs& of0, State& st) {
+    Offs of = of0;
+    asm volatile("" : "+v"(of.rb), "+v"(of.tb));  // form the addresses per block, not held across the loop
+    const int lane = threadIdx.x % kWave;
+    const int hf = lane / 32;
+    f32x16 sc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+#pragma unroll
+    for (int j = 0; j < KSH; ++j) {
+      const int s = hw * KSH + j;  // score step over the 576 dims
+      const half8 kf = lds_at<half8>(buf, (of.rb ^ (32u * (s % 4))) + 128 * (s / 4));
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, st.qf[j], sc, 0, 0, 0);
+    }
+    // Partial scores meet the partner's: same lane, same (key, query) elements.
+    f32x4* mine = reinterpret_cast<f32x4*>(xch) + (threadIdx.x / kWave) * kWave * 4 + lane;
+    const f32x4* theirs = reinterpret_cast<const f32x4*>(xch) + ((threadIdx.x / kWave) ^ 1) * kWave * 4 + lane;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) mine[g * kWave] = f32x4{sc[4 * g], sc[4 * g + 1], sc[4 * g + 2], sc[4 * g + 3]};
+    lds_barrier();
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 o4 = theirs[g * kWave];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) sc[4 * g + k] += o4[k];
+    }
+    // Causal mask on blocks that reach past the pair's first query token:
+    // key key0 + 8(r/4) + 4hf + r%4 is masked above the lane's token.
+    if (key0 + BN - 1 > t_lo) {
+      const int rel = static_cast<int>(tq - key0) - 4 * hf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r / 4) + (r % 4) > rel) sc[r] = -INFINITY;
+    }
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sc[r]);
+    mloc = pair_max(mloc) * a.scale_log2;
+    if (__any(mloc > st.m_run + kRescale)) {
+      const float m_new = fmaxf(st.m_run, mloc);
+      const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
+      st.l_run *= alpha;
+#pragma unroll
+      for (int n = 0; n < NOH; ++n)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.o[n][r] *= alpha;
+      st.m_run = m_new;
+    }
+    float lsum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(sc[r], a.scale_log2, -st.m_run));
+      sc[r] = p;
+      lsum += p;
+    }
+    st.l_run += pair_sum(lsum);
+
+    // O^T += V^T P^T over the block's 32 keys for this wavefront's 256 columns.
+#pragma unroll
+    for (int sp = 0; sp < 2; ++sp) {
+      half8 pf;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pf[j] = static_cast<half_t>(sc[sp * 8 + j]);
+#pragma unroll
+      for (int nl = 0; nl < NOH; ++nl) {
+        const int n = hw * NOH + nl;
+        const uint32_t row0 = sp * 16 * PITCH + 128 * (n >> 1);
+        const uint32_t x0 = (of.tb ^ (64u * (n & 1))) + row0;
+        const uint32_t x1 = (of.tb ^ (64u * (n & 1) + 32u)) + row0 + 8 * PITCH;
+        const s16x4 lo = ds_read_tr16(buf + x0), hi = ds_read_tr16(buf + x1);
+        typedef short s16x8 __attribute__((ext_vector_type(8)));
+        const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        st.o[nl] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, v), pf, st.o[nl], 0, 0, 0);
+      }
+    }
+  }
+
+  // Blocks are computed by both wavefronts of a pair or by neither (skipped
+  // when they lie wholly after the pair's last query token), but every
+  // wavefront reaches both barriers of every step.
+  template <bool P>
+  __device__ static void step(const AbsArgs& a, int kb, int b, int64_t t_lo, int64_t t_hi, int64_t tq, int hw,
+                              const char* cur, char* nxt, float* xch, const Offs& of, State& st) {
+    __syncthreads();  // block kb has landed in `cur`; `nxt` (block kb-1) and the exchange area are free
+    const int64_t key0 = static_cast<int64_t>(kb) * BN;
+    issue(a, b, key0 + BN, nxt);  // on every step, so every path has the same loads in flight
+    if (key0 <= t_hi) {
+      compute(a, cur, xch, key0, t_lo, tq, hw, of, st);
+    } else {
+      lds_barrier();  // the exchange barrier of the pairs that compute
+    }
+  }
+
+  __device__ static void run(const AbsArgs& a, char* lds0, char* lds1, float* xch) {
+    const int lane = threadIdx.x % kWave;
+    const int wv = threadIdx.x / kWave;
+    const int pr = wv / 2, hw = wv % 2;  // pair, half
+    const int hf = lane / 32, col = lane % 32, g = lane / 16, sl = lane % 16;
+    // Row tiles longest first; every tile reads the same keys, so L2 serves them all.
+    const int b = static_cast<int>(blockIdx.x) % a.B;
+    const int rt = a.n_rt - 1 - static_cast<int>(blockIdx.x) / a.B;
+    const int64_t rows = a.S * a.h;
+    const int64_t r0 = static_cast<int64_t>(rt) * ROWS + pr * 32;  // the pair's first query row
+    const int64_t row = r0 + col;
+    const bool qvalid = row < rows;
+    const int64_t rc = qvalid ? row : rows - 1;
+    const int64_t tq = rc / a.h;  // the lane's query token
+    const int i = static_cast<int>(rc % a.h);
+    const int64_t t_lo = (r0 < rows ? r0 : rows - 1) / a.h;
+    const int64_t t_hi = (r0 + 31 < rows ? r0 + 31 : rows - 1) / a.h;
+    const int64_t last = static_cast<int64_t>(rt) * ROWS + ROWS - 1;
+    const int64_t tile_hi = (last < rows ? last : rows - 1) / a.h;
+    const int nkb = static_cast<int>(tile_hi / BN) + 1;
+
+    issue(a, b, 0, lds0);
+
+    State st;
+    {
+      const half_t* qa = a.q_abs + (static_cast<int64_t>(b) * a.S * a.h + rc) * DL;
+      const bf16_t* qr = a.q + (static_cast<int64_t>(b) * a.S * a.h + rc) * (DNQ + DR) + DNQ;
+#pragma unroll
+      for (int j = 0; j < KSH; ++j) {
+        const int d = (hw * KSH + j) * 16 + hf * 8;  // score dim of this lane's fragment
+        if (d < DL) {
+          st.qf[j] = qvalid ? *reinterpret_cast<const half8*>(qa + d) : half8{};
+        } else {
+          const u16x8 raw = qvalid ? *reinterpret_cast<const u16x8*>(qr + (d - DL)) : u16x8{};
+          half8 h;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) h[k] = static_cast<half_t>(bf16_to_f32(raw[k]));
+          st.qf[j] = h;
+        }
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < NOH; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.o[n][r] = 0.f;
+    st.m_run = -INFINITY;
+    st.l_run = 0.f;
+
+    Offs of;
+    of.rb = col * PITCH + 16 * (hf ^ swz(col));
+    {
+      const int tr = 4 * hf + sl / 4;  // + 16 st; swz() of it is the same for both halves of the block
+      const int cl = 2 * (g % 2) + (sl % 4) / 2;
+      of.tb = tr * PITCH + 16 * (cl ^ swz(tr)) + 8 * (sl % 2);
+    }
+
+    // Unrolled by two so that each step names its buffers statically.
+    int kb = 0;
+    for (; kb + 1 < nkb; kb += 2) {
+      step<false>(a, kb, b, t_lo, t_hi, tq, hw, lds0, lds1, xch, of, st);
+      step<true>(a, kb + 1, b, t_lo, t_hi, tq, hw, lds1, lds0, xch, of, st);
+    }
+    if (kb < nkb) step<false>(a, kb, b, t_lo, t_hi, tq, hw, lds0, lds1, xch, of, st);
+    // The last step's prefetch must land before the wave ends: the
+    // workgroup's LDS is handed to another workgroup afterwards.
+    __builtin_amdgcn_s_waitcnt(0);
+
+    if (qvalid) {
+      const float inv = 1.0f / st.l_run;
+      float* op = a.acc + (static_cast<int64_t>(b) * a.S * a.h + row) * DL + hw * (DL / 2);
+#pragma unroll
+      for (int n = 0; n < NOH; ++n)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 w = {st.o[n][4 * q4] * inv, st.o[n][4 * q4 + 1] * inv, st.o[n][4 * q4 + 2] * inv,
+                           st.o[n][4 * q4 + 3] * inv};
+          *reinterpret_cast<f32x4*>(op + n * 32 + 8 * q4 + 4 * hf) = w;
+        }
+      if (hw == 0 && hf == 0)
+        a.lse[(static_cast<int64_t>(b) * a.h + i) * a.S + tq] = (st.m_run + log2f(st.l_run)) * 0.69314718055994531f;
+    }
+  }
+};
+
+__global__ __launch_bounds__(NT, 1) void absorbed_attn_kernel(AbsArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds0[TILE];
+  __shared__ __attribute__((aligned(1024))) char lds1[TILE];
+  __shared__ __attribute__((aligned(16))) float xch[XCH / 4];
+  Abs::run(a, lds0, lds1, xch);
+}
+
+// kx[t] = fp16(L[t]) || fp16(k_pe[t]); one thread per 8 elements.
+__global__ __launch_bounds__(256) void absorbed_pack_kernel(const float* __restrict__ L, const bf16_t* __restrict__ k_pe,
+                                                            half_t* __restrict__ kx, int64_t T) {
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;  // 8-element chunk
+  if (j >= T * (DQ / 8)) return;
+  const int64_t t = j / (DQ / 8);
+  const int c = static_cast<int>(j % (DQ / 8)) * 8;
+  half8 h;
+  if (c < DL) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(L + t * DL + c);
+    const f32x4 y = *reinterpret_cast<const f32x4*>(L + t * DL + c + 4);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      h[k] = static_cast<half_t>(x[k]);
+      h[4 + k] = static_cast<half_t>(y[k]);
+    }
+  } else {
+    const u16x8 r = *reinterpret_cast<const u16x8*>(k_pe + t * DR + (c - DL));
+#pragma unroll
+    for (int k = 0; k < 8; ++k) h[k] = static_cast<half_t>(bf16_to_f32(r[k]));
+  }
+  *reinterpret_cast<half8*>(kx + t * DQ + c) = h;
+}
+
+}  // namespace
+
+hipError_t launch_absorbed_pack(const Shape& s, const float* L, const void* k_pe, void* kx, hipStream_t st) {
+  if (!(s.bf16 && s.d_kv == DL && s.d_rope == DR && s.d_nope == DNQ)) return hipErrorNotSupported;
+  const int64_t n = s.T * (DQ / 8);
+  hipLaunchKernelGGL(absorbed_pack_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, L,
+                     static_cast<const bf16_t*>(k_pe), static_cast<half_t*>(kx), s.T);
+  return hipGetLastError();
+}
+
+hipError_t launch_absorbed_attn(const Shape& s, const void* q_abs, const void* q, const void* kx, float* acc,
+                                float* lse, hipStream_t st) {
+  if (!(s.bf16 && s.d_kv == DL && s.d_rope == DR && s.d_nope == DNQ)) return hipErrorNotSupported;
+  AbsArgs a;
+  a.q_abs = static_cast<const half_t*>(q_abs);
+  a.q = static_cast<const bf16_t*>(q);
+  a.kx = static_cast<const half_t*>(kx);
+  a.acc = acc;
+  a.lse = lse;
+  a.S = s.S;
+  a.B = static_cast<int>(s.B);
+  a.h = s.h;
+  a.n_rt = static_cast<int>((s.S * s.h + ROWS - 1) / ROWS);
+  a.scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(s.d_nope + s.d_rope));
+  const int64_t grid = static_cast<int64_t>(a.n_rt) * s.B;
+  hipLaunchKernelGGL(absorbed_attn_kernel, dim3(static_cast<unsigned>(grid)), dim3(NT), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace laga

@@ -120,6 +120,25 @@ laga_status laga_attn_fwd(const laga_dims* dims, const void* q, const void* k_no
   return from_hip(laga::launch_attn_fwd(s, q, k_nope, k_pe, v, o, lse, static_cast<hipStream_t>(stream)));
 }
 
+laga_status laga_absorbed_fwd(const laga_dims* dims, const void* q, const float* latent_n, const void* k_pe,
+                              const void* w_kv_b, void* q_abs, void* kx, float* acc, float* o, float* lse,
+                              void* stream) {
+  Shape s;
+  laga_status st = check_dims(dims, &s);
+  if (st != LAGA_OK) return st;
+  if (!s.bf16) return LAGA_ERR_UNSUPPORTED;  // built for the V3 head dims with bf16 inputs
+  if (!q || !latent_n || !k_pe || !w_kv_b || !q_abs || !kx || !acc || !o || !lse) return LAGA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(latent_n) || !aligned16(k_pe) || !aligned16(w_kv_b) || !aligned16(q_abs) ||
+      !aligned16(kx) || !aligned16(acc) || !aligned16(o) || !aligned16(lse))
+    return LAGA_ERR_ALIGN;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if ((e = laga::launch_absorb_q(s, q, w_kv_b, q_abs, hs)) != hipSuccess) return from_hip(e);
+  if ((e = laga::launch_absorbed_pack(s, latent_n, k_pe, kx, hs)) != hipSuccess) return from_hip(e);
+  if ((e = laga::launch_absorbed_attn(s, q_abs, q, kx, acc, lse, hs)) != hipSuccess) return from_hip(e);
+  return from_hip(laga::launch_unabsorb_o(s, acc, w_kv_b, o, hs));
+}
+
 size_t laga_attn_bwd_workspace_bytes(const laga_dims* dims) {
   Shape s;
   if (check_dims(dims, &s) != LAGA_OK) return 0;

@@ -15,9 +15,10 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // 4j + i/4 (j = 0..3) addressed.  If lane s of the group addresses row
 // k0 + s/4, columns c0 + 4(s%4) .. +3 of a row-major tile, lane i therefore
 // gets column c0 + i, rows k0 .. k0+3.
+// (The address-space cast keeps the compiler's knowledge of which shared
+// array is read, which global->LDS loads into another array rely on.)
 __device__ __forceinline__ s16x4 ds_read_tr16(const void* lds_ptr) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4*)(reinterpret_cast<uintptr_t>(lds_ptr)));
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_ptr));
 }
 
 // Fragment of an operand whose k index runs down the rows of a row-major
@@ -92,7 +93,7 @@ typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 // lanes, byte j (0..7) that lane i receives is element i % 8 of the 8-byte
 // word addressed by lane 2j + i/8 of the group.
 __device__ __forceinline__ i32x2 ds_read_tr8(const void* lds_ptr) {
-  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(reinterpret_cast<uintptr_t>(lds_ptr)));
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(lds_ptr));
 }
 
 // e4m3 A operand (K = 64) of a product against 32x32 accumulators fed as B:
@@ -116,6 +117,24 @@ __device__ __forceinline__ i32x8 tr8_frag_acc64(const uint8_t* tile, int n) {
     out[2 * m + 1] = x[1];
   }
   return out;
+}
+
+// Load of a T from shared memory at byte offset `off` of `base`.  Pointer
+// arithmetic on the shared array (rather than integer addresses) lets the
+// compiler see which array is read, so loads in flight into another array are
+// not waited for.
+template <class T>
+__device__ __forceinline__ T lds_at(const void* base, uint32_t off) {
+  return *reinterpret_cast<const T*>(static_cast<const char*>(base) + off);
+}
+
+// 16 bytes per lane from a buffer resource straight into LDS: lane l's bytes
+// land at lds_window + 16 l (lds_window wave-uniform); offsets outside the
+// resource's range read as zero.  The wave's later s_waitcnt on loads covers
+// the LDS write.
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, void* lds_window, int voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds_window), 16, voffset, 0, 0, 0);
 }
 
 // One 16-byte chunk of a [rows x cols] tile copied from global memory:

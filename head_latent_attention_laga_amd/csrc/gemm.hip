@@ -36,12 +36,14 @@ constexpr int BM = 128, BN = 128, BK = 32;
 constexpr int kThreads = 256;
 
 // A GEMM operand in global memory: element (row r, k) of plane s at
-//   p + s * plane + r * ld + k   (KC)   or   p + s * plane + k * ld + r   (RC).
-// Rows >= R and k >= K read as zero.
+//   p + s * plane + r * ld + k   (KC)   or   p + s * plane + k * ld + r   (RC),
+// plus zstride * z for batch z of a batched GEMM.  Rows >= R and k >= K read
+// as zero.
 template <class Src>
 struct Operand {
   const Src* p;
   int64_t ld, plane, R, K;
+  int64_t zstride = 0;
 };
 
 // ROWS x BK slab of one operand, in NS LDS planes of the MFMA element type.
@@ -167,6 +169,18 @@ struct EpiKvUp {
   }
 };
 
+// out[z * zstride + m * ld + n] as fp16, four consecutive n at a time.
+struct EpiHalf {
+  static constexpr bool TRANS = true;
+  half_t* p; int64_t M; int N; int64_t ld, zstride;
+  __device__ void store4(int64_t m, int n, f32x4 val) const {
+    if (m >= M || n >= N) return;
+    half_t h4[4] = {static_cast<half_t>(val[0]), static_cast<half_t>(val[1]), static_cast<half_t>(val[2]),
+                    static_cast<half_t>(val[3])};
+    *reinterpret_cast<u16x4*>(p + blockIdx.z * zstride + m * ld + n) = *reinterpret_cast<const u16x4*>(h4);
+  }
+};
+
 struct EpiStore {  // out[m * ld + n] (+ chunk offset)
   static constexpr bool TRANS = false;
   float* p; int64_t M; int N; int64_t ld; int64_t chunk_stride;
@@ -180,7 +194,7 @@ struct EpiStore {  // out[m * ld + n] (+ chunk offset)
 template <class M, class SA, class SB, class EPI>
 __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(Operand<typename SA::Src_t> A,
                                                            Operand<typename SB::Src_t> B, EPI epi,
-                                                           int64_t k_chunk, int64_t K) {
+                                                           int64_t k_chunk, int64_t K, int nchunks) {
   typedef typename M::elem E;
   constexpr int STAGE = SA::BYTES + SB::BYTES;
   __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
@@ -189,7 +203,11 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(Operand<typename SA::
   const int wm = wv / 2, wn = wv % 2;
   const int64_t m0 = static_cast<int64_t>(blockIdx.y) * BM;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * BN;
-  const int64_t kbeg = static_cast<int64_t>(blockIdx.z) * k_chunk;
+  // blockIdx.z = batch * nchunks + K chunk (the epilogues index their output by blockIdx.z).
+  const int chunk = static_cast<int>(blockIdx.z) % nchunks, batch = static_cast<int>(blockIdx.z) / nchunks;
+  A.p += batch * A.zstride;
+  B.p += batch * B.zstride;
+  const int64_t kbeg = static_cast<int64_t>(chunk) * k_chunk;
   const int64_t kend = (kbeg + k_chunk < K) ? kbeg + k_chunk : K;
 
   f32x16 acc[2][2];
@@ -299,12 +317,12 @@ struct Side {
 
 template <class M, class SA, class SB, class EPI>
 hipError_t run_gemm(Operand<typename SA::Src_t> A, Operand<typename SB::Src_t> B, EPI epi, int64_t Mrows,
-                    int64_t Ncols, int64_t K, int chunks, hipStream_t st) {
+                    int64_t Ncols, int64_t K, int chunks, hipStream_t st, int batches = 1) {
   const int64_t per = ((K + chunks - 1) / chunks + BK - 1) / BK * BK;
   const int nchunks = static_cast<int>((K + per - 1) / per);
   dim3 grid(static_cast<unsigned>((Ncols + BN - 1) / BN), static_cast<unsigned>((Mrows + BM - 1) / BM),
-            static_cast<unsigned>(nchunks));
-  hipLaunchKernelGGL((gemm_kernel<M, SA, SB, EPI>), grid, dim3(kThreads), 0, st, A, B, epi, per, K);
+            static_cast<unsigned>(nchunks * batches));
+  hipLaunchKernelGGL((gemm_kernel<M, SA, SB, EPI>), grid, dim3(kThreads), 0, st, A, B, epi, per, K, nchunks);
   return hipGetLastError();
 }
 
@@ -358,6 +376,30 @@ hipError_t launch_kv_up(const Shape& s, const float* L, const void* w, void* k_n
   EpiKvUp<float, 1> e{static_cast<float*>(k_nope), static_cast<float*>(v), s.T, static_cast<int>(N),
                       s.C(), s.d_nope, s.d_v, s.h, 0, 0};
   return run_gemm<MmaF32, SA, SB>(A, B, e, s.T, N, s.d_kv, 1, st);
+}
+
+// Absorbed form [LAGA §3.2 (B2)], per local head i (batch z = i):
+//   absorb    q_abs[t, i, c] = sum_n q_nope[t, i, n] W[i, n, c]        (c < d_kv)
+//   un-absorb o[t, i, d]     = sum_c acc[t, i, c] W[i, d_nope + d, c]  (d < d_v)
+hipError_t launch_absorb_q(const Shape& s, const void* q, const void* w, void* q_abs, hipStream_t st) {
+  const int64_t w0 = static_cast<int64_t>(s.head_lo) * s.C() * s.d_kv;
+  typedef Side<MmaBf16, 1, true, BM, bf16_t> SA;   // q_nope rows, n contiguous
+  typedef Side<MmaBf16, 1, false, BN, bf16_t> SB;  // W^k[i]: c contiguous, n strides memory
+  Operand<bf16_t> A{static_cast<const bf16_t*>(q), static_cast<int64_t>(s.h) * s.d_qk(), 0, s.T, s.d_nope, s.d_qk()};
+  Operand<bf16_t> B{static_cast<const bf16_t*>(w) + w0, s.d_kv, 0, s.d_kv, s.d_nope,
+                    static_cast<int64_t>(s.C()) * s.d_kv};
+  EpiHalf e{static_cast<half_t*>(q_abs), s.T, s.d_kv, static_cast<int64_t>(s.h) * s.d_kv, s.d_kv};
+  return run_gemm<MmaBf16, SA, SB>(A, B, e, s.T, s.d_kv, s.d_nope, 1, st, s.h);
+}
+
+hipError_t launch_unabsorb_o(const Shape& s, const float* acc, const void* w, float* o, hipStream_t st) {
+  const int64_t w0 = static_cast<int64_t>(s.head_lo) * s.C() * s.d_kv + static_cast<int64_t>(s.d_nope) * s.d_kv;
+  typedef Side<MmaBf16, 2, true, BM, float> SA;   // acc rows in fp32, split into bf16 hi + lo while staged
+  typedef Side<MmaBf16, 1, true, BN, bf16_t> SB;  // W^v[i] rows, c contiguous
+  Operand<float> A{acc, static_cast<int64_t>(s.h) * s.d_kv, 0, s.T, s.d_kv, s.d_kv};
+  Operand<bf16_t> B{static_cast<const bf16_t*>(w) + w0, s.d_kv, 0, s.d_v, s.d_kv, static_cast<int64_t>(s.C()) * s.d_kv};
+  EpiStore e{o, s.T, s.d_v, static_cast<int64_t>(s.h) * s.d_v, s.d_v};
+  return run_gemm<MmaBf16, SA, SB>(A, B, e, s.T, s.d_v, s.d_kv, 1, st, s.h);
 }
 
 hipError_t launch_fold_dl(const Shape& s, const void* dkv, const void* w, float* dL, hipStream_t st) {

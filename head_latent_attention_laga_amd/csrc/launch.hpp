@@ -62,6 +62,16 @@ hipError_t launch_fold_dw(const Shape& s, const void* dkv, const void* lplanes, 
 hipError_t launch_norm_planes(const Shape& s, const void* latent, const void* gamma, const float* rstd,
                               void* lplanes, hipStream_t st);
 size_t norm_bwd_partial_floats(const Shape& s);
+
+// Absorbed form (B2): q_abs [T, h, d_kv] fp16 = W^k^T q_nope per head; the
+// latent attention over kx = fp16 [T, d_kv + d_rope] (L || k_pe) writing the
+// normalised latent accumulator acc [T, h, d_kv] fp32 and lse [B, h, S]; and
+// o [T, h, d_v] = W^v acc per head.
+hipError_t launch_absorb_q(const Shape& s, const void* q, const void* w, void* q_abs, hipStream_t st);
+hipError_t launch_absorbed_pack(const Shape& s, const float* L, const void* k_pe, void* kx, hipStream_t st);
+hipError_t launch_absorbed_attn(const Shape& s, const void* q_abs, const void* q, const void* kx, float* acc,
+                                float* lse, hipStream_t st);
+hipError_t launch_unabsorb_o(const Shape& s, const float* acc, const void* w, float* o, hipStream_t st);
 hipError_t launch_norm_bwd(const Shape& s, const float* dL, const void* latent, const void* gamma,
                            const float* rstd, float* d_latent, float* dgamma_part, float* d_gamma,
                            hipStream_t st);

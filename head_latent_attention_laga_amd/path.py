@@ -65,6 +65,25 @@ class LagaPath:
         _lib.attn_fwd(self.dims, x["q"], out["k_nope"], x["k_pe"], out["v"], out["o"], out["lse"], stream)
         return out
 
+    def alloc_absorbed(self):
+        """Buffers of the absorbed-form (B2) forward: its n_h*d_kv-wide intermediates
+        q_abs (fp16) and acc (float32), the fp16 key rows kx, and o, lse."""
+        B, S, h = self.B, self.S, self.h
+        return dict(
+            latent_n=self._empty((B, S, self.d_kv)), rstd=self._empty((B, S)),
+            q_abs=self._empty((B, S, h, self.d_kv), torch.float16),
+            kx=self._empty((B, S, self.d_kv + self.d_rope), torch.float16),
+            acc=self._empty((B, S, h, self.d_kv)),
+            o=self._empty((B, S, h, self.d_v)), lse=self._empty((B, h, S)))
+
+    def absorbed_forward(self, x, out=None, stream=None):
+        """The absorbed form's forward on the same inputs: norm, then laga_absorbed_fwd."""
+        out = out or self.alloc_absorbed()
+        _lib.latent_norm(self.dims, x["latent"], x["gamma"], out["latent_n"], out["rstd"], stream)
+        _lib.absorbed_fwd(self.dims, x["q"], out["latent_n"], x["k_pe"], x["w_kv_b"], out["q_abs"], out["kx"],
+                          out["acc"], out["o"], out["lse"], stream)
+        return out
+
     def alloc_backward(self):
         B, S, h = self.B, self.S, self.h
         ws = _lib.attn_bwd_workspace_bytes(self.dims)

@@ -140,6 +140,30 @@ laga_status laga_kv_up(const laga_dims* dims, const float* latent_n, const void*
 laga_status laga_attn_fwd(const laga_dims* dims, const void* q, const void* k_nope,
                           const void* k_pe, const void* v, float* o, float* lse, void* stream);
 
+/*
+ * Absorbed form (B2) forward of the h local heads, the baseline that the
+ * pages port from inference to training [LAGA §3.2 (B2), Fig. 2; §4.3 the
+ * memory it costs].  W_kv_b's K half is folded into the query, attention runs
+ * against the shared latent, and the V half is applied afterwards:
+ *   q_abs[t,i,c] = sum_n q_nope[t,i,n] W[i,n,c]                        (absorb)
+ *   s[t,i,u]     = (q_abs[t,i] . L[u] + q_rope[t,i] . k_pe[u]) / sqrt(d_nope + d_rope), u <= t
+ *   acc[t,i]     = sum_u softmax_u(s) L[u]                           (latent accumulator)
+ *   o[t,i,d]     = sum_c acc[t,i,c] W[i, d_nope + d, c]              (un-absorb)
+ * which equals laga_attn_fwd's o up to rounding (same scores).  Arrays:
+ *   q, k_pe, w_kv_b  as for the LAGA path (bf16); latent_n from laga_latent_norm
+ *   q_abs  [B,S,h,d_kv]          fp16    written: the absorbed query
+ *   kx     [B,S,d_kv + d_rope]   fp16    written: fp16(L) || fp16(k_pe), shared by all heads
+ *   acc    [B,S,h,d_kv]          float32 written: the normalised latent accumulator
+ *   o      [B,S,h,d_v]           float32, lse [B,h,S] float32 (natural log)
+ * q_abs and acc are the n_h * d_kv-wide intermediates whose activation memory
+ * the pages measure; the caller owns them, as it owns LAGA's K/V.  Operands
+ * enter the matrix cores as fp16 (the precision field is ignored).  LAGA_BF16
+ * with the V3 head dims only; anything else returns LAGA_ERR_UNSUPPORTED.
+ */
+laga_status laga_absorbed_fwd(const laga_dims* dims, const void* q, const float* latent_n,
+                              const void* k_pe, const void* w_kv_b, void* q_abs, void* kx,
+                              float* acc, float* o, float* lse, void* stream);
+
 /* Workspace bytes laga_attn_bwd needs for these dims (0 if invalid). */
 size_t laga_attn_bwd_workspace_bytes(const laga_dims* dims);
 

@@ -81,6 +81,7 @@ def test_dims_rejected_before_launch(lib, bad, code):
     assert lib.laga_attn_bwd_workspace_bytes(ctypes.byref(d)) == 0
     args = [FAKE] * 17 + [ctypes.c_size_t(1 << 40), None]
     assert lib.laga_attn_bwd(ctypes.byref(d), *args) == code
+    assert lib.laga_absorbed_fwd(ctypes.byref(d), *([FAKE] * 9), None) == code
 
 
 def test_null_dims(lib):
@@ -96,6 +97,21 @@ def test_null_and_misaligned_pointers(lib, slot):
     assert lib.laga_attn_fwd(ctypes.byref(d), *args, None) == INVALID
     args[slot] = MISALIGNED
     assert lib.laga_attn_fwd(ctypes.byref(d), *args, None) == ALIGN
+
+
+@pytest.mark.parametrize("slot", range(9))
+def test_absorbed_null_and_misaligned_pointers(lib, slot):
+    d = v3()
+    args = [FAKE] * 9
+    args[slot] = None
+    assert lib.laga_absorbed_fwd(ctypes.byref(d), *args, None) == INVALID
+    args[slot] = MISALIGNED
+    assert lib.laga_absorbed_fwd(ctypes.byref(d), *args, None) == ALIGN
+
+
+def test_absorbed_form_needs_bf16_v3_dims(lib):
+    assert lib.laga_absorbed_fwd(ctypes.byref(tiny()), *([FAKE] * 9), None) == UNSUPPORTED
+    assert lib.laga_absorbed_fwd(None, *([FAKE] * 9), None) == INVALID
 
 
 def test_backward_argument_checks(lib):
