@@ -63,16 +63,6 @@ struct AbsArgs {
 
 __device__ __forceinline__ int swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 
-// Workgroup barrier for LDS data written by ds_write only: wait for this
-// wave's LDS operations, then s_barrier, with a compiler memory barrier so no
-// LDS access moves across it.  Unlike __syncthreads it does not wait for the
-// global->LDS loads in flight into the other buffer (those are not read until
-// the next __syncthreads).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt left at their maximum
-  asm volatile("s_barrier" ::: "memory");
-}
-
 struct Abs {
   // Issue one key block (rows key0 ..) into `buf`; rows past the sequence read as zero.
   __device__ static void issue(const AbsArgs& a, int b, int64_t key0, char* buf) {
@@ -186,7 +176,7 @@ struct Abs {
   template <bool P>
   __device__ static void step(const AbsArgs& a, int kb, int b, int64_t t_lo, int64_t t_hi, int64_t tq, int hw,
                               const char* cur, char* nxt, float* xch, const Offs& of, State& st) {
-    __syncthreads();  // block kb has landed in `cur`; `nxt` (block kb-1) and the exchange area are free
+    dma_barrier();  // block kb has landed in `cur`; `nxt` (block kb-1) and the exchange area are free
     const int64_t key0 = static_cast<int64_t>(kb) * BN;
     issue(a, b, key0 + BN, nxt);  // on every step, so every path has the same loads in flight
     if (key0 <= t_hi) {

@@ -137,6 +137,25 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, void* lds_
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds_window), 16, voffset, 0, 0, 0);
 }
 
+// Workgroup barrier for LDS data written by ds_write only: wait for this
+// wave's LDS operations, then s_barrier, with a compiler memory barrier so no
+// LDS access moves across it.  Unlike __syncthreads it does not wait for the
+// global->LDS loads in flight into another buffer.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt left at their maximum
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// Barrier after global->LDS loads: wait for this wave's loads (vmcnt(0);
+// expcnt and lgkmcnt left at their maximum), then __syncthreads.  The
+// compiler tracks such loads only as register writes, not as LDS writes: at a
+// loop head it may issue the barrier with loads still in flight, so that a
+// wave reads rows that another wave's load has not yet written.
+__device__ __forceinline__ void dma_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+  __syncthreads();
+}
+
 // One 16-byte chunk of a [rows x cols] tile copied from global memory:
 // row r of the source starts at src + r*ld (elements), rows >= nrows read as 0.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

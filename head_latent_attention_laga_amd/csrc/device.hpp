@@ -133,6 +133,9 @@ __device__ __forceinline__ f32x2 unpack_e4m3x2(uint32_t w) {
 
 // C += (A * 2^(ea-127)) . (B * 2^(eb-127)) with e4m3 operands, K = 64: lane l
 // supplies row / column l % 32 and k = (l / 32) * 32 + [0, 32) as 32 bytes.
+// The scales act per row of A / column of B: lanes l and l ^ 32 must pass the
+// same ea (eb) -- with different values the products came out wrong, as if
+// one lane's scale were applied to both halves of k.
 __device__ __forceinline__ f32x16 mma_e4m3(i32x8 a, i32x8 b, f32x16 c, int ea, int eb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, ea, 0, eb);
 }
