@@ -308,12 +308,12 @@ struct Dkdv {
     }
   }
 
-  // Publish the staged block `it`, start loading the next one, compute.
+  // Publish the staged block `it` into `buf` (the buffer of its parity),
+  // start loading the next one, compute.
   template <bool MASK>
-  __device__ static void step(const BwdArgs& a, char* lds, int it, int nqb, int b, int head, int64_t k0,
+  __device__ static void step(const BwdArgs& a, char* buf, int it, int nqb, int b, int head, int64_t k0,
                               int64_t wk0, Regs& R, const Stat& K, Acc& acc) {
     const int64_t q0 = k0 + static_cast<int64_t>(it) * BQ;
-    char* buf = lds + (it & 1) * BUF_BYTES;
     store(R, buf);
     __syncthreads();
     if (it + 1 < nqb) load(a, b, head, q0 + BQ, R);
@@ -375,6 +375,7 @@ struct Dkdv {
     // a ragged last block is masked again.
     const int nqb = static_cast<int>((a.S - k0 + BQ - 1) / BQ);
     const int ndiag = nqb < BK / BQ ? nqb : BK / BQ;
+    static_assert((BK / BQ) % 2 == 0, "the unmasked blocks start at an even index");
     const int nfull = static_cast<int>((a.S - k0) / BQ);
     const int nmid = nfull > ndiag ? nfull : ndiag;
     Regs R;
@@ -382,9 +383,16 @@ struct Dkdv {
     R.dsc = pow2i(R.dsh);
     load(a, b, head, k0, R);
     int it = 0;
-    for (; it < ndiag; ++it) step<true>(a, lds, it, nqb, b, head, k0, wk0, R, K, acc);
-    for (; it < nmid; ++it) step<false>(a, lds, it, nqb, b, head, k0, wk0, R, K, acc);
-    for (; it < nqb; ++it) step<true>(a, lds, it, nqb, b, head, k0, wk0, R, K, acc);
+    for (; it < ndiag; ++it) step<true>(a, lds + (it & 1) * BUF_BYTES, it, nqb, b, head, k0, wk0, R, K, acc);
+    // The unmasked blocks start at an even index (ndiag = BK / BQ whenever
+    // there are any), so unrolled by two each step names its buffer as a
+    // constant offset and the LDS addresses fold into immediates.
+    for (; it + 1 < nmid; it += 2) {
+      step<false>(a, lds, it, nqb, b, head, k0, wk0, R, K, acc);
+      step<false>(a, lds + BUF_BYTES, it + 1, nqb, b, head, k0, wk0, R, K, acc);
+    }
+    for (; it < nmid; ++it) step<false>(a, lds + (it & 1) * BUF_BYTES, it, nqb, b, head, k0, wk0, R, K, acc);
+    for (; it < nqb; ++it) step<true>(a, lds + (it & 1) * BUF_BYTES, it, nqb, b, head, k0, wk0, R, K, acc);
     const f32x16* dk = acc.dk;
     const f32x16* dvt = acc.dvt;
 

@@ -199,11 +199,10 @@ struct Dq {
   }
 
   template <bool MASK>
-  __device__ static void step(const BwdArgs& a, char* lds, int kb, int nkb, int b, int head, int64_t qw,
+  __device__ static void step(const BwdArgs& a, char* buf, int kb, int nkb, int b, int head, int64_t qw,
                               Regs& R, const Stat& Q, f32x16* dq) {
     const int64_t key0 = static_cast<int64_t>(kb) * BN;
-    char* buf = lds + (kb & 1) * BUF_BYTES;
-    store(R, buf);
+    store(R, buf);  // `buf`: the buffer of kb's parity
     __syncthreads();
     if (kb + 1 < nkb) load(a, b, head, key0 + BN, R);
     block<MASK>(a, buf, key0, qw, Q, dq);
@@ -261,8 +260,14 @@ struct Dq {
     Regs R;
     load(a, b, head, 0, R);
     int kb = 0;
-    for (; kb < nfree; ++kb) step<false>(a, lds, kb, nkb, b, head, qw, R, Q, dq);
-    for (; kb < nkb; ++kb) step<true>(a, lds, kb, nkb, b, head, qw, R, Q, dq);
+    // Unrolled by two so that each step names its buffer as a constant offset
+    // and the LDS addresses fold into immediates.
+    for (; kb + 1 < nfree; kb += 2) {
+      step<false>(a, lds, kb, nkb, b, head, qw, R, Q, dq);
+      step<false>(a, lds + BUF_BYTES, kb + 1, nkb, b, head, qw, R, Q, dq);
+    }
+    for (; kb < nfree; ++kb) step<false>(a, lds + (kb & 1) * BUF_BYTES, kb, nkb, b, head, qw, R, Q, dq);
+    for (; kb < nkb; ++kb) step<true>(a, lds + (kb & 1) * BUF_BYTES, kb, nkb, b, head, qw, R, Q, dq);
     if (!qvalid) return;
     float* out = a.dq + qrow * DQK;
     const float osc = a.scale * pow2i(-g);
