@@ -391,6 +391,15 @@ struct Fwd {
     int nall = static_cast<int>((q0 + 31) / BN) + 1;
     if (nall > nkb) nall = nkb;
     int kb = 0;
+    // Unrolled by two so that each step names its buffer as a constant offset
+    // and the LDS addresses fold into immediates (single-term operands only:
+    // the split instantiation has no registers to spare for it).
+    if constexpr (!LO8) {
+      for (; kb + 1 < nall; kb += 2) {
+        step<true>(a, kb, nkb, b, head, qw, tq, lds, R, st_);
+        step<true>(a, kb + 1, nkb, b, head, qw, tq, lds + BUF_BYTES, R, st_);
+      }
+    }
     for (; kb < nall; ++kb) step<true>(a, kb, nkb, b, head, qw, tq, lds + (kb & 1) * BUF_BYTES, R, st_);
     for (; kb < nkb; ++kb) step<false>(a, kb, nkb, b, head, qw, tq, lds + (kb & 1) * BUF_BYTES, R, st_);
 
