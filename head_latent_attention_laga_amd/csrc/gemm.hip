@@ -146,7 +146,7 @@ struct EpiKvUp {
   static constexpr bool TRANS = true;  // takes 4 consecutive n of one row m
   KvT* kn; KvT* v; int64_t M; int N, C, dn, dv, h; int64_t plane_k, plane_v;
   // n .. n+3 lie in one head and one part (C, dn multiples of 4).
-  __device__ void store4(int64_t m, int n, f32x4 val) const {
+  __device__ void store4(int64_t m, int n, f32x4 val, int /*z*/) const {
     if (m >= M || n >= N) return;
     const int i = n / C, c = n - i * C;
     const bool isk = c < dn;
@@ -169,42 +169,54 @@ struct EpiKvUp {
   }
 };
 
-// out[z * zstride + m * ld + n] as fp16, four consecutive n at a time.
+// out[z * zstride + m * ld + n] as fp16, four consecutive n at a time
+// (z: the batch of a batched GEMM).
 struct EpiHalf {
   static constexpr bool TRANS = true;
   half_t* p; int64_t M; int N; int64_t ld, zstride;
-  __device__ void store4(int64_t m, int n, f32x4 val) const {
+  __device__ void store4(int64_t m, int n, f32x4 val, int z) const {
     if (m >= M || n >= N) return;
     half_t h4[4] = {static_cast<half_t>(val[0]), static_cast<half_t>(val[1]), static_cast<half_t>(val[2]),
                     static_cast<half_t>(val[3])};
-    *reinterpret_cast<u16x4*>(p + blockIdx.z * zstride + m * ld + n) = *reinterpret_cast<const u16x4*>(h4);
+    *reinterpret_cast<u16x4*>(p + z * zstride + m * ld + n) = *reinterpret_cast<const u16x4*>(h4);
   }
 };
 
-struct EpiStore {  // out[m * ld + n] (+ chunk offset)
+struct EpiStore {  // out[z * chunk_stride + m * ld + n] (z: batch * chunks + K chunk)
   static constexpr bool TRANS = false;
   float* p; int64_t M; int N; int64_t ld; int64_t chunk_stride;
-  __device__ void operator()(int64_t m, int n, float val) const {
+  __device__ void operator()(int64_t m, int n, float val, int z) const {
     if (m >= M || n >= N) return;
-    p[blockIdx.z * chunk_stride + m * ld + n] = val;
+    p[z * chunk_stride + m * ld + n] = val;
   }
 };
 
 // ------------------------------------------------------------------- kernel
+// Tiles (x = N tile, y = M tile, z = batch * nchunks + K chunk) come from a
+// 1-D launch.  Workgroup ids are dealt round-robin to the 8 XCDs, each with
+// its own L2; they are remapped so that every XCD takes one contiguous range
+// of tiles in x-fastest order: the N tiles that share an A row block (and the
+// M tiles that share a B block) then run on the same XCD and read those rows
+// from HBM once instead of once per XCD.
 template <class M, class SA, class SB, class EPI>
 __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(Operand<typename SA::Src_t> A,
                                                            Operand<typename SB::Src_t> B, EPI epi,
-                                                           int64_t k_chunk, int64_t K, int nchunks) {
+                                                           int64_t k_chunk, int64_t K, int nchunks, int gx, int gy,
+                                                           int gz) {
   typedef typename M::elem E;
   constexpr int STAGE = SA::BYTES + SB::BYTES;
   __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
 
+  const int total = gx * gy * gz;
+  const int id = static_cast<int>(blockIdx.x);
+  const int tile = total % 8 == 0 ? (id % 8) * (total / 8) + id / 8 : id;
+  const int bx = tile % gx, by = (tile / gx) % gy, bz = tile / (gx * gy);
   const int wv = threadIdx.x / kWave;
   const int wm = wv / 2, wn = wv % 2;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * BM;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * BN;
-  // blockIdx.z = batch * nchunks + K chunk (the epilogues index their output by blockIdx.z).
-  const int chunk = static_cast<int>(blockIdx.z) % nchunks, batch = static_cast<int>(blockIdx.z) / nchunks;
+  const int64_t m0 = static_cast<int64_t>(by) * BM;
+  const int64_t n0 = static_cast<int64_t>(bx) * BN;
+  // bz = batch * nchunks + K chunk (the epilogues index their output by it).
+  const int chunk = bz % nchunks, batch = bz / nchunks;
   A.p += batch * A.zstride;
   B.p += batch * B.zstride;
   const int64_t kbeg = static_cast<int64_t>(chunk) * k_chunk;
@@ -294,14 +306,14 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(Operand<typename SA::
         for (int g = 0; g < 4; ++g) {
           const int n = static_cast<int>(n0 + wn * 64 + b * 32 + 8 * g + 4 * (lane / 32));
           const f32x4 v4 = {acc[a][b][4 * g], acc[a][b][4 * g + 1], acc[a][b][4 * g + 2], acc[a][b][4 * g + 3]};
-          epi.store4(m, n, v4);
+          epi.store4(m, n, v4, bz);
         }
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t m = m0 + wm * 64 + a * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
           const int n = static_cast<int>(n0 + wn * 64 + b * 32 + (lane % 32));
-          epi(m, n, acc[a][b][r]);
+          epi(m, n, acc[a][b][r], bz);
         }
       }
     }
@@ -320,9 +332,10 @@ hipError_t run_gemm(Operand<typename SA::Src_t> A, Operand<typename SB::Src_t> B
                     int64_t Ncols, int64_t K, int chunks, hipStream_t st, int batches = 1) {
   const int64_t per = ((K + chunks - 1) / chunks + BK - 1) / BK * BK;
   const int nchunks = static_cast<int>((K + per - 1) / per);
-  dim3 grid(static_cast<unsigned>((Ncols + BN - 1) / BN), static_cast<unsigned>((Mrows + BM - 1) / BM),
-            static_cast<unsigned>(nchunks * batches));
-  hipLaunchKernelGGL((gemm_kernel<M, SA, SB, EPI>), grid, dim3(kThreads), 0, st, A, B, epi, per, K, nchunks);
+  const int gx = static_cast<int>((Ncols + BN - 1) / BN), gy = static_cast<int>((Mrows + BM - 1) / BM),
+            gz = nchunks * batches;
+  hipLaunchKernelGGL((gemm_kernel<M, SA, SB, EPI>), dim3(static_cast<unsigned>(gx * gy * gz)), dim3(kThreads), 0, st,
+                     A, B, epi, per, K, nchunks, gx, gy, gz);
   return hipGetLastError();
 }
 
