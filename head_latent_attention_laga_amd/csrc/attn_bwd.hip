@@ -204,6 +204,25 @@ struct Dkdv {
     }
   }
 
+  // Runs use(i, read(i)) for i = 0 .. N-1 with each read issued kAhead uses
+  // before its own, rotating over kAhead + 1 registers; the scheduling barrier
+  // after each use keeps that order (left to itself the compiler issues a
+  // read or two at a time and waits out the LDS latency before each product).
+  static constexpr int kAhead = 4;
+  template <int N, class Read, class Use>
+  __device__ static void pipelined(Read rd, Use use) {
+    constexpr int D = kAhead < N ? kAhead : N;
+    u32x4 fr[D + 1];
+#pragma unroll
+    for (int i = 0; i < D; ++i) fr[i] = rd(i);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if (i + D < N) fr[(i + D) % (D + 1)] = rd(i + D);
+      use(i, fr[i % (D + 1)]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
   // One block of BQ queries starting at q0 against the wavefront's 32 keys
   // from wk0 (lane column `col`).  MASK: the block may cross the causal
   // diagonal or the end of the sequence (and may lie wholly before the keys).
@@ -226,23 +245,58 @@ struct Dkdv {
     f32x16 sc, dp;
 #pragma unroll
     for (int r = 0; r < 16; ++r) { sc[r] = 0.f; dp[r] = 0.f; }
-#pragma unroll
-    for (int s = 0; s < KS_N; ++s) sc = M::mma(lds_frag<M>(qrow + s * M::K), K.kf[s], sc);
-#pragma unroll
-    for (int s = KS_N; s < KS_QK; ++s) sc = M::mma(lds_frag<M>(qrow + s * M::K), K.kr[s - KS_N], sc);
-    if constexpr (LO8) {  // + (q8 * 2^-s_q) . (K_lo * 2^-kLoShift)^T, per-query scale in the A operand
-      const int qs = reinterpret_cast<const int*>(st)[2 * BQ + col];
-      const char* q8row = buf + OFF_Q8 + col * (DN + P8) + 32 * hf;
-#pragma unroll
-      for (int s = 0; s < KS8_N; ++s) sc = mma_e4m3(frag8(q8row + 64 * s), K.k8[s], sc, qs, 127 - kLoShift);
-    }
-#pragma unroll
-    for (int s = 0; s < KS_V; ++s) dp = M::mma(lds_frag<M>(orow + s * M::K), K.vf[s], dp);
     if constexpr (LO8) {
+      // One chain of 16-byte operand reads feeds both score products:
+      //   q rows (KS_QK) | q8 halves (2 KS8_N) | dO rows (KS_V) | dO8 halves (2 KS8_V)
+      // the low terms adding (q8 * 2^-s_q) . (K_lo * 2^-kLoShift)^T with the
+      // per-query scale in the A operand (dP likewise).
+      const int qs = reinterpret_cast<const int*>(st)[2 * BQ + col];
       const int os = reinterpret_cast<const int*>(st)[3 * BQ + col];
+      const char* q8row = buf + OFF_Q8 + col * (DN + P8) + 32 * hf;
       const char* o8row = buf + OFF_O8 + col * (DV + P8) + 32 * hf;
+      constexpr int N8Q = 2 * KS8_N, N8O = 2 * KS8_V;
+      u32x4 half8lo;  // first 16 bytes of an e4m3 fragment
+      auto join = [](u32x4 x, u32x4 y) {
+        return i32x8{static_cast<int>(x[0]), static_cast<int>(x[1]), static_cast<int>(x[2]), static_cast<int>(x[3]),
+                     static_cast<int>(y[0]), static_cast<int>(y[1]), static_cast<int>(y[2]), static_cast<int>(y[3])};
+      };
+      pipelined<KS_QK + N8Q + KS_V + N8O>(
+          [&](int i) {
+            if (i < KS_QK) return *reinterpret_cast<const u32x4*>(qrow + i * M::K);
+            i -= KS_QK;
+            if (i < N8Q) return *reinterpret_cast<const u32x4*>(q8row + 64 * (i / 2) + 16 * (i % 2));
+            i -= N8Q;
+            if (i < KS_V) return *reinterpret_cast<const u32x4*>(orow + i * M::K);
+            i -= KS_V;
+            return *reinterpret_cast<const u32x4*>(o8row + 64 * (i / 2) + 16 * (i % 2));
+          },
+          [&](int i, const u32x4& f) {
+            if (i < KS_QK) {
+              sc = M::mma(__builtin_bit_cast(F, f), i < KS_N ? K.kf[i] : K.kr[i - KS_N], sc);
+              return;
+            }
+            i -= KS_QK;
+            if (i < N8Q) {
+              if (i % 2 == 0) half8lo = f;
+              else sc = mma_e4m3(join(half8lo, f), K.k8[i / 2], sc, qs, 127 - kLoShift);
+              return;
+            }
+            i -= N8Q;
+            if (i < KS_V) {
+              dp = M::mma(__builtin_bit_cast(F, f), K.vf[i], dp);
+              return;
+            }
+            i -= KS_V;
+            if (i % 2 == 0) half8lo = f;
+            else dp = mma_e4m3(join(half8lo, f), K.v8[i / 2], dp, os, 127 - kLoShift);
+          });
+    } else {
 #pragma unroll
-      for (int s = 0; s < KS8_V; ++s) dp = mma_e4m3(frag8(o8row + 64 * s), K.v8[s], dp, os, 127 - kLoShift);
+      for (int s = 0; s < KS_N; ++s) sc = M::mma(lds_frag<M>(qrow + s * M::K), K.kf[s], sc);
+#pragma unroll
+      for (int s = KS_N; s < KS_QK; ++s) sc = M::mma(lds_frag<M>(qrow + s * M::K), K.kr[s - KS_N], sc);
+#pragma unroll
+      for (int s = 0; s < KS_V; ++s) dp = M::mma(lds_frag<M>(orow + s * M::K), K.vf[s], dp);
     }
 
     // P = exp(s - lse) per query row of the block, split into NS terms
