@@ -204,24 +204,7 @@ struct Dkdv {
     }
   }
 
-  // Runs use(i, read(i)) for i = 0 .. N-1 with each read issued kAhead uses
-  // before its own, rotating over kAhead + 1 registers; the scheduling barrier
-  // after each use keeps that order (left to itself the compiler issues a
-  // read or two at a time and waits out the LDS latency before each product).
-  static constexpr int kAhead = 4;
-  template <int N, class Read, class Use>
-  __device__ static void pipelined(Read rd, Use use) {
-    constexpr int D = kAhead < N ? kAhead : N;
-    u32x4 fr[D + 1];
-#pragma unroll
-    for (int i = 0; i < D; ++i) fr[i] = rd(i);
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      if (i + D < N) fr[(i + D) % (D + 1)] = rd(i + D);
-      use(i, fr[i % (D + 1)]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
+  static constexpr int kAhead = 4;  // operand reads in flight ahead of the score products
 
   // One block of BQ queries starting at q0 against the wavefront's 32 keys
   // from wk0 (lane column `col`).  MASK: the block may cross the causal
@@ -260,7 +243,7 @@ struct Dkdv {
         return i32x8{static_cast<int>(x[0]), static_cast<int>(x[1]), static_cast<int>(x[2]), static_cast<int>(x[3]),
                      static_cast<int>(y[0]), static_cast<int>(y[1]), static_cast<int>(y[2]), static_cast<int>(y[3])};
       };
-      pipelined<KS_QK + N8Q + KS_V + N8O>(
+      pipelined<KS_QK + N8Q + KS_V + N8O, kAhead, u32x4>(
           [&](int i) {
             if (i < KS_QK) return *reinterpret_cast<const u32x4*>(qrow + i * M::K);
             i -= KS_QK;

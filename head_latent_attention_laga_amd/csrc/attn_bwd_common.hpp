@@ -12,9 +12,25 @@ namespace bwd {
 
 constexpr int kThreads = 256;  // 4 wavefronts, one per SIMD
 constexpr float kLog2e = 1.4426950408889634f;
-// Instruction classes of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
-constexpr int kReadAhead = 3;  // LDS operand reads kept in flight ahead of the products
+
+// Runs use(i, read(i)) for i = 0 .. N-1 with each read issued D uses before
+// its own, rotating over D + 1 registers; the scheduling barrier after each
+// use keeps that order.  Left to itself the compiler issues a read or two at
+// a time and, with one wavefront per SIMD, waits out the LDS latency before
+// each product.
+template <int N, int D, class Frag, class Read, class Use>
+__device__ __forceinline__ void pipelined(Read rd, Use use) {
+  constexpr int A = D < N ? D : N;
+  Frag fr[A + 1];
+#pragma unroll
+  for (int i = 0; i < A; ++i) fr[i] = rd(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (i + A < N) fr[(i + A) % (A + 1)] = rd(i + A);
+    use(i, fr[i % (A + 1)]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
 
 struct BwdArgs {
   const void* q; const void* k_nope; const void* k_pe; const void* v;
@@ -28,9 +44,6 @@ struct BwdArgs {
   int64_t S, plane_k, plane_v, plane_dkv; int B, h; float scale_log2, scale;
 };
 
-// Row pitches (elements) of LDS tiles: rows read one per lane with 16-byte
-// reads are padded by 16 bytes; rows read with transposing reads (4 rows x
-// 64 bytes per half-wavefront) are padded to a pitch of 16 mod 64 dwords.
 // Row padding (elements) of LDS tiles.  `row`: tiles read only with 16-byte
 // row fragments.  `both`: tiles also read with transposing reads; a pitch of
 // 8 (mod 16) dwords keeps the eight rows of a 16-byte read and the four rows

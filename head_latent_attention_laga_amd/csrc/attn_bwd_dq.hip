@@ -44,6 +44,7 @@ struct Dq {
   static constexpr int IV = (VCH + kThreads - 1) / kThreads;
 
   struct Regs { u32x4 k[IK]; u32x4 p[IP]; u32x4 v[IV]; };
+  static constexpr int kScoreAhead = 4, kDqAhead = 4;  // operand reads in flight ahead of the products
 
   __device__ static void load(const BwdArgs& a, int b, int head, int64_t key0, Regs& R) {
     const int nk = static_cast<int>(a.S - key0 < BN ? a.S - key0 : BN);
@@ -152,24 +153,29 @@ struct Dq {
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) { sc[t][r] = 0.f; dp[t][r] = 0.f; }
-#pragma unroll
-    for (int s = 0; s < KS_QK; ++s)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        sc[t] = M::mma(lds_frag<M>(Kr + (t * 32 + col) * LKR + hf * M::KPL + s * M::K), Q.qf[s], sc[t]);
-        if (s < KS_V)
-          dp[t] = M::mma(lds_frag<M>(Vr + (t * 32 + col) * LVR + hf * M::KPL + s * M::K), Q.of[s], dp[t]);
+    // Products in the order (s, t): S^T from K row s, then (s < KS_V) dP^T
+    // from V row s; each operand read kScoreAhead products ahead.
+    constexpr int NKV = KS_V * 2 * NT;  // products of the steps that have both
+    auto item = [](int i, int& s, int& t, bool& isv) {
+      if (i < NKV) {
+        s = i / (2 * NT); t = (i % (2 * NT)) / 2; isv = i % 2;
+      } else {
+        s = KS_V + (i - NKV) / NT; t = (i - NKV) % NT; isv = false;
       }
-    // Schedule: three operand reads ahead, then one read per product.
-    constexpr int NPROD = NT * (KS_QK + KS_V);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kReadAhead, 0);
-#pragma unroll
-    for (int i = 0; i < NPROD - kReadAhead; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, kReadAhead, 0);
-    __builtin_amdgcn_sched_barrier(0);
+    };
+    pipelined<NKV + (KS_QK - KS_V) * NT, kScoreAhead, F>(
+        [&](int i) {
+          int s, t; bool isv;
+          item(i, s, t, isv);
+          return isv ? lds_frag<M>(Vr + (t * 32 + col) * LVR + hf * M::KPL + s * M::K)
+                     : lds_frag<M>(Kr + (t * 32 + col) * LKR + hf * M::KPL + s * M::K);
+        },
+        [&](int i, const F& f) {
+          int s, t; bool isv;
+          item(i, s, t, isv);
+          if (isv) dp[t] = M::mma(f, Q.of[s], dp[t]);
+          else sc[t] = M::mma(f, Q.qf[s], sc[t]);
+        });
     // rel = key - query of accumulator row 0 of atom t (32-bit: within a block).
     const int rel = static_cast<int>(key0 - qw) - col;
     const int kin = static_cast<int>(a.S - key0);  // keys of the block inside the sequence
@@ -184,7 +190,9 @@ struct Dq {
         }
         dp[t][r] = p * (dp[t][r] - Q.dl);
       }
-    // dq^T[d, q] += K^T dS^T  (k = keys of the accumulators)
+    // dq^T[d, q] += K^T dS^T  (k = keys of the accumulators), the K^T
+    // operands read kDqAhead products ahead.
+    F df[NT][STEPS];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -192,10 +200,11 @@ struct Dq {
         E dh[M::KPL];
 #pragma unroll
         for (int j = 0; j < M::KPL; ++j) dh[j] = M::from_f32(dp[t][stp * M::KPL + j]);
-        const F df = *reinterpret_cast<F*>(dh);
-#pragma unroll
-        for (int n = 0; n < NQT; ++n) dq[n] = M::mma(kt_frag(Kr, t, stp, n * 32), df, dq[n]);
+        df[t][stp] = *reinterpret_cast<F*>(dh);
       }
+    pipelined<NT * STEPS * NQT, kDqAhead, F>(
+        [&](int i) { return kt_frag(Kr, i / NQT / STEPS, (i / NQT) % STEPS, (i % NQT) * 32); },
+        [&](int i, const F& f) { dq[i % NQT] = M::mma(f, df[i / NQT / STEPS][(i / NQT) % STEPS], dq[i % NQT]); });
   }
 
   template <bool MASK>
