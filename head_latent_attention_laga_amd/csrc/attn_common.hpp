@@ -159,6 +159,7 @@ __device__ __forceinline__ void dma_barrier() {
 // One 16-byte chunk of a [rows x cols] tile copied from global memory:
 // row r of the source starts at src + r*ld (elements), rows >= nrows read as 0.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <class T>
 __device__ __forceinline__ u32x4 load_chunk(const T* src, int64_t ld, int r, int c, int nrows) {

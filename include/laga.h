@@ -164,7 +164,13 @@ laga_status laga_absorbed_fwd(const laga_dims* dims, const void* q, const float*
                               const void* k_pe, const void* w_kv_b, void* q_abs, void* kx,
                               float* acc, float* o, float* lse, void* stream);
 
-/* Workspace bytes laga_attn_bwd needs for these dims (0 if invalid). */
+/*
+ * Workspace bytes laga_attn_bwd needs for these dims (0 if invalid).  The
+ * largest part holds dS for every causal 32x32 block of every local head,
+ * passed from the dK/dV kernel to the dq kernel: about B * h * S^2 bytes for
+ * LAGA_BF16 (fp16 elements), twice that for LAGA_F32; 4.3 GB at S = 16384,
+ * h = 16.
+ */
 size_t laga_attn_bwd_workspace_bytes(const laga_dims* dims);
 
 /*
