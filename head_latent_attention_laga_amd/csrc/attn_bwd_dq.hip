@@ -30,8 +30,11 @@ struct Dq {
   static constexpr int DQK = DN + DR;
   static constexpr int BM = 128, BN = 64;
   static constexpr bool TR = M::KPL == 8;
-  // K tile, read transposed only.
-  static constexpr int LKR = DQK + TilePad<M>::both;
+  // K tile, read transposed only: a row pitch of 64 or 192 (mod 256) bytes
+  // puts the four rows a half-wavefront's transposing read touches in four
+  // disjoint 64-byte bank windows.
+  static constexpr int LKR = TR ? DQK + 32 : DQK + TilePad<M>::both;
+  static_assert(!TR || (LKR * 2) % 256 == 64 || (LKR * 2) % 256 == 192, "conflict-free transposing reads");
   static constexpr int BUF_BYTES = BN * LKR * sizeof(E);
   static constexpr int NQT = (DQK + 31) / 32;  // dq^T row atoms (the last may run past d_qk)
   static constexpr int NKS = BN / M::K;        // k-steps (keys) per block
@@ -49,12 +52,12 @@ struct Dq {
   static constexpr int OFF_DS = 2 * BUF_BYTES;
   static constexpr int LDS_BYTES = OFF_DS + 4 * DS_BYTES + (NQT * 32 - DQK) * static_cast<int>(sizeof(E));
 
-  struct Regs { u32x4 k[IK]; u32x4 p[IP]; u32x4 ds[NDC]; };
+  // dS tiles are loaded two key blocks ahead (into the set of the block's
+  // parity), the K tile one block ahead.
+  struct Regs { u32x4 k[IK]; u32x4 p[IP]; u32x4 ds[2][NDC]; };
 
-  // Stage key block key0: the K tile rows (zero past the sequence) and the
-  // wavefront's dS tiles (qb, key0 / 32 + t), zero for tiles above the
-  // diagonal and for wavefronts past the sequence.
-  __device__ static void load(const BwdArgs& a, int b, int head, int64_t key0, int64_t qb, bool qin, Regs& R) {
+  // Stage key block key0's K tile rows (zero past the sequence).
+  __device__ static void load_k(const BwdArgs& a, int b, int head, int64_t key0, Regs& R) {
     const int nk = static_cast<int>(a.S - key0 < BN ? a.S - key0 : BN);
     const int64_t row0 = (b * a.S + key0) * a.h + head;
     const int krow_b = a.h * DN * static_cast<int>(sizeof(E));
@@ -74,6 +77,13 @@ struct Dq {
       const int r = c / (DR / IPC), j = c % (DR / IPC);
       if (PCH % kThreads == 0 || c < PCH) R.p[i] = __builtin_amdgcn_raw_buffer_load_b128(rp, r * prow_b + j * 16, 0, 0);
     }
+  }
+
+  // Stage the wavefront's dS tiles (qb, key0 / 32 + t) of key block key0 into
+  // `ds`, zero for tiles above the diagonal and for wavefronts past the
+  // sequence.
+  __device__ static void load_ds(const BwdArgs& a, int b, int head, int64_t key0, int64_t qb, bool qin,
+                                 u32x4 (&ds)[NDC]) {
     const int lane = threadIdx.x % kWave;
     constexpr int CPT = NDC / (BN / 32);  // chunks per lane per tile
 #pragma unroll
@@ -83,10 +93,10 @@ struct Dq {
         const u32x4* tile = reinterpret_cast<const u32x4*>(static_cast<const E*>(a.ds) +
                                                            ds_tile(a, b, head, qb, kt) * kDsTile);
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) R.ds[t * CPT + c] = __builtin_nontemporal_load(tile + c * kWave + lane);
+        for (int c = 0; c < CPT; ++c) ds[t * CPT + c] = __builtin_nontemporal_load(tile + c * kWave + lane);
       } else {
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) R.ds[t * CPT + c] = u32x4{0, 0, 0, 0};
+        for (int c = 0; c < CPT; ++c) ds[t * CPT + c] = u32x4{0, 0, 0, 0};
       }
     }
   }
@@ -138,17 +148,19 @@ struct Dq {
     }
   }
 
-  // Publish key block kb's K tile into `buf` (the buffer of its parity) and
-  // the wavefront's dS tiles into its area, start loading the next block,
-  // accumulate.
+  // Publish key block kb's K tile into `buf` and the wavefront's dS tiles
+  // into its area (P = kb's parity), start loading the K tile of kb + 1 and
+  // the dS tiles of kb + 2, accumulate.
+  template <int P>
   __device__ static void step(const BwdArgs& a, char* buf, char* dsa, int kb, int nkb, int b, int head,
                               int64_t qb, bool qin, Regs& R, f32x16* dq) {
     store(R, buf);
     const int lane = threadIdx.x % kWave;
 #pragma unroll
-    for (int c = 0; c < NDC; ++c) reinterpret_cast<u32x4*>(dsa)[c * kWave + lane] = R.ds[c];
+    for (int c = 0; c < NDC; ++c) reinterpret_cast<u32x4*>(dsa)[c * kWave + lane] = R.ds[P][c];
     __syncthreads();
-    if (kb + 1 < nkb) load(a, b, head, static_cast<int64_t>(kb + 1) * BN, qb, qin, R);
+    if (kb + 1 < nkb) load_k(a, b, head, static_cast<int64_t>(kb + 1) * BN, R);
+    if (kb + 2 < nkb) load_ds(a, b, head, static_cast<int64_t>(kb + 2) * BN, qb, qin, R.ds[P]);
     const E* D = reinterpret_cast<const E*>(dsa);
     F ds[NKS];
 #pragma unroll
@@ -183,16 +195,18 @@ struct Dq {
     if (kend > a.S) kend = a.S;
     const int nkb = static_cast<int>((kend + BN - 1) / BN);
     Regs R;
-    load(a, b, head, 0, qb, qin, R);
+    load_k(a, b, head, 0, R);
+    load_ds(a, b, head, 0, qb, qin, R.ds[0]);
+    if (nkb > 1) load_ds(a, b, head, BN, qb, qin, R.ds[1]);
     char* dsa = lds + OFF_DS + wv * DS_BYTES;  // this wavefront's dS area
     int kb = 0;
-    // Unrolled by two so that each step names its buffer as a constant offset
-    // and the LDS addresses fold into immediates.
+    // Unrolled by two so that each step names its buffers as constants and
+    // the LDS addresses fold into immediates.
     for (; kb + 1 < nkb; kb += 2) {
-      step(a, lds, dsa, kb, nkb, b, head, qb, qin, R, dq);
-      step(a, lds + BUF_BYTES, dsa, kb + 1, nkb, b, head, qb, qin, R, dq);
+      step<0>(a, lds, dsa, kb, nkb, b, head, qb, qin, R, dq);
+      step<1>(a, lds + BUF_BYTES, dsa, kb + 1, nkb, b, head, qb, qin, R, dq);
     }
-    if (kb < nkb) step(a, lds, dsa, kb, nkb, b, head, qb, qin, R, dq);
+    if (kb < nkb) step<0>(a, lds, dsa, kb, nkb, b, head, qb, qin, R, dq);
     if (tq >= a.S) return;
     float* out = a.dq + ((b * a.S + tq) * a.h + head) * DQK;
     // dS carries dO's scale 2^g.
