@@ -13,25 +13,6 @@ namespace bwd {
 constexpr int kThreads = 256;  // 4 wavefronts, one per SIMD
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Runs use(i, read(i)) for i = 0 .. N-1 with each read issued D uses before
-// its own, rotating over D + 1 registers; the scheduling barrier after each
-// use keeps that order.  Left to itself the compiler issues a read or two at
-// a time and, with one wavefront per SIMD, waits out the LDS latency before
-// each product.
-template <int N, int D, class Frag, class Read, class Use>
-__device__ __forceinline__ void pipelined(Read rd, Use use) {
-  constexpr int A = D < N ? D : N;
-  Frag fr[A + 1];
-#pragma unroll
-  for (int i = 0; i < A; ++i) fr[i] = rd(i);
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    if (i + A < N) fr[(i + A) % (A + 1)] = rd(i + A);
-    use(i, fr[i % (A + 1)]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
 struct BwdArgs {
   const void* q; const void* k_nope; const void* k_pe; const void* v;
   const float* lse; const float* delta; const void* d_o;

@@ -21,6 +21,25 @@ __device__ __forceinline__ s16x4 ds_read_tr16(const void* lds_ptr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_ptr));
 }
 
+// Runs use(i, read(i)) for i = 0 .. N-1 with each read issued D uses before
+// its own, rotating over D + 1 registers; the scheduling barrier after each
+// use keeps that order.  Left to itself the compiler issues a read or two at
+// a time and, with one wavefront per SIMD, waits out the LDS latency before
+// each product.
+template <int N, int D, class Frag, class Read, class Use>
+__device__ __forceinline__ void pipelined(Read rd, Use use) {
+  constexpr int A = D < N ? D : N;
+  Frag fr[A + 1];
+#pragma unroll
+  for (int i = 0; i < A; ++i) fr[i] = rd(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (i + A < N) fr[(i + A) % (A + 1)] = rd(i + A);
+    use(i, fr[i % (A + 1)]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // Fragment of an operand whose k index runs down the rows of a row-major
 // 16-bit tile (k = row, n = column; row pitch `ld` elements), for a 32x32x16
 // atom: lane l gets column n0 + l%32 and the 8 rows

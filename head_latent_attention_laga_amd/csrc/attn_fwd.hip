@@ -160,6 +160,7 @@ struct Fwd {
     }
   }
 
+  static constexpr int kScoreAhead = 2;  // score operand reads in flight ahead of the products
   __device__ static F k_frag(const E* Kp, int r, int c0) { return lds_frag<M>(Kp + r * LDK + c0); }
   __device__ static FR r_frag(const ER* Rp, int r, int c0) { return lds_frag<MR>(Rp + r * LDR + c0); }
 
@@ -207,23 +208,64 @@ struct Fwd {
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[t][r] = 0.f;
+    if constexpr (sizeof(F) == 16 && sizeof(FR) == 16) {
+      // One chain of 16-byte operand reads, kScoreAhead ahead of the products:
+      //   K_nope (s, t) | rope band (s, t) | e4m3 K_lo halves (s, t, half)
+      // the low terms adding Q . K_lo (e4m3 K_lo * 2^kLoShift against e4m3 q).
+      constexpr int NN = 2 * KS_N, NR = 2 * KS_R, N8 = LO8 ? 4 * KS_8 : 0;
+      u32x4 lo;  // first half of an e4m3 fragment
+      pipelined<NN + NR + N8, kScoreAhead, u32x4>(
+          [&](int i) {
+            if (i < NN) {
+              return __builtin_bit_cast(u32x4, k_frag(Ks, (i % 2) * 32 + col, (i / 2) * M::K + hf * M::KPL));
+            } else if (i < NN + NR) {
+              const int j = i - NN;
+              return __builtin_bit_cast(u32x4, r_frag(Kr, (j % 2) * 32 + col, (j / 2) * MR::K + hf * MR::KPL));
+            } else {
+              const int j = i - NN - NR;  // (s, t, half) = (j / 4, (j / 2) % 2, j % 2)
+              return *reinterpret_cast<const u32x4*>(K8 + ((j / 2) % 2 * 32 + col) * K8P + 64 * (j / 4) + 32 * hf +
+                                                      16 * (j % 2));
+            }
+          },
+          [&](int i, const u32x4& f) {
+            if (i < NN) {
+              sc[i % 2] = M::mma(__builtin_bit_cast(F, f), st_.qn[i / 2], sc[i % 2]);
+            } else if (i < NN + NR) {
+              const int j = i - NN;
+              sc[j % 2] = MR::mma(__builtin_bit_cast(FR, f), st_.qr[j / 2], sc[j % 2]);
+            } else {
+              const int j = i - NN - NR;
+              if (j % 2 == 0) {
+                lo = f;
+              } else {
+                const i32x8 k8 = {static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]),
+                                  static_cast<int>(lo[3]), static_cast<int>(f[0]), static_cast<int>(f[1]),
+                                  static_cast<int>(f[2]), static_cast<int>(f[3])};
+                const int t = (j / 2) % 2;
+                sc[t] = mma_e4m3(k8, st_.q8[j / 4], sc[t], 127 - kLoShift, 127);
+              }
+            }
+          });
+    } else {
 #pragma unroll
-    for (int s = 0; s < KS_N; ++s)
+      for (int s = 0; s < KS_N; ++s)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int krow = t * 32 + col;
-        sc[t] = M::mma(k_frag(Ks, krow, s * M::K + hf * M::KPL), st_.qn[s], sc[t]);
-      }
+        for (int t = 0; t < 2; ++t) {
+          const int krow = t * 32 + col;
+          sc[t] = M::mma(k_frag(Ks, krow, s * M::K + hf * M::KPL), st_.qn[s], sc[t]);
+        }
 #pragma unroll
-    for (int s = 0; s < KS_R; ++s)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) sc[t] = MR::mma(r_frag(Kr, t * 32 + col, s * MR::K + hf * MR::KPL), st_.qr[s], sc[t]);
-    if constexpr (LO8) {  // + Q . K_lo: e4m3 K_lo * 2^kLoShift against e4m3 q
-#pragma unroll
-      for (int s = 0; s < KS_8; ++s)
+      for (int s = 0; s < KS_R; ++s)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
-          sc[t] = mma_e4m3(k8_frag(K8, t * 32 + col, s, hf), st_.q8[s], sc[t], 127 - kLoShift, 127);
+          sc[t] = MR::mma(r_frag(Kr, t * 32 + col, s * MR::K + hf * MR::KPL), st_.qr[s], sc[t]);
+      if constexpr (LO8) {  // + Q . K_lo: e4m3 K_lo * 2^kLoShift against e4m3 q
+#pragma unroll
+        for (int s = 0; s < KS_8; ++s)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+            sc[t] = mma_e4m3(k8_frag(K8, t * 32 + col, s, hf), st_.q8[s], sc[t], 127 - kLoShift, 127);
+      }
     }
 
     // Causal mask, only on blocks that cross this wavefront's diagonal: key
@@ -268,17 +310,35 @@ struct Fwd {
     st_.l_run += pair_sum(lsum);
 
     // O^T += V^T P^T; one step covers K keys, accumulator r = st*KPL + j.
+    if constexpr (sizeof(F) == 16) {
+      // V^T operands read kScoreAhead products ahead; P of (t, st) converted
+      // where its first product needs it.
+      F pf;
+      pipelined<2 * PV_STEPS * NO, kScoreAhead, F>(
+          [&](int i) { return v_frag(Vs, i / NO / PV_STEPS, (i / NO) % PV_STEPS, (i % NO) * 32); },
+          [&](int i, const F& v) {
+            const int t = i / NO / PV_STEPS, st = (i / NO) % PV_STEPS;
+            if (i % NO == 0) {
+              E ph[M::KPL];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+              for (int j = 0; j < M::KPL; ++j) ph[j] = M::from_f32(sc[t][st * M::KPL + j]);
+              pf = *reinterpret_cast<F*>(ph);
+            }
+            st_.o[i % NO] = M::mma(v, pf, st_.o[i % NO]);
+          });
+    } else {
 #pragma unroll
-      for (int st = 0; st < PV_STEPS; ++st) {
-        E ph[M::KPL];
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int j = 0; j < M::KPL; ++j) ph[j] = M::from_f32(sc[t][st * M::KPL + j]);
-        const F pf = *reinterpret_cast<F*>(ph);
+        for (int st = 0; st < PV_STEPS; ++st) {
+          E ph[M::KPL];
 #pragma unroll
-        for (int n = 0; n < NO; ++n) st_.o[n] = M::mma(v_frag(Vs, t, st, n * 32), pf, st_.o[n]);
-      }
+          for (int j = 0; j < M::KPL; ++j) ph[j] = M::from_f32(sc[t][st * M::KPL + j]);
+          const F pf = *reinterpret_cast<F*>(ph);
+#pragma unroll
+          for (int n = 0; n < NO; ++n) st_.o[n] = M::mma(v_frag(Vs, t, st, n * 32), pf, st_.o[n]);
+        }
+    }
     if constexpr (LO8) {
       // + P . V_lo over the whole block in one e4m3 atom per 32 dv: byte
       // 16 t + r of a lane's P operand is its probability sc[t][r].
