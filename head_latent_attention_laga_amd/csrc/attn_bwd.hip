@@ -219,6 +219,29 @@ struct Dkdv {
 
   static constexpr int kAhead = 4;  // operand reads in flight ahead of the score products
 
+  // v (accumulator order r) as NS-term MFMA operands: out[r / KPL][q][r % KPL].
+  __device__ static void split16(const float (&v)[16], E (&out)[STEPS][NS][M::KPL]) {
+    if constexpr (std::is_same<E, half_t>::value && NS == 2) {
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        half2_t hi, lo;
+        split_f16_pair(v[r], v[r + 1], hi, lo);
+        out[r / M::KPL][0][r % M::KPL] = hi[0];
+        out[r / M::KPL][0][r % M::KPL + 1] = hi[1];
+        out[r / M::KPL][1][r % M::KPL] = lo[0];
+        out[r / M::KPL][1][r % M::KPL + 1] = lo[1];
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        E t[NS];
+        split_to<M, NS>(v[r], t);
+#pragma unroll
+        for (int q = 0; q < NS; ++q) out[r / M::KPL][q][r % M::KPL] = t[q];
+      }
+    }
+  }
+
   // One block of BQ queries starting at q0 against the wavefront's 32 keys
   // from wk0 (lane column `col`).  MASK: the block may cross the causal
   // diagonal or the end of the sequence (and may lie wholly before the keys).
@@ -313,12 +336,9 @@ struct Dkdv {
           if (rel > qi || qi >= nq) p = 0.f;
         }
         pv[r] = p;
-        E t[NS];
-        split_to<M, NS>(p, t);
-#pragma unroll
-        for (int q = 0; q < NS; ++q) ph[r / M::KPL][q][r % M::KPL] = t[q];
       }
     }
+    split16(pv, ph);
     // dV^T[dv, key] += dO^T P   (k = queries)
 #pragma unroll
     for (int stp = 0; stp < STEPS; ++stp) {
@@ -333,18 +353,14 @@ struct Dkdv {
 
     // dS = P (dP - delta), split the same way.
     E dh[STEPS][NS][M::KPL];
+    float dsv[16];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const f32x4 d4 = *reinterpret_cast<const f32x4*>(st + BQ + 8 * g + 4 * hf);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * g + i;
-        E t[NS];
-        split_to<M, NS>(pv[r] * (dp[r] - d4[i]), t);
-#pragma unroll
-        for (int q = 0; q < NS; ++q) dh[r / M::KPL][q][r % M::KPL] = t[q];
-      }
+      for (int i = 0; i < 4; ++i) dsv[4 * g + i] = pv[4 * g + i] * (dp[4 * g + i] - d4[i]);
     }
+    split16(dsv, dh);
     // dS for the dq kernel (its first split term) into the block's tile
     // [key][query]: lane `col` writes row col, queries 8g + 4hf + [0, 4) as
     // one 4-element store per g.  Streamed past the caches: the tiles are

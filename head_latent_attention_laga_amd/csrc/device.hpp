@@ -151,6 +151,22 @@ __device__ __forceinline__ void split_to(float x, typename M::elem* part) {
   }
 }
 
+// fp16 hi/lo pairs of x0 and x1: hi = fp16(x) and lo = fp16(x - hi), both
+// rounded to nearest even, as split_to<fp16, 2> gives them.  x - hi is exact
+// in fp32, so one mixed-precision FMA per value forms and rounds it, and one
+// packed conversion makes both hi terms.
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split_f16_pair(float x0, float x1, half2_t& hi, half2_t& lo) {
+  hi = __builtin_convertvector(f32x2{x0, x1}, half2_t);
+  // (The compiler turns the FMA form back into a convert and a subtract
+  // about half the time; the two VALU instructions are therefore stated.)
+  const uint32_t h = __builtin_bit_cast(uint32_t, hi);
+  uint32_t l;
+  asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(l) : "v"(h), "v"(x0));
+  asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(l) : "v"(h), "v"(x1));
+  lo = __builtin_bit_cast(half2_t, l);
+}
+
 // Load a KPL-element fragment from LDS (contiguous, aligned to KPL elements).
 template <class M>
 __device__ __forceinline__ typename M::frag lds_frag(const typename M::elem* p) {
