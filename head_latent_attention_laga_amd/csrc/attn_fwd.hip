@@ -341,14 +341,16 @@ struct Fwd {
     }
     if constexpr (LO8) {
       // + P . V_lo over the whole block in one e4m3 atom per 32 dv: byte
-      // 16 t + r of a lane's P operand is its probability sc[t][r].
+      // 16 t + r of a lane's P operand is its probability sc[t][r].  P stays
+      // at or below 2^kRescale (the running max), inside e4m3's range.
+      static_assert(kRescale <= 8, "unnormalised probabilities within e4m3's 448");
       i32x8 p8;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int g = 0; g < 4; ++g)
           p8[4 * t + g] = static_cast<int>(
-              pack_e4m3x4(sc[t][4 * g], sc[t][4 * g + 1], sc[t][4 * g + 2], sc[t][4 * g + 3]));
+              pack_e4m3x4_in_range(sc[t][4 * g], sc[t][4 * g + 1], sc[t][4 * g + 2], sc[t][4 * g + 3]));
 #pragma unroll
       for (int n = 0; n < NO; ++n) st_.o[n] = mma_e4m3(tr8_frag_acc64(V8, n), p8, st_.o[n], 127 - kLoShift, 127);
     }

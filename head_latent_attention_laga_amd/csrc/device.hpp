@@ -115,6 +115,12 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
   return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
 }
 
+// The same for values already within +-448 (no saturation step).
+__device__ __forceinline__ uint32_t pack_e4m3x4_in_range(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
+}
+
 // Power-of-two shift s for a row of e4m3 values with largest magnitude m:
 // m * 2^s lies in [128, 256) (below e4m3's 448 with room for rounding); 0 for
 // an all-zero row.  Clamped so that 127 - s stays a valid E8M0 scale byte.
