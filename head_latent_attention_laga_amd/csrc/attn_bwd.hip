@@ -266,7 +266,8 @@ struct Dkdv {
     for (int r = 0; r < 16; ++r) { sc[r] = 0.f; dp[r] = 0.f; }
     if constexpr (LO8) {
       // One chain of 16-byte operand reads feeds both score products:
-      //   q rows (KS_QK) | q8 halves (2 KS8_N) | dO rows (KS_V) | dO8 halves (2 KS8_V)
+      //   q8 halves (2 KS8_N) | q rows (KS_QK) | dO8 halves (2 KS8_V) | dO rows (KS_V)
+      // (the longer e4m3 products first, so each chain ends on a short one)
       // the low terms adding (q8 * 2^-s_q) . (K_lo * 2^-kLoShift)^T with the
       // per-query scale in the A operand (dP likewise).
       const int qs = reinterpret_cast<const int*>(st)[2 * BQ + col];
@@ -279,35 +280,35 @@ struct Dkdv {
         return i32x8{static_cast<int>(x[0]), static_cast<int>(x[1]), static_cast<int>(x[2]), static_cast<int>(x[3]),
                      static_cast<int>(y[0]), static_cast<int>(y[1]), static_cast<int>(y[2]), static_cast<int>(y[3])};
       };
-      pipelined<KS_QK + N8Q + KS_V + N8O, kAhead, u32x4>(
+      pipelined<N8Q + KS_QK + N8O + KS_V, kAhead, u32x4>(
           [&](int i) {
-            if (i < KS_QK) return *reinterpret_cast<const u32x4*>(qrow + i * M::K);
-            i -= KS_QK;
             if (i < N8Q) return *reinterpret_cast<const u32x4*>(q8row + 64 * (i / 2) + 16 * (i % 2));
             i -= N8Q;
-            if (i < KS_V) return *reinterpret_cast<const u32x4*>(orow + i * M::K);
-            i -= KS_V;
-            return *reinterpret_cast<const u32x4*>(o8row + 64 * (i / 2) + 16 * (i % 2));
+            if (i < KS_QK) return *reinterpret_cast<const u32x4*>(qrow + i * M::K);
+            i -= KS_QK;
+            if (i < N8O) return *reinterpret_cast<const u32x4*>(o8row + 64 * (i / 2) + 16 * (i % 2));
+            i -= N8O;
+            return *reinterpret_cast<const u32x4*>(orow + i * M::K);
           },
           [&](int i, const u32x4& f) {
-            if (i < KS_QK) {
-              sc = M::mma(__builtin_bit_cast(F, f), i < KS_N ? K.kf[i] : K.kr[i - KS_N], sc);
-              return;
-            }
-            i -= KS_QK;
             if (i < N8Q) {
               if (i % 2 == 0) half8lo = f;
               else sc = mma_e4m3(join(half8lo, f), K.k8[i / 2], sc, qs, 127 - kLoShift);
               return;
             }
             i -= N8Q;
-            if (i < KS_V) {
-              dp = M::mma(__builtin_bit_cast(F, f), K.vf[i], dp);
+            if (i < KS_QK) {
+              sc = M::mma(__builtin_bit_cast(F, f), i < KS_N ? K.kf[i] : K.kr[i - KS_N], sc);
               return;
             }
-            i -= KS_V;
-            if (i % 2 == 0) half8lo = f;
-            else dp = mma_e4m3(join(half8lo, f), K.v8[i / 2], dp, os, 127 - kLoShift);
+            i -= KS_QK;
+            if (i < N8O) {
+              if (i % 2 == 0) half8lo = f;
+              else dp = mma_e4m3(join(half8lo, f), K.v8[i / 2], dp, os, 127 - kLoShift);
+              return;
+            }
+            i -= N8O;
+            dp = M::mma(__builtin_bit_cast(F, f), K.vf[i], dp);
           });
     } else {
 #pragma unroll
