@@ -25,11 +25,8 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
           f"-I{INCLUDE}"] + DEVICE_FLAGS
-# Per-file code generation choices.  The dq kernel keeps its matrix-core
-# accumulators in VGPRs: with the default AGPR form the register allocator
-# copies part of the dq accumulators between the register files on every
-# key block.
-FILE_FLAGS = {"attn_bwd_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-file extra compiler flags (none at present).
+FILE_FLAGS: dict = {}
 
 
 def hipcc() -> str:

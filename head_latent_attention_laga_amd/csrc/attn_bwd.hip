@@ -9,21 +9,21 @@
 //   dq  = dS K / sqrt(d_qk)
 // P is rebuilt from the forward's lse, never stored.
 //
-// Two flash-style kernels, neither of which holds an S x S matrix:
+// Two kernels, neither of which holds an S x S matrix in registers or LDS:
 //  * dkdv: a workgroup of 4 wavefronts owns 128 keys of one head (32 per
 //    wavefront; K and V held in registers as B operands) and walks the
 //    queries from its diagonal to the end, 32 at a time.  q and dO blocks
 //    stream through double-buffered LDS (buffer loads in flight in registers
-//    while the previous block is computed), converted to fp16 on the way and
-//    stored twice: rows padded for 16-byte operand reads of S = q K^T and
-//    dP = dO V^T, and rows padded for conflict-free transposing reads that
-//    feed dK^T = q^T dS and dV^T = dO^T P.  The 32x32 accumulators of S / dP
-//    hold one key per lane column, which is the B-operand layout of the
-//    dK / dV products, so P and dS never leave registers.
-//  * dq (attn_bwd_dq.hip): a workgroup of 4 wavefronts owns 128 queries (q
-//    and dO in registers) and walks keys 0 .. diagonal, 64 at a time,
-//    computing S^T = K q^T and dP^T = V dO^T (one query per lane column) and
-//    dq^T = K^T dS^T with K^T from transposing reads.
+//    while the previous block is computed), one tile each, read both as
+//    16-byte rows (the A operands of S = q K^T and dP = dO V^T) and with
+//    transposing reads (the A operands of dK^T = q^T dS and dV^T = dO^T P).
+//    The 32x32 accumulators of S / dP hold one key per lane column, which is
+//    the B-operand layout of the dK / dV products, so P and dS feed them
+//    straight from registers.  Each block's dS also goes to HBM as an fp16
+//    32x32 tile (ds_tile) for the dq kernel.
+//  * dq (attn_bwd_dq.hip): a workgroup of 4 wavefronts owns 128 queries and
+//    walks keys 0 .. diagonal, 64 at a time, accumulating dq^T = K^T dS^T
+//    from those tiles (no score recompute).
 // dk_pe is written per head into a workspace and summed over heads in a fixed
 // order (deterministic, no atomics).
 //
@@ -32,8 +32,8 @@
 // are exact in fp16): S and dP add the low planes of K and V as e4m3 products
 // against e4m3 copies of q_nope and dO, each query row scaled by its own power
 // of two (the row's E8M0 byte is the A operand's scale), and dK, dV take P and
-// dS as fp16 hi + lo.  dq uses the hi parts of K and V and single fp16 dS.
-// The float32 instantiation uses fp32 MFMAs.
+// dS as fp16 hi + lo.  dq takes the hi part of that dS (single fp16) and the
+// hi plane of K.  The float32 instantiation uses fp32 MFMAs.
 #include "attn_bwd_common.hpp"
 
 namespace laga {
