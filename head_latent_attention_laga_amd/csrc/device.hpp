@@ -37,10 +37,8 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t b) {
 }
 
 // Round-to-nearest-even float -> bfloat16 bits (inputs are finite).
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {  // round to nearest even (hardware conversion)
+  return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
 }
 
 // Element tags for templated code: what a value is stored as in memory.
@@ -171,6 +169,16 @@ __device__ __forceinline__ void split_f16_pair(float x0, float x1, half2_t& hi, 
   asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(l) : "v"(h), "v"(x0));
   asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(l) : "v"(h), "v"(x1));
   lo = __builtin_bit_cast(half2_t, l);
+}
+
+// bf16 hi/lo pairs of x0 and x1 (hi = bf16(x), lo = bf16(x - hi), both
+// rounded to nearest even, as split_to<bf16, 2> gives them), packed two to a
+// word: one packed conversion per pair and term, x - hi exact in fp32.
+__device__ __forceinline__ void split_bf16_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2_t));
+  const float r0 = x0 - __uint_as_float(hi << 16), r1 = x1 - __uint_as_float(hi & 0xffff0000u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16x2_t));
 }
 
 // Load a KPL-element fragment from LDS (contiguous, aligned to KPL elements).

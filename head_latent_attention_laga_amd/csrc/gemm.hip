@@ -100,7 +100,22 @@ struct SlabT {
       int r, k;
       chunk_pos(i * kThreads + static_cast<int>(threadIdx.x), r, k);
       E* dst = lds + (KC ? r * LD + k : k * LD + r);
-      if constexpr (SPLIT) {
+      if constexpr (SPLIT && std::is_same<M, MmaBf16>::value) {  // bf16 hi/lo planes, two values per word
+        u32x4 hw, lw;
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          const f32x4 x = __builtin_bit_cast(f32x4, reg[0][i][w]);
+          uint32_t h, l;
+          split_bf16_pair(x[0], x[1], h, l);
+          hw[2 * w] = h;
+          lw[2 * w] = l;
+          split_bf16_pair(x[2], x[3], h, l);
+          hw[2 * w + 1] = h;
+          lw[2 * w + 1] = l;
+        }
+        *reinterpret_cast<u32x4*>(dst) = hw;
+        *reinterpret_cast<u32x4*>(dst + PLANE) = lw;
+      } else if constexpr (SPLIT) {
         E part[NS][EPC];
 #pragma unroll
         for (int w = 0; w < 2; ++w) {
