@@ -190,6 +190,12 @@ def main():
     wall = time.perf_counter() - t0
     per = {n: statistics.mean(ev[i][k].elapsed_time(ev[i][k + 1]) for i in range(args.steps))
            for k, n in enumerate(names)}
+    # Median and minimum over the timed steps: of each kernel, and of a whole
+    # step between its first and last event (launch gaps included).
+    per_med = {n: statistics.median(ev[i][k].elapsed_time(ev[i][k + 1]) for i in range(args.steps))
+               for k, n in enumerate(names)}
+    per_min = {n: min(ev[i][k].elapsed_time(ev[i][k + 1]) for i in range(args.steps)) for k, n in enumerate(names)}
+    step_ev = [ev[i][0].elapsed_time(ev[i][nev - 1]) for i in range(args.steps)]
     ms_step = wall * 1e3 / args.steps
     fl = alg_flops(d)
     tok_s = d.B * d.S / (ms_step / 1e3)
@@ -275,6 +281,10 @@ def main():
             "attn_tflops": round(fl["attn_fwd"] / (fper["attn_fwd"] / 1e3) / 1e12, 2),
             "kernels_ms": {k: round(v, 4) for k, v in fper.items()}},
         "kernels_ms": {k: round(v, 4) for k, v in per.items()},
+        "kernels_ms_median": {k: round(v, 4) for k, v in per_med.items()},
+        "kernels_ms_min": {k: round(v, 4) for k, v in per_min.items()},
+        "step_ms_events": {"median": round(statistics.median(step_ev), 4), "min": round(min(step_ev), 4)},
+        "sclk": gpu_sclk(),
         "roofline": roofline,
         "activation_mb": act,
         "absorbed_form_fwd": absorbed,
@@ -287,6 +297,17 @@ def main():
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
+
+
+def gpu_sclk():
+    """The GPU's current shader clock as rocm-smi reports it (None if unavailable)."""
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    lines = [ln.strip() for ln in out.splitlines() if "sclk" in ln.lower()]
+    return lines[0] if lines else None
 
 
 if __name__ == "__main__":
