@@ -139,3 +139,22 @@ def test_workspace_grows_with_sequence(lib):
     b = lib.laga_attn_bwd_workspace_bytes(ctypes.byref(v3(S=2048)))
     assert b > a > 0
     assert lib.laga_attn_bwd_workspace_bytes(ctypes.byref(tiny())) > 0
+
+
+def _ds_tile_bytes(B, S, h, elem):
+    n = (S + 31) // 32                  # 32-query / 32-key blocks
+    return B * h * n * (n + 1) // 2 * 32 * 32 * elem   # every causal block of every local head
+
+
+def test_workspace_holds_the_ds_tiles(lib):
+    # The backward hands dS from the dK/dV kernel to the dq kernel as one tile
+    # per causal 32x32 block (fp16 for bf16 inputs, fp32 for f32 inputs), so
+    # the workspace grows with S^2 by at least that much.
+    for B, S in ((1, 1000), (2, 4096)):
+        d = v3(B=B, S=S)
+        assert lib.laga_attn_bwd_workspace_bytes(ctypes.byref(d)) >= _ds_tile_bytes(B, S, 16, 2)
+    small = lib.laga_attn_bwd_workspace_bytes(ctypes.byref(v3(S=2048)))
+    large = lib.laga_attn_bwd_workspace_bytes(ctypes.byref(v3(S=4096)))
+    assert large - small >= _ds_tile_bytes(1, 4096, 16, 2) - _ds_tile_bytes(1, 2048, 16, 2)
+    t = tiny(S=300)
+    assert lib.laga_attn_bwd_workspace_bytes(ctypes.byref(t)) >= _ds_tile_bytes(1, 300, 2, 4)
