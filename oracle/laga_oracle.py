@@ -11,7 +11,7 @@ is the explicit MLA attention of §2.1 restricted to the rank's head shard H_r
 this equals the explicit form, so the oracle is the plain definition written
 out in NumPy float64, one head at a time, with no blocking or fusion.
 
-Readings where the paper is silent or garbled (each listed again in the design doc):
+Readings where the paper is silent or garbled:
   * Score formula: §2.1 prints q_nope on the key side; §3.3 Algorithm 1 and
     §5.3 use (k_nope || k_pe).  The key side is (k_nope || k_pe).
   * Scale 1/sqrt(d): d is the per-head q.k width d_nope + d_rope (192 at V3
