@@ -217,7 +217,7 @@ struct Dkdv {
     }
   }
 
-  static constexpr int kAhead = 4;  // operand reads in flight ahead of the score products
+  static constexpr int kAhead = 6;  // operand reads in flight ahead of the score products
 
   // v (accumulator order r) as NS-term MFMA operands: out[r / KPL][q][r % KPL].
   __device__ static void split16(const float (&v)[16], E (&out)[STEPS][NS][M::KPL]) {

@@ -42,7 +42,7 @@ struct Dq {
   static constexpr int EPC = 16 / sizeof(E), IPC = 16 / sizeof(InT);
   static constexpr int KCH = BN * DN / EPC, PCH = BN * DR / IPC;
   static constexpr int IK = (KCH + kThreads - 1) / kThreads, IP = (PCH + kThreads - 1) / kThreads;
-  static constexpr int kAhead = 4;  // K^T operand reads in flight ahead of the products
+  static constexpr int kAhead = 6;  // K^T operand reads in flight ahead of the products
   // dS: the wavefront's two tiles of a key block, as 16-byte chunks (NDC per
   // lane) and in its private LDS area.
   static constexpr int DS_BYTES = (BN / 32) * kDsTile * static_cast<int>(sizeof(E));
