@@ -641,6 +641,7 @@ __global__ __launch_bounds__(1024) void do_shift_kernel(const float* __restrict_
                                                         int* __restrict__ shift) {
   __shared__ float part[1024 / kWave];
   float m = 0.f;
+#pragma unroll 8  // eight loads in flight per thread
   for (int64_t i = threadIdx.x; i < n; i += 1024) m = fmaxf(m, part_max[i]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
@@ -673,6 +674,7 @@ __global__ __launch_bounds__(256) void head_sum_kernel(const float* __restrict__
   const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (j >= n) return;
   float s = 0.f;
+#pragma unroll 8  // the loads issue together; the sum keeps its order
   for (int i = 0; i < h; ++i) s += part[i * n + j];
   out[j] = s;
 }

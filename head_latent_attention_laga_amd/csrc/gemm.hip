@@ -373,6 +373,7 @@ __global__ __launch_bounds__(256) void chunk_sum_kernel(const float* __restrict_
   const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (j >= n) return;
   float s = 0.f;
+#pragma unroll 8  // the loads issue together; the sum keeps its order
   for (int c = 0; c < chunks; ++c) s += part[c * n + j];
   out[j] = s;
 }

@@ -146,6 +146,7 @@ __global__ __launch_bounds__(kNormBlock) void column_sum_kernel(const float* __r
   const int c = blockIdx.x * kSumCols + cl;
   float s = 0.f;
   if (c < cols)
+#pragma unroll 8  // the loads issue together; the sum keeps its order
     for (int p = g; p < rows; p += kSumGroups) s += part[static_cast<int64_t>(p) * cols + c];
   red[g][cl] = s;
   __syncthreads();
