@@ -558,6 +558,8 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(const float* __restrict__ 
 // with plain 16-byte copies.  One wavefront per (b, t, i) row: the first DV/8
 // lanes take 8 elements of dO and o each, the next DQK/8 lanes 8 elements of
 // q, and on the i == 0 row the next DR/8 lanes 8 elements of k_pe.
+constexpr int kRowsPerWave = 4;  // rows of the delta / copy pass per wavefront
+
 template <int DN, int DR, int DV>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__ o, const bf16_t* __restrict__ q,
                                                        const bf16_t* __restrict__ d_o,
@@ -570,68 +572,82 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
   static_assert(NO + NQ + NR <= kWave && DV % 8 == 0 && DQK % 8 == 0 && DR % 8 == 0, "one chunk per lane");
   static_assert(NO == 16 && DN / 8 == 16, "dO and q_nope fill one 16-lane group each");
   const int lane = threadIdx.x % kWave;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;  // (b, t, i)
-  // Rows past the end still reach the workgroup barrier below; they touch no memory.
-  const bool live = row < rows;
-  const int64_t bt = (live ? row : 0) / h;
-  const int i = static_cast<int>((live ? row : 0) % h);
-  auto to_half8 = [](u16x8 v, float* f) {
-    half8 r;
+  // kRowsPerWave consecutive rows (b, t, i) per wavefront, their loads issued
+  // together; rows past the end still reach the workgroup barrier below and
+  // touch no memory.
+  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave) * kRowsPerWave;
+  u16x8 raw[kRowsPerWave];
+  f32x4 o0[kRowsPerWave], o1[kRowsPerWave];
+#pragma unroll
+  for (int r = 0; r < kRowsPerWave; ++r) {
+    const int64_t row = row0 + r;
+    const int i = static_cast<int>(row % h);
+    raw[r] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    o0[r] = o1[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (row >= rows) continue;
+    if (lane < NO) {
+      const int64_t at = row * DV + lane * 8;
+      raw[r] = *reinterpret_cast<const u16x8*>(d_o + at);
+      o0[r] = *reinterpret_cast<const f32x4*>(o + at);
+      o1[r] = *reinterpret_cast<const f32x4*>(o + at + 4);
+    } else if (lane < NO + NQ) {
+      raw[r] = *reinterpret_cast<const u16x8*>(q + row * DQK + (lane - NO) * 8);
+    } else if (lane < NO + NQ + NR && i == 0) {
+      raw[r] = *reinterpret_cast<const u16x8*>(k_pe + (row / h) * DR + (lane - NO - NQ) * 8);
+    }
+  }
+  float wave_amax = 0.f;  // largest |dO| of the wavefront's rows (dO lanes)
+#pragma unroll
+  for (int r = 0; r < kRowsPerWave; ++r) {
+    const int64_t row = row0 + r;
+    const bool live = row < rows;
+    const int64_t bt = (live ? row : 0) / h;
+    const int i = static_cast<int>((live ? row : 0) % h);
+    float f[8];
+    half8 hv;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      f[j] = bf16_to_f32(v[j]);
-      r[j] = static_cast<half_t>(f[j]);
+      f[j] = bf16_to_f32(raw[r][j]);
+      hv[j] = static_cast<half_t>(f[j]);
     }
-    return r;
-  };
-  float acc = 0.f;
-  float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (!live) {
-    // no memory: f stays 0
-  } else if (lane < NO) {
-    const int64_t at = row * DV + lane * 8;
-    to_half8(*reinterpret_cast<const u16x8*>(d_o + at), f);  // dO's fp16 copy follows the global scale
-    const f32x4 o0 = *reinterpret_cast<const f32x4*>(o + at), o1 = *reinterpret_cast<const f32x4*>(o + at + 4);
+    float acc = 0.f;
+    if (live && lane < NO) {  // dO's fp16 copy follows the global scale (do_convert_kernel)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc += f[j] * o0[j] + f[4 + j] * o1[j];
-  } else if (lane < NO + NQ) {
-    const int64_t at = row * DQK + (lane - NO) * 8;
-    *reinterpret_cast<half8*>(q16 + at) = to_half8(*reinterpret_cast<const u16x8*>(q + at), f);
-  } else if (lane < NO + NQ + NR && i == 0) {
-    const int64_t at = bt * DR + (lane - NO - NQ) * 8;
-    *reinterpret_cast<half8*>(kpe16 + at) = to_half8(*reinterpret_cast<const u16x8*>(k_pe + at), f);
+      for (int j = 0; j < 4; ++j) acc += f[j] * o0[r][j] + f[4 + j] * o1[r][j];
+    } else if (live && lane < NO + NQ) {
+      *reinterpret_cast<half8*>(q16 + row * DQK + (lane - NO) * 8) = hv;
+    } else if (live && lane < NO + NQ + NR && i == 0) {
+      *reinterpret_cast<half8*>(kpe16 + bt * DR + (lane - NO - NQ) * 8) = hv;
+    }
+    // e4m3 copies of the dO row (lanes 0..15) and the q_nope row (lanes
+    // 16..31), each scaled by the power of two 2^s that brings its largest
+    // magnitude into [128, 256); the E8M0 byte 127 - s undoes it inside the
+    // matrix-core product.
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[j]));
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, kWave));
+    wave_amax = fmaxf(wave_amax, amax);
+    const int sh = e4m3_row_shift(amax);
+    const float sc = __uint_as_float(static_cast<uint32_t>(127 + sh) << 23);
+    const int64_t b = bt / S, t = bt % S;
+    const int64_t si = (b * h + i) * S + t;
+    if (live && lane < NO + DN / 8) {
+      uint8_t* dst = lane < NO ? do8 + row * DV + lane * 8 : q8 + row * DN + (lane - NO) * 8;
+      *reinterpret_cast<uint2*>(dst) = make_uint2(pack_e4m3x4(f[0] * sc, f[1] * sc, f[2] * sc, f[3] * sc),
+                                                  pack_e4m3x4(f[4] * sc, f[5] * sc, f[6] * sc, f[7] * sc));
+      if (lane == 0) osc[si] = 127 - sh;
+      if (lane == NO) qsc[si] = 127 - sh;
+    }
+    acc = wave_sum(acc);
+    if (live && lane == 0) delta[si] = acc;
   }
-  // e4m3 copies of the dO row (lanes 0..15) and the q_nope row (lanes 16..31),
-  // each scaled by the power of two 2^s that brings its largest magnitude into
-  // [128, 256); the E8M0 byte 127 - s undoes it inside the matrix-core product.
-  float amax = 0.f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[j]));
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, kWave));
-  const int s = e4m3_row_shift(amax);
-  const float sc = __uint_as_float(static_cast<uint32_t>(127 + s) << 23);
-  const int64_t b = bt / S, t = bt % S;
-  const int64_t si = (b * h + i) * S + t;
-  if (live && lane < NO + DN / 8) {
-    uint8_t* dst = lane < NO ? do8 + row * DV + lane * 8 : q8 + row * DN + (lane - NO) * 8;
-    *reinterpret_cast<uint2*>(dst) = make_uint2(pack_e4m3x4(f[0] * sc, f[1] * sc, f[2] * sc, f[3] * sc),
-                                                pack_e4m3x4(f[4] * sc, f[5] * sc, f[6] * sc, f[7] * sc));
-    if (lane == 0) osc[si] = 127 - s;
-    if (lane == NO) qsc[si] = 127 - s;
-  }
-  acc = wave_sum(acc);
-  if (live && lane == 0) delta[si] = acc;
   // Largest |dO| of the workgroup's rows (lane 0's group holds dO), one value per workgroup.
   __shared__ float wmax[4];
-  if (lane == 0) wmax[threadIdx.x / kWave] = amax;
+  if (lane == 0) wmax[threadIdx.x / kWave] = wave_amax;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const int nw = static_cast<int>(rows - static_cast<int64_t>(blockIdx.x) * 4 < 4 ? rows - blockIdx.x * 4 : 4);
-    float m = wmax[0];
-    for (int w = 1; w < nw; ++w) m = fmaxf(m, wmax[w]);
-    do_max[blockIdx.x] = m;
-  }
+  if (threadIdx.x == 0) do_max[blockIdx.x] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
 }
 
 // g = the shift that brings max |dO| into [8, 16) (0 for an all-zero dO),
@@ -686,12 +702,13 @@ hipError_t launch_bwd_prep(const Shape& s, const float* o, const void* q, const 
   const int64_t rows = s.T * s.h;
   const unsigned blocks = static_cast<unsigned>((rows + 3) / 4);
   if (s.bf16 && s.d_nope == 128 && s.d_rope == 64 && s.d_v == 128) {
-    hipLaunchKernelGGL((bwd_prep_kernel<128, 64, 128>), dim3(blocks), dim3(256), 0, st, o,
+    const unsigned pblocks = static_cast<unsigned>((rows + 4 * kRowsPerWave - 1) / (4 * kRowsPerWave));
+    hipLaunchKernelGGL((bwd_prep_kernel<128, 64, 128>), dim3(pblocks), dim3(256), 0, st, o,
                        static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(d_o),
                        static_cast<const bf16_t*>(k_pe), delta, static_cast<half_t*>(c.q16),
                        static_cast<half_t*>(c.kpe16), static_cast<uint8_t*>(c.q8), static_cast<uint8_t*>(c.do8),
                        c.qsc, c.osc, c.do_row_max, rows, s.h, s.S);
-    hipLaunchKernelGGL(do_shift_kernel, dim3(1), dim3(1024), 0, st, c.do_row_max, static_cast<int64_t>(blocks),
+    hipLaunchKernelGGL(do_shift_kernel, dim3(1), dim3(1024), 0, st, c.do_row_max, static_cast<int64_t>(pblocks),
                        c.do_shift);
     const int64_t n8 = rows * s.d_v / 8;
     hipLaunchKernelGGL(do_convert_kernel, dim3(static_cast<unsigned>((n8 + 255) / 256)), dim3(256), 0, st,
