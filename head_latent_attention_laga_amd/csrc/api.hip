@@ -49,7 +49,7 @@ laga_status from_hip(hipError_t e) {
 
 // Backward workspace regions, each 256-byte aligned, in float32 elements.
 struct BwdLayout {
-  size_t delta, cvt, lo8, dos, ds, dkv, dkpe, dL, lp, dw, dg, total;  // byte offsets, total bytes
+  size_t delta, cvt, lo8, dos, dkv, dkpe, dL, lp, dw, dg, total;  // byte offsets, total bytes
 };
 
 size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
@@ -69,7 +69,6 @@ BwdLayout bwd_layout(const Shape& s) {
   L.lo8 = take(s.split ? (static_cast<size_t>(s.T) * s.h * (s.d_nope + s.d_v) + 3) / 4 + 2 * s.T * s.h : 0);
   // Maxima of |dO| per delta workgroup (4 rows) and the dO scale shift (bfloat16 inputs).
   L.dos = take(s.bf16 ? (static_cast<size_t>(s.T) * s.h + 3) / 4 + 64 : 0);
-  L.ds = take(laga::ds_tile_bytes(s) / sizeof(float));  // dS tiles (dK/dV kernel -> dq kernel)
   L.dkv = take(static_cast<size_t>(s.T) * s.h * s.C());
   L.dkpe = take(static_cast<size_t>(s.h) * s.T * s.d_rope);
   L.dL = take(static_cast<size_t>(s.T) * s.d_kv);
@@ -203,12 +202,11 @@ laga_status laga_attn_bwd_traced(const laga_dims* dims, const void* q, const voi
     k_pe = cp.kpe16;
   }
   if ((e = mark(1)) != hipSuccess) return from_hip(e);
-  void* ds = ws + L.ds;
-  if ((e = laga::launch_attn_bwd_dkdv(s, q, k_nope, k_pe, v, lse, delta, d_o, cp, dkv, dkpe, ds, hs)) !=
-      hipSuccess)
+  if ((e = laga::launch_attn_bwd_dkdv(s, q, k_nope, k_pe, v, lse, delta, d_o, cp, dkv, dkpe, hs)) != hipSuccess)
     return from_hip(e);
   if ((e = mark(2)) != hipSuccess) return from_hip(e);
-  if ((e = laga::launch_attn_bwd_dq(s, k_nope, k_pe, ds, cp.do_shift, dq, hs)) != hipSuccess) return from_hip(e);
+  if ((e = laga::launch_attn_bwd_dq(s, q, k_nope, k_pe, v, lse, delta, d_o, cp.do_shift, dq, hs)) != hipSuccess)
+    return from_hip(e);
   if ((e = mark(3)) != hipSuccess) return from_hip(e);
   if ((e = laga::launch_head_sum(s, dkpe, d_k_pe, hs)) != hipSuccess) return from_hip(e);
   if ((e = mark(4)) != hipSuccess) return from_hip(e);

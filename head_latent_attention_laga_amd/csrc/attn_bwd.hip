@@ -9,7 +9,8 @@
 //   dq  = dS K / sqrt(d_qk)
 // P is rebuilt from the forward's lse, never stored.
 //
-// Two kernels, neither of which holds an S x S matrix in registers or LDS:
+// Two kernels, neither of which holds or writes an S x S quantity, so the
+// backward's memory grows linearly with S:
 //  * dkdv: a workgroup of 4 wavefronts owns 128 keys of one head (32 per
 //    wavefront; K and V held in registers as B operands) and walks the
 //    queries from its diagonal to the end, 32 at a time.  q and dO blocks
@@ -19,11 +20,9 @@
 //    transposing reads (the A operands of dK^T = q^T dS and dV^T = dO^T P).
 //    The 32x32 accumulators of S / dP hold one key per lane column, which is
 //    the B-operand layout of the dK / dV products, so P and dS feed them
-//    straight from registers.  Each block's dS also goes to HBM as an fp16
-//    32x32 tile (ds_tile) for the dq kernel.
-//  * dq (attn_bwd_dq.hip): a workgroup of 4 wavefronts owns 128 queries and
-//    walks keys 0 .. diagonal, 64 at a time, accumulating dq^T = K^T dS^T
-//    from those tiles (no score recompute).
+//    straight from registers.
+//  * dq (attn_bwd_dq.hip): query-stationary, like the forward; it recomputes
+//    P and dS for its queries from lse and delta.
 // dk_pe is written per head into a workspace and summed over heads in a fixed
 // order (deterministic, no atomics).
 //
@@ -32,8 +31,7 @@
 // are exact in fp16): S and dP add the low planes of K and V as e4m3 products
 // against e4m3 copies of q_nope and dO, each query row scaled by its own power
 // of two (the row's E8M0 byte is the A operand's scale), and dK, dV take P and
-// dS as fp16 hi + lo.  dq takes the hi part of that dS (single fp16) and the
-// hi plane of K.  The float32 instantiation uses fp32 MFMAs.
+// dS as fp16 hi + lo.  The float32 instantiation uses fp32 MFMAs.
 #include "attn_bwd_common.hpp"
 
 namespace laga {
@@ -170,19 +168,6 @@ struct Dkdv {
     }
   }
 
-  // Four consecutive elements to global memory, non-temporal.
-  __device__ static void store4_nt(E* p, const E (&v)[4]) {
-    if constexpr (sizeof(E) == 2) {
-      u32x2 w;
-      __builtin_memcpy(&w, v, 8);
-      __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(p));
-    } else {
-      u32x4 w;
-      __builtin_memcpy(&w, v, 16);
-      __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
-    }
-  }
-
   // 32 e4m3 bytes of an LDS row (the A or B operand of one e4m3 atom).
   __device__ static i32x8 frag8(const char* p) {
     const u32x4 x = *reinterpret_cast<const u32x4*>(p), y = *reinterpret_cast<const u32x4*>(p + 16);
@@ -246,7 +231,7 @@ struct Dkdv {
   // from wk0 (lane column `col`).  MASK: the block may cross the causal
   // diagonal or the end of the sequence (and may lie wholly before the keys).
   template <bool MASK>
-  __device__ static void block(const BwdArgs& a, const char* buf, int64_t q0, int64_t wk0, E* ds, const Stat& K,
+  __device__ static void block(const BwdArgs& a, const char* buf, int64_t q0, int64_t wk0, const Stat& K,
                                Acc& acc) {
     const int lane = threadIdx.x % kWave;
     const int hf = lane / 32, col = lane % 32;
@@ -362,18 +347,6 @@ struct Dkdv {
       for (int i = 0; i < 4; ++i) dsv[4 * g + i] = pv[4 * g + i] * (dp[4 * g + i] - d4[i]);
     }
     split16(dsv, dh);
-    // dS for the dq kernel (its first split term) into the block's tile
-    // [key][query]: lane `col` writes row col, queries 8g + 4hf + [0, 4) as
-    // one 4-element store per g.  Streamed past the caches: the tiles are
-    // read once, by the next kernel.
-    E* drow = ds + col * 32 + 4 * hf;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      E v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = dh[(4 * g + i) / M::KPL][0][(4 * g + i) % M::KPL];
-      store4_nt(drow + 8 * g, v);
-    }
     // dK^T[d, key] += q^T dS   (k = queries)
 #pragma unroll
     for (int stp = 0; stp < STEPS; ++stp) {
@@ -396,10 +369,7 @@ struct Dkdv {
     store(R, buf);
     __syncthreads();
     if (it + 1 < nqb) load(a, b, head, q0 + BQ, R);
-    // The dS tile of (query block q0 / 32, key block wk0 / 32); blocks before
-    // the keys return before using it.
-    E* ds = static_cast<E*>(a.ds) + ds_tile(a, b, head, q0 / 32, wk0 / 32) * kDsTile;
-    block<MASK>(a, buf, q0, wk0, ds, K, acc);
+    block<MASK>(a, buf, q0, wk0, K, acc);
   }
 
   __device__ static void run(const BwdArgs& a, char* lds) {
@@ -729,16 +699,10 @@ hipError_t launch_head_sum(const Shape& s, const float* part, float* out, hipStr
   return hipGetLastError();
 }
 
-size_t ds_tile_bytes(const Shape& s) {
-  const size_t n = static_cast<size_t>((s.S + 31) / 32);
-  return static_cast<size_t>(s.B) * s.h * (n * (n + 1) / 2) * kDsTile * (s.bf16 ? 2 : 4);
-}
-
 hipError_t launch_attn_bwd_dkdv(const Shape& s, const void* q, const void* kn, const void* kp, const void* v,
                                 const float* lse, const float* delta, const void* d_o, const BwdCopies& c,
-                                void* dkv, float* dk_pe_part, void* ds, hipStream_t st) {
+                                void* dkv, float* dk_pe_part, hipStream_t st) {
   BwdArgs a = make_args(s, q, kn, kp, v, lse, delta, d_o);
-  a.ds = ds;
   a.do_shift = c.do_shift;
   a.q8 = static_cast<const uint8_t*>(c.q8);
   a.do8 = static_cast<const uint8_t*>(c.do8);

@@ -22,19 +22,8 @@ struct BwdArgs {
   // dO (and with it delta, dP, dS) enters scaled by 2^g, g = *do_shift
   // (nullptr: g = 0); the kernels scale their outputs by 2^-g.
   const int* do_shift;
-  // dS tiles written by the dK/dV kernel and read by the dq kernel (ds_tile).
-  void* ds;
   int64_t S, plane_k, plane_v, plane_dkv; int B, h; float scale_log2, scale;
 };
-
-// dS, the link between the two kernels: for each (b, head) the 32x32 blocks
-// (query block qb, key block kb <= qb) of dS in the MFMA operand type, block
-// (qb, kb) at index qb (qb + 1) / 2 + kb, each stored [key][query] row-major.
-constexpr int kDsTile = 32 * 32;  // elements per tile
-__device__ __forceinline__ int64_t ds_tile(const BwdArgs& a, int b, int head, int64_t qb, int64_t kb) {
-  const int64_t n = (a.S + 31) / 32;
-  return (static_cast<int64_t>(b) * a.h + head) * (n * (n + 1) / 2) + qb * (qb + 1) / 2 + kb;
-}
 
 // Row padding (elements) of LDS tiles.  `row`: tiles read only with 16-byte
 // row fragments.  `both`: tiles also read with transposing reads; a pitch of
@@ -74,7 +63,7 @@ inline BwdArgs make_args(const Shape& s, const void* q, const void* kn, const vo
   BwdArgs a;
   a.q = q; a.k_nope = kn; a.k_pe = kp; a.v = v; a.lse = lse; a.delta = delta; a.d_o = d_o;
   a.dkv = nullptr; a.dk_pe_part = nullptr; a.dq = nullptr;
-  a.q8 = nullptr; a.do8 = nullptr; a.qsc = nullptr; a.osc = nullptr; a.do_shift = nullptr; a.ds = nullptr;
+  a.q8 = nullptr; a.do8 = nullptr; a.qsc = nullptr; a.osc = nullptr; a.do_shift = nullptr;
   a.S = s.S; a.B = static_cast<int>(s.B); a.h = s.h;
   a.plane_k = s.T * s.h * s.d_nope;
   a.plane_v = s.T * s.h * s.d_v;

@@ -45,15 +45,15 @@ struct BwdCopies {
 // delta = rowsum(dO * o) and, for bfloat16 inputs, the copies above.
 hipError_t launch_bwd_prep(const Shape& s, const float* o, const void* q, const void* d_o, const void* k_pe,
                            float* delta, const BwdCopies& c, hipStream_t st);
-// Bytes of the dS tiles the dK/dV kernel writes for the dq kernel (every
-// causal 32x32 block of every head, fp16 for bfloat16 inputs, else fp32).
-size_t ds_tile_bytes(const Shape& s);
 hipError_t launch_attn_bwd_dkdv(const Shape& s, const void* q, const void* k_nope,
                                 const void* k_pe, const void* v, const float* lse,
                                 const float* delta, const void* d_o, const BwdCopies& c, void* dkv,
-                                float* dk_pe_part, void* ds, hipStream_t st);
-hipError_t launch_attn_bwd_dq(const Shape& s, const void* k_nope, const void* k_pe, const void* ds,
-                              const int* do_shift, float* dq, hipStream_t st);
+                                float* dk_pe_part, hipStream_t st);
+// dq, recomputing P and dS from lse and delta.  q, k_pe, d_o: the fp16 copies
+// (bfloat16 inputs) or the float32 inputs; k_nope, v: their first plane.
+hipError_t launch_attn_bwd_dq(const Shape& s, const void* q, const void* k_nope, const void* k_pe, const void* v,
+                              const float* lse, const float* delta, const void* d_o, const int* do_shift, float* dq,
+                              hipStream_t st);
 hipError_t launch_head_sum(const Shape& s, const float* part, float* out, hipStream_t st);
 // dkv: [T, h, d_nope + d_v] as bf16 hi/lo planes (bf16 inputs) or one fp32 plane.
 hipError_t launch_fold_dl(const Shape& s, const void* dkv, const void* w, float* dL, hipStream_t st);

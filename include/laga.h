@@ -165,11 +165,12 @@ laga_status laga_absorbed_fwd(const laga_dims* dims, const void* q, const float*
                               float* acc, float* o, float* lse, void* stream);
 
 /*
- * Workspace bytes laga_attn_bwd needs for these dims (0 if invalid).  The
- * largest part holds dS for every causal 32x32 block of every local head,
- * passed from the dK/dV kernel to the dq kernel: about B * h * S^2 bytes for
- * LAGA_BF16 (fp16 elements), twice that for LAGA_F32; 4.3 GB at S = 16384,
- * h = 16.
+ * Workspace bytes laga_attn_bwd needs for these dims (0 if invalid).  It grows
+ * linearly with the token count B * S (no S x S quantity is ever stored: both
+ * attention-backward kernels rebuild the probabilities from lse): for
+ * LAGA_BF16 at the V3 head dims about 2.2 KB per token and local head plus
+ * 4.2 KB per token, and a fixed part for the dW_kv_b partial sums (at most
+ * about 70 MB) -- 0.66 GiB at S = 16384, h = 16 and 4.9 GiB at S = 131072.
  */
 size_t laga_attn_bwd_workspace_bytes(const laga_dims* dims);
 

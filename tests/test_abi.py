@@ -141,20 +141,18 @@ def test_workspace_grows_with_sequence(lib):
     assert lib.laga_attn_bwd_workspace_bytes(ctypes.byref(tiny())) > 0
 
 
-def _ds_tile_bytes(B, S, h, elem):
-    n = (S + 31) // 32                  # 32-query / 32-key blocks
-    return B * h * n * (n + 1) // 2 * 32 * 32 * elem   # every causal block of every local head
-
-
-def test_workspace_holds_the_ds_tiles(lib):
-    # The backward hands dS from the dK/dV kernel to the dq kernel as one tile
-    # per causal 32x32 block (fp16 for bf16 inputs, fp32 for f32 inputs), so
-    # the workspace grows with S^2 by at least that much.
-    for B, S in ((1, 1000), (2, 4096)):
-        d = v3(B=B, S=S)
-        assert lib.laga_attn_bwd_workspace_bytes(ctypes.byref(d)) >= _ds_tile_bytes(B, S, 16, 2)
-    small = lib.laga_attn_bwd_workspace_bytes(ctypes.byref(v3(S=2048)))
-    large = lib.laga_attn_bwd_workspace_bytes(ctypes.byref(v3(S=4096)))
-    assert large - small >= _ds_tile_bytes(1, 4096, 16, 2) - _ds_tile_bytes(1, 2048, 16, 2)
+def test_workspace_is_linear_in_the_sequence(lib):
+    # No S x S quantity is stored: the workspace is an affine function of the
+    # token count (a per-token part plus the fixed dW_kv_b partial sums), far
+    # below the fp16 score matrix of a single head once S is large.
+    def ws(S, B=1, **kw):
+        return lib.laga_attn_bwd_workspace_bytes(ctypes.byref(v3(S=S, B=B, **kw)))
+    a, b, c = ws(8192), ws(16384), ws(32768)
+    per_token = (c - b) / 16384
+    assert abs((b - a) / 8192 - per_token) <= 1e-3 * per_token
+    assert ws(131072) < 6 * 2**30                       # 4.9 GiB at S = 128K (16 local heads)
+    assert ws(131072) < 131072 * 131072 * 2 / 4         # a quarter of one head's fp16 score matrix
+    assert ws(16384) < 0.7 * 2**30
+    assert ws(4096, B=4) == ws(16384) or abs(ws(4096, B=4) - ws(16384)) < 2**20  # only the token count matters
     t = tiny(S=300)
-    assert lib.laga_attn_bwd_workspace_bytes(ctypes.byref(t)) >= _ds_tile_bytes(1, 300, 2, 4)
+    assert lib.laga_attn_bwd_workspace_bytes(ctypes.byref(t)) > 0
