@@ -1,6 +1,6 @@
 // C ABI of the LAGA per-rank attention path: argument checks, workspace
 // carving and kernel sequencing.  Declarations and contracts: include/laga.h.
-#include "../../include/laga.h"
+#include "laga.h"
 
 #include "launch.hpp"
 
