@@ -9,21 +9,26 @@
 //           of the W_kv_b gradient [LAGA §5.2]); the reduction over t is split
 //           into chunks summed by a second, deterministic kernel.
 //
-// One kernel template serves all three: a 128x128 output tile per 256-thread
-// workgroup (four wavefronts in 2x2, each 64x64 = 2x2 MFMA atoms of 32x32),
-// K staged through double-buffered LDS 32 at a time, one barrier per step.
-// Each operand slab moves global -> registers -> LDS in 16-byte chunks along
-// the operand's contiguous axis:
+// Two kernel templates, both with a (64 TM) x (64 TN) output tile per
+// 256-thread workgroup (four wavefronts in 2x2, each TM x TN MFMA atoms of
+// 32x32) and K taken 32 at a time, one barrier per step:
+//  * gemm_dma_kernel (every bf16 product): operand slabs go from global memory
+//    straight into a ring of LDS stages (no staging registers); the fp32
+//    normalised latent of the up-projection (and the absorbed form's fp32
+//    accumulator) is split into bf16 hi + lo as it is read from LDS.  Short
+//    steps (K = 512 for the up-projection) make load latency the limit, so
+//    the tiles are small enough for 2-3 workgroups per CU.
+//  * gemm_kernel (the float32 test dims): slabs move global -> registers ->
+//    LDS, one step ahead.
+// Operand orientation:
 //   KC operands (k contiguous in memory) land as LDS rows [row][k] and are
 //      read with 16-byte fragment loads;
 //   RC operands (row contiguous: the k axis strides memory) land as [k][row]
 //      and 16-bit fragments come from gfx950's transposing LDS read.
 // Operands are stored as NS planes of the MFMA element type (x ~= sum of the
-// planes).  bf16 planes are written by the producing kernels, except the
-// normalised latent of the up-projection, which arrives in fp32 and is split
-// into bf16 hi + lo while it is staged.  The product keeps the term pairs
-// (sa, sb) with sa + sb < max(NSA, NSB), which makes the bf16 GEMM accurate to
-// about 2^-16 relative.
+// planes), written by the producing kernels.  The product keeps the term
+// pairs (sa, sb) with sa + sb < max(NSA, NSB), which makes the bf16 GEMM
+// accurate to about 2^-16 relative.
 #include <type_traits>
 
 #include "attn_common.hpp"
@@ -32,7 +37,7 @@
 namespace laga {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 32;
+constexpr int BK = 32;
 constexpr int kThreads = 256;
 
 // A GEMM operand in global memory: element (row r, k) of plane s at
@@ -52,9 +57,13 @@ struct SlabT {
   typedef typename M::elem E;
   typedef typename M::frag F;
   static constexpr int EPC = 16 / sizeof(E);  // elements per 16-byte chunk
+  // Conversions on the way into LDS: fp32 -> 16-bit (NS == 2: hi + lo planes;
+  // NS == 1: one rounded plane), or bf16 -> fp16 (one plane).
   static constexpr bool SPLIT = !std::is_same<Src, E>::value;
-  static_assert(!SPLIT || (std::is_same<Src, float>::value && NS == 2 && EPC == 8),
-                "only fp32 -> 16-bit hi/lo splitting");
+  static constexpr bool FROM_F32 = std::is_same<Src, float>::value;
+  static_assert(!SPLIT || (EPC == 8 && (FROM_F32 || (std::is_same<Src, bf16_t>::value && NS == 1 &&
+                                                     std::is_same<E, half_t>::value))),
+                "fp32 -> 16-bit planes or bf16 -> fp16 only");
   static constexpr int LD = KC ? BK + EPC : ROWS + (sizeof(E) == 2 ? 32 : 4);  // LDS pitch, elements
   static constexpr int PLANE = (KC ? ROWS : BK) * LD;
   static constexpr int BYTES = NS * PLANE * static_cast<int>(sizeof(E));
@@ -62,7 +71,7 @@ struct SlabT {
   static constexpr int PER = CHUNKS / kThreads;
   static_assert(CHUNKS % kThreads == 0, "whole chunks per thread");
   static constexpr int NP = SPLIT ? 1 : NS;  // planes read from memory
-  static constexpr int WORDS = SPLIT ? 2 : 1;  // 16-byte words per chunk read
+  static constexpr int WORDS = SPLIT && FROM_F32 ? 2 : 1;  // 16-byte words per chunk read
 
   u32x4 reg[NP][PER][WORDS];
 
@@ -76,21 +85,30 @@ struct SlabT {
     }
   }
 
+  // Buffer loads: one descriptor per plane whose range ends with the last
+  // row (KC) or k-row (RC) of the slab that exists, so chunks past it read as
+  // zero with no branch.  KC operands need K to be a multiple of BK; rows of
+  // an RC slab past R read neighbouring data, which only reaches output rows
+  // or columns that are never stored.
   __device__ void load(const Operand<Src>& op, int64_t row0, int64_t k0) {
+    constexpr int es = sizeof(Src);
+    const Src* base = op.p + (KC ? row0 * op.ld + k0 : k0 * op.ld + row0);
+    int64_t lim = KC ? op.R - row0 : op.K - k0;
+    if (lim > (KC ? ROWS : BK)) lim = KC ? ROWS : BK;
+    const int nbytes = static_cast<int>(lim * op.ld) * es;
+    const int ld_b = static_cast<int>(op.ld) * es;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      int r, k;
-      chunk_pos(i * kThreads + static_cast<int>(threadIdx.x), r, k);
-      const int64_t gr = row0 + r, gk = k0 + k;
-      // KC: rows are whole; K is a multiple of the chunk.  RC: R is a multiple of the chunk.
-      const bool ok = gr < op.R && gk < op.K;
-      const Src* src = op.p + (KC ? gr * op.ld + gk : gk * op.ld + gr);
+    for (int s = 0; s < NP; ++s) {
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<Src*>(base + s * op.plane), 0, nbytes, 0x00020000);
 #pragma unroll
-      for (int s = 0; s < NP; ++s)
+      for (int i = 0; i < PER; ++i) {
+        int r, k;
+        chunk_pos(i * kThreads + static_cast<int>(threadIdx.x), r, k);
+        const int off = KC ? r * ld_b + k * es : k * ld_b + r * es;
 #pragma unroll
-        for (int w = 0; w < WORDS; ++w)
-          reg[s][i][w] = ok ? *reinterpret_cast<const u32x4*>(src + s * op.plane + w * (16 / sizeof(Src)))
-                            : u32x4{0u, 0u, 0u, 0u};
+        for (int w = 0; w < WORDS; ++w) reg[s][i][w] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16 * w, 0, 0);
+      }
     }
   }
 
@@ -115,6 +133,21 @@ struct SlabT {
         }
         *reinterpret_cast<u32x4*>(dst) = hw;
         *reinterpret_cast<u32x4*>(dst + PLANE) = lw;
+      } else if constexpr (SPLIT && !FROM_F32) {  // bf16 -> fp16, exact within fp16's range
+        const u16x8 x = __builtin_bit_cast(u16x8, reg[0][i][0]);
+        half8 h;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) h[j] = static_cast<half_t>(bf16_to_f32(x[j]));
+        *reinterpret_cast<half8*>(dst) = h;
+      } else if constexpr (SPLIT && NS == 1) {  // fp32 -> one rounded 16-bit plane
+        E part[EPC];
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          const f32x4 x = __builtin_bit_cast(f32x4, reg[0][i][w]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) part[4 * w + j] = M::from_f32(x[j]);
+        }
+        *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<u32x4*>(part);
       } else if constexpr (SPLIT) {
         E part[NS][EPC];
 #pragma unroll
@@ -155,18 +188,22 @@ struct SlabT {
 // n = i*C + c -> k_nope[t,i,c] or v[t,i,c-d_nope].  With NS == 2 (fp16
 // storage) the value x is written as hi = fp16(x) in a first plane and the
 // rest as an e4m3 byte of (x - hi) * 2^kLoShift in a byte plane after it.
-template <class KvT, int NS>
+template <class KvT, int NS, int DN, int DV>
 struct EpiKvUp {
   static_assert(NS == 1 || sizeof(KvT) == 2, "the split form stores fp16 + e4m3");
   static constexpr bool TRANS = true;  // takes 4 consecutive n of one row m
-  KvT* kn; KvT* v; int64_t M; int N, C, dn, dv, h; int64_t plane_k, plane_v;
-  // n .. n+3 lie in one head and one part (C, dn multiples of 4).
+  static constexpr int C = DN + DV;
+  KvT* kn; KvT* v; int64_t M; int N, h; int64_t plane_k, plane_v;
+  // n .. n+3 lie in one head and one part (C, DN multiples of 4).
   __device__ void store4(int64_t m, int n, f32x4 val, int /*z*/) const {
     if (m >= M || n >= N) return;
-    const int i = n / C, c = n - i * C;
-    const bool isk = c < dn;
-    const int64_t e = isk ? (m * h + i) * dn + c : (m * h + i) * dv + (c - dn);
-    KvT* base = isk ? kn : v;
+    const int i = n / C, c = n % C;
+    // Two explicit paths rather than a selected pointer: selecting between
+    // the two struct fields made the compiler index a stack copy of them.
+    if (c < DN) put(kn, plane_k, (m * h + i) * DN + c, val);
+    else put(v, plane_v, (m * h + i) * DV + (c - DN), val);
+  }
+  __device__ static void put(KvT* base, int64_t plane, int64_t e, f32x4 val) {
     KvT hi[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) hi[j] = static_cast<KvT>(val[j]);
@@ -176,7 +213,7 @@ struct EpiKvUp {
       *reinterpret_cast<f32x4*>(base + e) = *reinterpret_cast<const f32x4*>(hi);
     if constexpr (NS == 2) {
       constexpr float sc = static_cast<float>(1 << kLoShift);
-      uint8_t* lo = reinterpret_cast<uint8_t*>(base + (isk ? plane_k : plane_v));
+      uint8_t* lo = reinterpret_cast<uint8_t*>(base + plane);
       *reinterpret_cast<uint32_t*>(lo + e) =
           pack_e4m3x4((val[0] - static_cast<float>(hi[0])) * sc, (val[1] - static_cast<float>(hi[1])) * sc,
                       (val[2] - static_cast<float>(hi[2])) * sc, (val[3] - static_cast<float>(hi[3])) * sc);
@@ -213,12 +250,14 @@ struct EpiStore {  // out[z * chunk_stride + m * ld + n] (z: batch * chunks + K 
 // of tiles in x-fastest order: the N tiles that share an A row block (and the
 // M tiles that share a B block) then run on the same XCD and read those rows
 // from HBM once instead of once per XCD.
-template <class M, class SA, class SB, class EPI>
-__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(Operand<typename SA::Src_t> A,
-                                                           Operand<typename SB::Src_t> B, EPI epi,
-                                                           int64_t k_chunk, int64_t K, int nchunks, int gx, int gy,
-                                                           int gz) {
+template <class M, class SA, class SB, class EPI, int TM, int TN>
+__global__ __launch_bounds__(kThreads, TM * TN > 4 ? 1 : 2) void gemm_kernel(Operand<typename SA::Src_t> A,
+                                                                            Operand<typename SB::Src_t> B, EPI epi,
+                                                                            int64_t k_chunk, int64_t K, int nchunks,
+                                                                            int gx, int gy, int gz) {
   typedef typename M::elem E;
+  constexpr int BM = 64 * TM, BN = 64 * TN;
+  static_assert(SA::ROWS == BM && SB::ROWS == BN, "slab rows match the tile");
   constexpr int STAGE = SA::BYTES + SB::BYTES;
   __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
 
@@ -237,44 +276,43 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(Operand<typename SA::
   const int64_t kbeg = static_cast<int64_t>(chunk) * k_chunk;
   const int64_t kend = (kbeg + k_chunk < K) ? kbeg + k_chunk : K;
 
-  f32x16 acc[2][2];
+  f32x16 acc[TM][TN];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < TM; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < TN; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-  // Two register stages of operand slabs in flight: the loads for step k+2
-  // are issued while step k computes, so about two steps of products cover
-  // the global-memory latency.  The loop is unrolled by two so that each
-  // stage keeps its own registers.
-  typename SA::Slab sa0, sa1;
-  typename SB::Slab sb0, sb1;
+  // One register stage of operand slabs in flight: the loads for step k + 1
+  // are issued right after the barrier of step k and stored to the other LDS
+  // buffer at the start of step k + 1, so one step of products (TM TN
+  // products per k16 and term pair) covers the global-memory latency.
+  typename SA::Slab sa;
+  typename SB::Slab sb;
   constexpr int NSA = SA::Slab::NS_, NSB = SB::Slab::NS_;
   constexpr int NSMAX = NSA > NSB ? NSA : NSB;
-
   auto compute = [&](const E* as, const E* bs) {
 #pragma unroll
     for (int kk = 0; kk < BK; kk += M::K) {
-      typename M::frag af[NSA][2], bfr[NSB][2];
+      typename M::frag af[NSA][TM], bfr[NSB][TN];
 #pragma unroll
       for (int s = 0; s < NSA; ++s)
 #pragma unroll
-        for (int a = 0; a < 2; ++a) af[s][a] = SA::Slab::frag(as, s, wm * 64 + a * 32, kk);
+        for (int a = 0; a < TM; ++a) af[s][a] = SA::Slab::frag(as, s, wm * 32 * TM + a * 32, kk);
 #pragma unroll
       for (int s = 0; s < NSB; ++s)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) bfr[s][b] = SB::Slab::frag(bs, s, wn * 64 + b * 32, kk);
+        for (int b = 0; b < TN; ++b) bfr[s][b] = SB::Slab::frag(bs, s, wn * 32 * TN + b * 32, kk);
 #pragma unroll
       for (int s1 = 0; s1 < NSA; ++s1)
 #pragma unroll
         for (int s2 = 0; s2 < NSB; ++s2) {
           if (s1 + s2 >= NSMAX) continue;
 #pragma unroll
-          for (int a = 0; a < 2; ++a)
+          for (int a = 0; a < TM; ++a)
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
+            for (int b = 0; b < TN; ++b) {
               // EPI::TRANS: the atom holds C^T (rows n, columns m).
               if constexpr (EPI::TRANS) acc[a][b] = M::mma(bfr[s2][b], af[s1][a], acc[a][b]);
               else acc[a][b] = M::mma(af[s1][a], bfr[s2][b], acc[a][b]);
@@ -283,51 +321,50 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(Operand<typename SA::
     }
   };
   // One step: publish the slabs of step k0 (held in sa/sb) into LDS buffer
-  // `buf`, refill sa/sb with step k0 + 2*BK, compute step k0.
-  auto step = [&](int64_t k0, int buf, typename SA::Slab& sa, typename SB::Slab& sb) {
+  // `buf`, refill sa/sb with step k0 + BK, compute step k0.  A buffer is
+  // written two steps after it was read; the barrier of the step in between
+  // orders the two.
+  auto step = [&](int64_t k0, int buf) {
     E* as = reinterpret_cast<E*>(lds + buf * STAGE);
     E* bs = reinterpret_cast<E*>(lds + buf * STAGE + SA::BYTES);
     sa.store(as);
     sb.store(bs);
-    __syncthreads();  // also orders the reads of this buffer two steps ago before the stores above
-    if (k0 + 2 * BK < kend) {
-      sa.load(A, m0, k0 + 2 * BK);
-      sb.load(B, n0, k0 + 2 * BK);
+    __syncthreads();
+    if (k0 + BK < kend) {
+      sa.load(A, m0, k0 + BK);
+      sb.load(B, n0, k0 + BK);
     }
     compute(as, bs);
   };
 
   if (kbeg < kend) {
-    sa0.load(A, m0, kbeg);
-    sb0.load(B, n0, kbeg);
+    sa.load(A, m0, kbeg);
+    sb.load(B, n0, kbeg);
   }
-  if (kbeg + BK < kend) {
-    sa1.load(A, m0, kbeg + BK);
-    sb1.load(B, n0, kbeg + BK);
-  }
+  // Unrolled by two so that each step names its buffer as a constant.
   for (int64_t k0 = kbeg; k0 < kend; k0 += 2 * BK) {
-    step(k0, 0, sa0, sb0);
-    if (k0 + BK < kend) step(k0 + BK, 1, sa1, sb1);
+    step(k0, 0);
+    if (k0 + BK < kend) step(k0 + BK, 1);
   }
   // C[r]: row 8*(r/4) + 4*(lane/32) + r%4 of the atom, column lane%32.
   const int lane = threadIdx.x % kWave;
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < TM; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < TN; ++b) {
       if constexpr (EPI::TRANS) {
-        const int64_t m = m0 + wm * 64 + a * 32 + (lane % 32);
+        const int64_t m = m0 + wm * 32 * TM + a * 32 + (lane % 32);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int n = static_cast<int>(n0 + wn * 64 + b * 32 + 8 * g + 4 * (lane / 32));
+          const int n = static_cast<int>(n0 + wn * 32 * TN + b * 32 + 8 * g + 4 * (lane / 32));
           const f32x4 v4 = {acc[a][b][4 * g], acc[a][b][4 * g + 1], acc[a][b][4 * g + 2], acc[a][b][4 * g + 3]};
           epi.store4(m, n, v4, bz);
         }
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t m = m0 + wm * 64 + a * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
-          const int n = static_cast<int>(n0 + wn * 64 + b * 32 + (lane % 32));
+          const int64_t m = m0 + wm * 32 * TM + a * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+          const int n = static_cast<int>(n0 + wn * 32 * TN + b * 32 + (lane % 32));
           epi(m, n, acc[a][b][r], bz);
         }
       }
@@ -335,29 +372,353 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(Operand<typename SA::
 }
 
 // Operand description: MFMA type, planes, orientation, rows per tile, source element.
-template <class M, int NS, bool KC, int ROWS, class Src>
+template <class M, int NS, bool KC_, int ROWS_, class Src>
 struct Side {
-  struct Slab : SlabT<M, NS, KC, ROWS, Src> { static constexpr int NS_ = NS; };
+  struct Slab : SlabT<M, NS, KC_, ROWS_, Src> { static constexpr int NS_ = NS; };
   typedef Src Src_t;
   static constexpr int BYTES = Slab::BYTES;
+  static constexpr int ROWS = ROWS_;
+  static constexpr bool KC = KC_;
 };
 
-template <class M, class SA, class SB, class EPI>
+// Launch with (64 TM) x (64 TN) tiles; SA / SB must have 64 TM / 64 TN rows.
+template <class M, int TM, int TN, class SA, class SB, class EPI>
 hipError_t run_gemm(Operand<typename SA::Src_t> A, Operand<typename SB::Src_t> B, EPI epi, int64_t Mrows,
                     int64_t Ncols, int64_t K, int chunks, hipStream_t st, int batches = 1) {
+  if ((SA::KC || SB::KC) && K % BK != 0) return hipErrorInvalidValue;  // KC slabs take whole BK steps
   const int64_t per = ((K + chunks - 1) / chunks + BK - 1) / BK * BK;
   const int nchunks = static_cast<int>((K + per - 1) / per);
-  const int gx = static_cast<int>((Ncols + BN - 1) / BN), gy = static_cast<int>((Mrows + BM - 1) / BM),
-            gz = nchunks * batches;
-  hipLaunchKernelGGL((gemm_kernel<M, SA, SB, EPI>), dim3(static_cast<unsigned>(gx * gy * gz)), dim3(kThreads), 0, st,
-                     A, B, epi, per, K, nchunks, gx, gy, gz);
+  const int gx = static_cast<int>((Ncols + 64 * TN - 1) / (64 * TN)),
+            gy = static_cast<int>((Mrows + 64 * TM - 1) / (64 * TM)), gz = nchunks * batches;
+  hipLaunchKernelGGL((gemm_kernel<M, SA, SB, EPI, TM, TN>), dim3(static_cast<unsigned>(gx * gy * gz)),
+                     dim3(kThreads), 0, st, A, B, epi, per, K, nchunks, gx, gy, gz);
   return hipGetLastError();
 }
 
-// Number of K chunks for the W_kv_b gradient so that about 1024 workgroups run.
+// ------------------------------------------------------- DMA-fed GEMM kernel
+// For bf16 matrix-core products (every GEMM of the path except the float32
+// test dims).  With K = 512 (the up-projection) a 32-wide k step holds only a
+// few hundred cycles of products per wavefront, too few to hide the latency
+// of the next step's global loads when they pass through registers.  Here the
+// operand slabs go from global memory straight into LDS (buffer loads with an
+// LDS destination: no staging registers, no LDS store instructions), NST - 1
+// steps ahead, into a ring of NST stages.  Each wavefront issues the same
+// number of 1 KB loads per stage, so waiting for a stage is one
+// s_waitcnt vmcnt(N) before the step's barrier.
+//
+// Operand layouts in a stage (16-byte slots XOR-swizzled so that the reads
+// below touch every LDS bank once per 16 or 32 lanes):
+//   DKC<NP, bf16>:  ROWS lines x 64 B (k contiguous), slot c of line r at c ^ ((r >> 2) & 3)
+//   DKC<1, float>:  ROWS lines x 128 B, slot c of line r at c ^ ((r >> 1) & 7); the
+//                   fp32 values become bf16 hi + lo terms as they are read
+//   DRC<NP>:        BK k-lines x ROWS * 2 B (rows contiguous), slot c of k-line k at
+//                   c ^ 4 (k % 4), read with transposing reads
+// A slot's source address follows from its LDS position, so the swizzle costs
+// nothing on the load side.
+
+// 16 bytes per lane from `rs` (byte offset voff + soff) to lds + 16 * lane.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, void* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds), 16, voff, soff, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) with expcnt and lgkmcnt left at their maximum.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// k-contiguous operand: NP planes of Src, ROWS rows per tile.
+template <int NP_, class Src, int ROWS_>
+struct DKC {
+  static constexpr int ROWS = ROWS_, NP = NP_;
+  static constexpr bool F32 = std::is_same<Src, float>::value;
+  static_assert(!F32 || NP == 1, "one fp32 plane, split when read");
+  static constexpr int NT = F32 ? 2 : NP;  // bf16 terms per element
+  static constexpr int LINE = BK * static_cast<int>(sizeof(Src));  // 64 or 128 bytes
+  static constexpr int SPL = LINE / 16;
+  static constexpr int PLANE = ROWS * LINE;
+  static constexpr int BYTES = NP * PLANE;
+  static constexpr int SLOTS = PLANE / 16;
+  static_assert(SLOTS % (4 * kWave) == 0, "whole 1 KB loads for every wavefront");
+  static constexpr int IPW = SLOTS / (4 * kWave);  // loads per wavefront and plane
+  __device__ static int swz(int line) { return F32 ? (line >> 1) & 7 : (line >> 2) & 3; }
+  // Source byte offset (within the step's slab) of load i of wavefront w for this lane.
+  __device__ static int voff(int i, int w, int lane, int ld_bytes) {
+    const int q = (i * 4 + w) * kWave + lane, line = q / SPL, c = (q % SPL) ^ swz(line);
+    return line * ld_bytes + c * 16;
+  }
+  // Lines of the step's slab that exist: rows past R read as zero.
+  __device__ static int lines(int64_t r_left, int64_t /*k_left*/) {
+    return static_cast<int>(r_left < ROWS ? r_left : ROWS);
+  }
+  // Per-lane byte offsets of the atom at row 32 * lane-independent offset, k step kk:
+  // bf16: one 16-byte slot per term; fp32: two slots.
+  struct Lane { int o[2][2]; };  // [kk / 16][half]
+  __device__ static Lane lane_offsets(int row0) {
+    const int lane = threadIdx.x % kWave, hf = lane / 32, line = row0 + lane % 32;
+    Lane L;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if constexpr (F32) {
+        const int c0 = (16 * s + 8 * hf) / 4;
+        L.o[s][0] = line * LINE + ((c0) ^ swz(line)) * 16;
+        L.o[s][1] = line * LINE + ((c0 + 1) ^ swz(line)) * 16;
+      } else {
+        L.o[s][0] = line * LINE + (((16 * s + 8 * hf) / 8) ^ swz(line)) * 16;
+        L.o[s][1] = 0;
+      }
+    }
+    return L;
+  }
+  // The bf16 terms of the fragment of atom `a` (rows row0 + 32 a ..) at k step s.
+  __device__ static void frag(const char* st, const Lane& L, int a, int s, u16x8* out) {
+    const char* base = st + a * 32 * LINE;
+    if constexpr (F32) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(base + L.o[s][0]);
+      const f32x4 y = *reinterpret_cast<const f32x4*>(base + L.o[s][1]);
+      uint32_t h[4], l[4];
+      split_bf16_pair(x[0], x[1], h[0], l[0]);
+      split_bf16_pair(x[2], x[3], h[1], l[1]);
+      split_bf16_pair(y[0], y[1], h[2], l[2]);
+      split_bf16_pair(y[2], y[3], h[3], l[3]);
+      out[0] = __builtin_bit_cast(u16x8, u32x4{h[0], h[1], h[2], h[3]});
+      out[1] = __builtin_bit_cast(u16x8, u32x4{l[0], l[1], l[2], l[3]});
+    } else {
+#pragma unroll
+      for (int p = 0; p < NP; ++p) out[p] = *reinterpret_cast<const u16x8*>(base + p * PLANE + L.o[s][0]);
+    }
+  }
+  static constexpr bool KC = true;
+};
+
+// Row-contiguous operand (k strides memory): NP bf16 planes, ROWS rows per tile.
+template <int NP_, int ROWS_>
+struct DRC {
+  static constexpr int ROWS = ROWS_, NP = NP_, NT = NP_;
+  static constexpr int LINE = ROWS * 2;  // one k-line
+  static constexpr int SPL = LINE / 16;
+  static_assert(LINE % 256 == 0, "k-lines span whole bank windows");
+  static constexpr int PLANE = BK * LINE;
+  static constexpr int BYTES = NP * PLANE;
+  static constexpr int SLOTS = PLANE / 16;
+  static_assert(SLOTS % (4 * kWave) == 0, "whole 1 KB loads for every wavefront");
+  static constexpr int IPW = SLOTS / (4 * kWave);
+  __device__ static int swz(int kl) { return 4 * (kl & 3); }
+  __device__ static int voff(int i, int w, int lane, int ld_bytes) {
+    const int q = (i * 4 + w) * kWave + lane, kl = q / SPL, c = (q % SPL) ^ swz(kl);
+    return kl * ld_bytes + c * 16;
+  }
+  __device__ static int lines(int64_t /*r_left*/, int64_t k_left) {
+    return static_cast<int>(k_left < BK ? k_left : BK);
+  }
+  // Transposing read of rows (k-lines) k0 + 8 hf + s/4 (+4) and columns
+  // n0 + 16 (g % 2) + 4 (s % 4) of a swizzled stage (lane = 16 g + s): the
+  // per-lane byte offset for the atom at column n0 (a multiple of 32);
+  // k steps add 16 lines.
+  struct Lane { int o[8]; };  // per atom of the wavefront (up to 8)
+  template <int NA>
+  __device__ static Lane lane_offsets(int col0) {
+    static_assert(NA <= 8, "atoms per wavefront");
+    const int lane = threadIdx.x % kWave, g = lane / 16, s = lane % 16, hf = lane / 32;
+    const int kl = 8 * hf + s / 4;  // k-line within the step (% 4 == (s / 4) % 4)
+    Lane L;
+#pragma unroll
+    for (int a = 0; a < NA; ++a) {
+      const int chunk = (col0 + 32 * a) / 8 + 2 * (g % 2) + (s % 4) / 2;
+      L.o[a] = kl * LINE + (chunk ^ swz(kl)) * 16 + 8 * (s % 2);
+    }
+    return L;
+  }
+  __device__ static void frag(const char* st, const Lane& L, int a, int s, u16x8* out) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const char* b = st + p * PLANE + L.o[a] + s * 16 * LINE;
+      const s16x4 x = ds_read_tr16(b);
+      const s16x4 y = ds_read_tr16(b + 4 * LINE);
+      typedef short s16x8 __attribute__((ext_vector_type(8)));
+      out[p] = __builtin_bit_cast(u16x8, s16x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]});
+    }
+  }
+  static constexpr bool KC = false;
+};
+
+// C[m, n] = sum_k A[m, k] B[n, k] over the term pairs (ta, tb) with
+// ta + tb < max(NT_A, NT_B), bf16 MFMAs, (64 TM) x (64 TN) tiles, NST stages.
+template <class OA, class OB, class EPI, int TM, int TN, int NST, int OCC>
+__global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(Operand<bf16_t> A16, Operand<float> A32,
+                                                                 Operand<bf16_t> B, EPI epi, int64_t k_chunk,
+                                                                 int64_t K, int nchunks, int gx, int gy, int gz) {
+  static_assert(OA::ROWS == 64 * TM && OB::ROWS == 64 * TN, "operand rows match the tile");
+  constexpr int STAGE = OA::BYTES + OB::BYTES;
+  constexpr int IPS = OA::IPW * OA::NP + OB::IPW * OB::NP;  // loads per wavefront and stage
+  static_assert((NST - 2) * IPS < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) char lds[NST * STAGE];
+  constexpr bool A_F32 = OA::KC && OA::NT == 2 && OA::NP == 1;  // fp32 A (split when read)
+
+  const int total = gx * gy * gz;
+  const int id = static_cast<int>(blockIdx.x);
+  const int tile = total % 8 == 0 ? (id % 8) * (total / 8) + id / 8 : id;
+  const int bx = tile % gx, by = (tile / gx) % gy, bz = tile / (gx * gy);
+  const int lane = threadIdx.x % kWave;
+  const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+  const int wm = wv / 2, wn = wv % 2;
+  const int64_t m0 = static_cast<int64_t>(by) * 64 * TM;
+  const int64_t n0 = static_cast<int64_t>(bx) * 64 * TN;
+  const int chunk = bz % nchunks, batch = bz / nchunks;
+  const int64_t kbeg = static_cast<int64_t>(chunk) * k_chunk;
+  const int64_t kend = (kbeg + k_chunk < K) ? kbeg + k_chunk : K;
+  const int nsteps = static_cast<int>((kend - kbeg + BK - 1) / BK);
+
+  // Operand bases at the tile's first row / k, and per-lane source offsets.
+  const int es_a = A_F32 ? 4 : 2;
+  const int64_t lda = A_F32 ? A32.ld : A16.ld, Ra = A_F32 ? A32.R : A16.R;
+  const char* abase = A_F32 ? reinterpret_cast<const char*>(A32.p + batch * A32.zstride)
+                            : reinterpret_cast<const char*>(A16.p + batch * A16.zstride);
+  abase += (OA::KC ? m0 * lda + kbeg : kbeg * lda + m0) * es_a;
+  const int64_t aplane = (A_F32 ? 0 : A16.plane) * es_a;
+  const char* bbase = reinterpret_cast<const char*>(B.p + batch * B.zstride) +
+                      (OB::KC ? n0 * B.ld + kbeg : kbeg * B.ld + n0) * 2;
+  const int64_t bplane = B.plane * 2;
+  const int lda_b = static_cast<int>(lda) * es_a, ldb_b = static_cast<int>(B.ld) * 2;
+  int va[OA::IPW], vb[OB::IPW];
+#pragma unroll
+  for (int i = 0; i < OA::IPW; ++i) va[i] = OA::voff(i, wv, lane, lda_b);
+#pragma unroll
+  for (int i = 0; i < OB::IPW; ++i) vb[i] = OB::voff(i, wv, lane, ldb_b);
+
+  // Issue step `it` (k = kbeg + it BK) into stage `sb`; steps past the end
+  // read zeros (an empty range), so every step issues the same loads.
+  auto issue = [&](int it, char* sb) {
+    const int64_t k0 = static_cast<int64_t>(it) * BK;
+    const int64_t kl = kend - kbeg - k0;
+    const int la = OA::lines(Ra - m0, kl), lb = OB::lines(B.R - n0, kl);
+    const int64_t adv_a = OA::KC ? k0 * es_a : k0 * lda_b, adv_b = OB::KC ? k0 * 2 : k0 * ldb_b;
+#pragma unroll
+    for (int p = 0; p < OA::NP; ++p) {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(abase + p * aplane + adv_a), 0, kl > 0 ? la * lda_b : 0, 0x00020000);
+#pragma unroll
+      for (int i = 0; i < OA::IPW; ++i) dma16(rs, sb + p * OA::PLANE + (i * 4 + wv) * 1024, va[i], 0);
+    }
+#pragma unroll
+    for (int p = 0; p < OB::NP; ++p) {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(bbase + p * bplane + adv_b), 0, kl > 0 ? lb * ldb_b : 0, 0x00020000);
+#pragma unroll
+      for (int i = 0; i < OB::IPW; ++i)
+        dma16(rs, sb + OA::BYTES + p * OB::PLANE + (i * 4 + wv) * 1024, vb[i], 0);
+    }
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+  typename OA::Lane la_off;
+  typename OB::Lane lb_off;
+  if constexpr (OA::KC) la_off = OA::lane_offsets(wm * 32 * TM);
+  else la_off = OA::template lane_offsets<TM>(wm * 32 * TM);
+  if constexpr (OB::KC) lb_off = OB::lane_offsets(wn * 32 * TN);
+  else lb_off = OB::template lane_offsets<TN>(wn * 32 * TN);
+
+  auto compute = [&](const char* st) {
+    const char* as = st;
+    const char* bs = st + OA::BYTES;
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+      u16x8 af[TM][OA::NT], bfr[TN][OB::NT];
+#pragma unroll
+      for (int a = 0; a < TM; ++a) OA::frag(as, la_off, a, s, af[a]);
+#pragma unroll
+      for (int b = 0; b < TN; ++b) OB::frag(bs, lb_off, b, s, bfr[b]);
+      constexpr int NTM = OA::NT > OB::NT ? OA::NT : OB::NT;
+#pragma unroll
+      for (int ta = 0; ta < OA::NT; ++ta)
+#pragma unroll
+        for (int tb = 0; tb < OB::NT; ++tb) {
+          if (ta + tb >= NTM) continue;
+#pragma unroll
+          for (int a = 0; a < TM; ++a)
+#pragma unroll
+            for (int b = 0; b < TN; ++b) {
+              if constexpr (EPI::TRANS) acc[a][b] = MmaBf16::mma(bfr[b][tb], af[a][ta], acc[a][b]);
+              else acc[a][b] = MmaBf16::mma(af[a][ta], bfr[b][tb], acc[a][b]);
+            }
+        }
+    }
+  };
+
+  // Prologue: NST - 1 steps in flight.
+#pragma unroll
+  for (int it = 0; it < NST - 1; ++it) issue(it, lds + it * STAGE);
+  // Unrolled by NST so that every stage offset is a constant.
+  for (int it0 = 0; it0 < nsteps; it0 += NST) {
+#pragma unroll
+    for (int j = 0; j < NST; ++j) {
+      const int it = it0 + j;
+      if (it >= nsteps) break;
+      wait_vmcnt<(NST - 2) * IPS>();  // this wavefront's loads of step `it` have landed
+      __syncthreads();                // so have every wavefront's; stage (it - 1) % NST is free
+      issue(it + NST - 1, lds + ((j + NST - 1) % NST) * STAGE);
+      compute(lds + j * STAGE);
+    }
+  }
+  wait_vmcnt<0>();  // no load into LDS outlives the workgroup
+
+  // C[r]: row 8*(r/4) + 4*(lane/32) + r%4 of the atom, column lane%32.
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b) {
+      if constexpr (EPI::TRANS) {
+        const int64_t m = m0 + wm * 32 * TM + a * 32 + (lane % 32);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = static_cast<int>(n0 + wn * 32 * TN + b * 32 + 8 * g + 4 * (lane / 32));
+          const f32x4 v4 = {acc[a][b][4 * g], acc[a][b][4 * g + 1], acc[a][b][4 * g + 2], acc[a][b][4 * g + 3]};
+          epi.store4(m, n, v4, bz);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t m = m0 + wm * 32 * TM + a * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+          const int n = static_cast<int>(n0 + wn * 32 * TN + b * 32 + (lane % 32));
+          epi(m, n, acc[a][b][r], bz);
+        }
+      }
+    }
+}
+
+// Launch of the DMA kernel: A either 16-bit planes (A16) or one fp32 plane (A32).
+template <class OA, class OB, int TM, int TN, int NST, int OCC, class EPI>
+hipError_t run_gemm_dma(Operand<bf16_t> A16, Operand<float> A32, Operand<bf16_t> B, EPI epi, int64_t Mrows,
+                        int64_t Ncols, int64_t K, int chunks, hipStream_t st, int batches = 1) {
+  if ((OA::KC || OB::KC) && K % BK != 0) return hipErrorInvalidValue;  // k-contiguous slabs take whole steps
+  const int64_t per = ((K + chunks - 1) / chunks + BK - 1) / BK * BK;
+  const int nchunks = static_cast<int>((K + per - 1) / per);
+  const int gx = static_cast<int>((Ncols + 64 * TN - 1) / (64 * TN)),
+            gy = static_cast<int>((Mrows + 64 * TM - 1) / (64 * TM)), gz = nchunks * batches;
+  hipLaunchKernelGGL((gemm_dma_kernel<OA, OB, EPI, TM, TN, NST, OCC>), dim3(static_cast<unsigned>(gx * gy * gz)),
+                     dim3(kThreads), 0, st, A16, A32, B, epi, per, K, nchunks, gx, gy, gz);
+  return hipGetLastError();
+}
+
+// Tiles (in 64-row units) of the W_kv_b gradient GEMM, rows h * C and columns
+// d_kv, for bfloat16 inputs (float32 inputs use 128 x 128).
+constexpr int DW_TM = 2, DW_TN = 2;
+
+// Number of K chunks for the W_kv_b gradient so that about DW_TARGET
+// workgroups run.
+constexpr int DW_TARGET = 512;
 int dw_chunks(const Shape& s) {
-  const int64_t tiles = ((static_cast<int64_t>(s.h) * s.C() + BM - 1) / BM) * ((s.d_kv + BN - 1) / BN);
-  int64_t c = (1024 + tiles - 1) / tiles;
+  const int tm = s.bf16 ? 64 * DW_TM : 128, tn = s.bf16 ? 64 * DW_TN : 128;
+  const int64_t tiles = ((static_cast<int64_t>(s.h) * s.C() + tm - 1) / tm) * ((s.d_kv + tn - 1) / tn);
+  int64_t c = (DW_TARGET + tiles - 1) / tiles;
   const int64_t kmax = (s.T + BK - 1) / BK;
   if (c > kmax) c = kmax;
   if (c < 1) c = 1;
@@ -386,25 +747,31 @@ hipError_t launch_kv_up(const Shape& s, const float* L, const void* w, void* k_n
   const int64_t w0 = static_cast<int64_t>(s.head_lo) * s.C() * s.d_kv;
   const int64_t pk = s.T * s.h * s.d_nope, pv = s.T * s.h * s.d_v;
   Operand<float> A{L, s.d_kv, 0, s.T, s.d_kv};
-  if (s.bf16) {
-    typedef Side<MmaBf16, 2, true, BM, float> SA;
-    typedef Side<MmaBf16, 1, true, BN, bf16_t> SB;
+  if (s.bf16 && s.d_nope == 128 && s.d_v == 128) {
+    // L as bf16 hi + lo (formed as it is read from LDS), W exact in bf16:
+    // K / V to about 2^-16 relative, then stored as split planes or fp16.
+    // 64 x 256 tiles, two stages, three workgroups per CU: with K = 512 the
+    // steps are short and the loads of the other workgroups cover each
+    // one's latency (measured best of 1-3 workgroups per CU, 2-4 stages).
+    typedef DKC<1, float, 64> OA;
+    typedef DKC<1, bf16_t, 256> OB;
     Operand<bf16_t> B{static_cast<const bf16_t*>(w) + w0, s.d_kv, 0, N, s.d_kv};
     if (s.split) {
-      EpiKvUp<half_t, 2> e{static_cast<half_t*>(k_nope), static_cast<half_t*>(v), s.T, static_cast<int>(N),
-                           s.C(), s.d_nope, s.d_v, s.h, pk, pv};
-      return run_gemm<MmaBf16, SA, SB>(A, B, e, s.T, N, s.d_kv, 1, st);
+      EpiKvUp<half_t, 2, 128, 128> e{static_cast<half_t*>(k_nope), static_cast<half_t*>(v), s.T,
+                                     static_cast<int>(N), s.h, pk, pv};
+      return run_gemm_dma<OA, OB, 1, 4, 2, 3>(Operand<bf16_t>{}, A, B, e, s.T, N, s.d_kv, 1, st);
     }
-    EpiKvUp<half_t, 1> e{static_cast<half_t*>(k_nope), static_cast<half_t*>(v), s.T, static_cast<int>(N),
-                         s.C(), s.d_nope, s.d_v, s.h, pk, pv};
-    return run_gemm<MmaBf16, SA, SB>(A, B, e, s.T, N, s.d_kv, 1, st);
+    EpiKvUp<half_t, 1, 128, 128> e{static_cast<half_t*>(k_nope), static_cast<half_t*>(v), s.T, static_cast<int>(N),
+                                   s.h, pk, pv};
+    return run_gemm_dma<OA, OB, 1, 4, 2, 3>(Operand<bf16_t>{}, A, B, e, s.T, N, s.d_kv, 1, st);
   }
-  typedef Side<MmaF32, 1, true, BM, float> SA;
-  typedef Side<MmaF32, 1, true, BN, float> SB;
+  if (s.bf16 || s.d_nope != 32 || s.d_v != 32) return hipErrorNotSupported;
+  typedef Side<MmaF32, 1, true, 128, float> SA;
+  typedef Side<MmaF32, 1, true, 128, float> SB;
   Operand<float> B{static_cast<const float*>(w) + w0, s.d_kv, 0, N, s.d_kv};
-  EpiKvUp<float, 1> e{static_cast<float*>(k_nope), static_cast<float*>(v), s.T, static_cast<int>(N),
-                      s.C(), s.d_nope, s.d_v, s.h, 0, 0};
-  return run_gemm<MmaF32, SA, SB>(A, B, e, s.T, N, s.d_kv, 1, st);
+  EpiKvUp<float, 1, 32, 32> e{static_cast<float*>(k_nope), static_cast<float*>(v), s.T, static_cast<int>(N),
+                              s.h, 0, 0};
+  return run_gemm<MmaF32, 2, 2, SA, SB>(A, B, e, s.T, N, s.d_kv, 1, st);
 }
 
 // Absorbed form [LAGA §3.2 (B2)], per local head i (batch z = i):
@@ -412,23 +779,23 @@ hipError_t launch_kv_up(const Shape& s, const float* L, const void* w, void* k_n
 //   un-absorb o[t, i, d]     = sum_c acc[t, i, c] W[i, d_nope + d, c]  (d < d_v)
 hipError_t launch_absorb_q(const Shape& s, const void* q, const void* w, void* q_abs, hipStream_t st) {
   const int64_t w0 = static_cast<int64_t>(s.head_lo) * s.C() * s.d_kv;
-  typedef Side<MmaBf16, 1, true, BM, bf16_t> SA;   // q_nope rows, n contiguous
-  typedef Side<MmaBf16, 1, false, BN, bf16_t> SB;  // W^k[i]: c contiguous, n strides memory
+  typedef DKC<1, bf16_t, 128> OA;  // q_nope rows, n contiguous
+  typedef DRC<1, 256> OB;          // W^k[i]: c contiguous, n strides memory
   Operand<bf16_t> A{static_cast<const bf16_t*>(q), static_cast<int64_t>(s.h) * s.d_qk(), 0, s.T, s.d_nope, s.d_qk()};
   Operand<bf16_t> B{static_cast<const bf16_t*>(w) + w0, s.d_kv, 0, s.d_kv, s.d_nope,
                     static_cast<int64_t>(s.C()) * s.d_kv};
   EpiHalf e{static_cast<half_t*>(q_abs), s.T, s.d_kv, static_cast<int64_t>(s.h) * s.d_kv, s.d_kv};
-  return run_gemm<MmaBf16, SA, SB>(A, B, e, s.T, s.d_kv, s.d_nope, 1, st, s.h);
+  return run_gemm_dma<OA, OB, 2, 4, 4, 1>(A, Operand<float>{}, B, e, s.T, s.d_kv, s.d_nope, 1, st, s.h);
 }
 
 hipError_t launch_unabsorb_o(const Shape& s, const float* acc, const void* w, float* o, hipStream_t st) {
   const int64_t w0 = static_cast<int64_t>(s.head_lo) * s.C() * s.d_kv + static_cast<int64_t>(s.d_nope) * s.d_kv;
-  typedef Side<MmaBf16, 2, true, BM, float> SA;   // acc rows in fp32, split into bf16 hi + lo while staged
-  typedef Side<MmaBf16, 1, true, BN, bf16_t> SB;  // W^v[i] rows, c contiguous
+  typedef DKC<1, float, 256> OA;   // acc rows in fp32, split into bf16 hi + lo as they are read
+  typedef DKC<1, bf16_t, 128> OB;  // W^v[i] rows, c contiguous
   Operand<float> A{acc, static_cast<int64_t>(s.h) * s.d_kv, 0, s.T, s.d_kv, s.d_kv};
   Operand<bf16_t> B{static_cast<const bf16_t*>(w) + w0, s.d_kv, 0, s.d_v, s.d_kv, static_cast<int64_t>(s.C()) * s.d_kv};
   EpiStore e{o, s.T, s.d_v, static_cast<int64_t>(s.h) * s.d_v, s.d_v};
-  return run_gemm<MmaBf16, SA, SB>(A, B, e, s.T, s.d_v, s.d_kv, 1, st, s.h);
+  return run_gemm_dma<OA, OB, 4, 2, 3, 1>(Operand<bf16_t>{}, A, B, e, s.T, s.d_v, s.d_kv, 1, st, s.h);
 }
 
 hipError_t launch_fold_dl(const Shape& s, const void* dkv, const void* w, float* dL, hipStream_t st) {
@@ -436,17 +803,17 @@ hipError_t launch_fold_dl(const Shape& s, const void* dkv, const void* w, float*
   const int64_t w0 = static_cast<int64_t>(s.head_lo) * s.C() * s.d_kv;
   EpiStore e{dL, s.T, s.d_kv, s.d_kv, 0};
   if (s.bf16) {
-    typedef Side<MmaBf16, 2, true, BM, bf16_t> SA;    // dKV[t, n]: bf16 hi/lo planes
-    typedef Side<MmaBf16, 1, false, BN, bf16_t> SB;   // W_r[n, k]: reduction over n strides memory
+    typedef DKC<2, bf16_t, 64> OA;  // dKV[t, n]: bf16 hi/lo planes
+    typedef DRC<1, 256> OB;         // W_r[n, k]: reduction over n strides memory
     Operand<bf16_t> A{static_cast<const bf16_t*>(dkv), Kd, s.T * Kd, s.T, Kd};
     Operand<bf16_t> B{static_cast<const bf16_t*>(w) + w0, s.d_kv, 0, s.d_kv, Kd};
-    return run_gemm<MmaBf16, SA, SB>(A, B, e, s.T, s.d_kv, Kd, 1, st);
+    return run_gemm_dma<OA, OB, 1, 4, 3, 2>(A, Operand<float>{}, B, e, s.T, s.d_kv, Kd, 1, st);
   }
-  typedef Side<MmaF32, 1, true, BM, float> SA;
-  typedef Side<MmaF32, 1, false, BN, float> SB;
+  typedef Side<MmaF32, 1, true, 128, float> SA;
+  typedef Side<MmaF32, 1, false, 128, float> SB;
   Operand<float> A{static_cast<const float*>(dkv), Kd, 0, s.T, Kd};
   Operand<float> B{static_cast<const float*>(w) + w0, s.d_kv, 0, s.d_kv, Kd};
-  return run_gemm<MmaF32, SA, SB>(A, B, e, s.T, s.d_kv, Kd, 1, st);
+  return run_gemm<MmaF32, 2, 2, SA, SB>(A, B, e, s.T, s.d_kv, Kd, 1, st);
 }
 
 size_t fold_dw_partial_floats(const Shape& s) {
@@ -460,17 +827,17 @@ hipError_t launch_fold_dw(const Shape& s, const void* dkv, const void* lplanes, 
   EpiStore e{partial, Mr, s.d_kv, s.d_kv, Mr * s.d_kv};
   hipError_t err;
   if (s.bf16) {
-    typedef Side<MmaBf16, 2, false, BM, bf16_t> SA;   // dKV[t, n] read as A(row = n, k = t)
-    typedef Side<MmaBf16, 2, false, BN, bf16_t> SB;   // L[t, c] read as B(row = c, k = t)
+    typedef DRC<2, 64 * DW_TM> OA;  // dKV[t, n] read as A(row = n, k = t)
+    typedef DRC<2, 64 * DW_TN> OB;  // L[t, c] read as B(row = c, k = t)
     Operand<bf16_t> A{static_cast<const bf16_t*>(dkv), Mr, s.T * Mr, Mr, s.T};
     Operand<bf16_t> B{static_cast<const bf16_t*>(lplanes), s.d_kv, s.T * s.d_kv, s.d_kv, s.T};
-    err = run_gemm<MmaBf16, SA, SB>(A, B, e, Mr, s.d_kv, s.T, chunks, st);
+    err = run_gemm_dma<OA, OB, DW_TM, DW_TN, 2, 2>(A, Operand<float>{}, B, e, Mr, s.d_kv, s.T, chunks, st);
   } else {
-    typedef Side<MmaF32, 1, false, BM, float> SA;
-    typedef Side<MmaF32, 1, false, BN, float> SB;
+    typedef Side<MmaF32, 1, false, 128, float> SA;
+    typedef Side<MmaF32, 1, false, 128, float> SB;
     Operand<float> A{static_cast<const float*>(dkv), Mr, 0, Mr, s.T};
     Operand<float> B{static_cast<const float*>(lplanes), s.d_kv, 0, s.d_kv, s.T};
-    err = run_gemm<MmaF32, SA, SB>(A, B, e, Mr, s.d_kv, s.T, chunks, st);
+    err = run_gemm<MmaF32, 2, 2, SA, SB>(A, B, e, Mr, s.d_kv, s.T, chunks, st);
   }
   if (err != hipSuccess) return err;
   const int64_t n = Mr * s.d_kv;
