@@ -11,8 +11,11 @@ workload's setting).
 
 Prints one JSON line with tokens/s, algorithmic TFLOP/s, per-kernel times
 (HIP events on the launch stream), the roofline of the dominant kernel, the
-fp64 oracle timed on a bounded sample on the host cores, and activation
-memory of LAGA against the explicit and absorbed forms.
+fp64 oracle timed on a bounded sample on the host cores, the forward alone at
+the other DeepSeek-V3 workloads (S=4096 with 16 local heads, and S=4096 with
+all 128 heads on one device), and memory: analytic activation bytes of LAGA
+against the explicit and absorbed forms, the backward workspace, and the peak
+that torch's allocator records over one training step.
 """
 from __future__ import annotations
 
@@ -99,13 +102,35 @@ def calibration_copy(nbytes: int = 256 << 20, reps: int = 3):
     del src, dst
 
 
+def host_info() -> dict:
+    """CPU model, logical CPU count and the BLAS numpy's oracle runs on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if libs:
+            blas = {"name": libs[0].get("internal_api"), "version": libs[0].get("version"),
+                    "threads": libs[0].get("num_threads")}
+    except Exception:  # noqa: BLE001 - informational only
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "blas": blas}
+
+
 def cpu_baseline(d) -> dict:
     """The fp64 oracle, untuned, on 4 of the workload's heads (n_h=128 at SP=32, rank 0):
     norm, up-projection of those heads, causal attention forward and backward, and the
     folds, at the full S.  Tokens/s is scaled to the workload's head count."""
     import laga_inputs as li
     import oracle
-    from threadpoolctl import threadpool_info
     sample_heads = 4
     one = li.Dims(B=d.B, S=d.S, n_h=d.n_h, sp_size=d.n_h // sample_heads, sp_rank=0, d_kv=d.d_kv, d_nope=d.d_nope,
                   d_rope=d.d_rope, d_v=d.d_v, dtype=d.dtype)
@@ -116,11 +141,82 @@ def cpu_baseline(d) -> dict:
     f = oracle.forward(v["q"], v["latent"], v["k_pe"], v["w_kv_b"], v["gamma"], **kw)
     oracle.backward(v["q"], v["latent"], v["k_pe"], v["w_kv_b"], v["gamma"], v["d_o"], fwd=f, **kw)
     dt = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    info = host_info()
+    threads = (info["blas"] or {}).get("threads") or 1
     return {"value": d.B * d.S * sample_heads / (dt * d.h), "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": f"fp64 oracle fwd+bwd of {sample_heads} of the {d.h} heads at full S={d.S} "
-                      f"({dt:.1f} s), scaled by {sample_heads}/{d.h}"}
+                      f"({dt:.1f} s), scaled by {sample_heads}/{d.h}",
+            **info}
+
+
+def time_forward(name: str, steps: int, warmup: int) -> dict:
+    """The forward (norm, up-projection, attention) of a forward-only workload with
+    single fp16 operands, HIP events around each kernel."""
+    import torch
+    import laga_inputs as li
+    from head_latent_attention_laga_amd import LagaPath, _lib
+    d, _ = li.workload(name)
+    x = {k: li.to_torch(t) for k, t in li.make_inputs(d, 0).items()}
+    p = LagaPath(d.B, d.S, d.n_h, d.sp_size, d.sp_rank, d.d_kv, d.d_nope, d.d_rope, d.d_v, d.dtype, FP16, d.eps)
+    out = p.alloc_forward()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for _ in range(warmup):
+        p.forward(x, out)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        e = ev[i]
+        e[0].record()
+        _lib.latent_norm(p.dims, x["latent"], x["gamma"], out["latent_n"], out["rstd"])
+        e[1].record()
+        _lib.kv_up(p.dims, out["latent_n"], x["w_kv_b"], out["k_nope"], out["v"])
+        e[2].record()
+        _lib.attn_fwd(p.dims, x["q"], out["k_nope"], x["k_pe"], out["v"], out["o"], out["lse"])
+        e[3].record()
+    torch.cuda.synchronize()
+    ks = {n: statistics.mean(ev[i][k].elapsed_time(ev[i][k + 1]) for i in range(steps))
+          for k, n in enumerate(["rmsnorm_fwd", "kv_up", "attn_fwd"])}
+    ms = sum(ks.values())
+    fl = alg_flops(d)
+    del x, out
+    torch.cuda.empty_cache()
+    return {"workload": name, "B": d.B, "S": d.S, "local_heads": d.h, "n_h": d.n_h, "sp_size": d.sp_size,
+            "ms": round(ms, 4), "tokens_s": round(d.B * d.S / (ms / 1e3), 1),
+            "tflops": round(fl["fwd"] / (ms / 1e3) / 1e12, 2),
+            "frac_peak": round(fl["fwd"] / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "kv_up_tflops": round(fl["kv_up"] / (ks["kv_up"] / 1e3) / 1e12, 2),
+            "attn_tflops": round(fl["attn_fwd"] / (ks["attn_fwd"] / 1e3) / 1e12, 2),
+            "kernels_ms": {k: round(v, 4) for k, v in ks.items()}}
+
+
+def step_peak_memory(d) -> dict:
+    """Device memory of one training step as torch's allocator records it: the
+    inputs, then the forward's kept outputs, then the backward's workspace and
+    gradients, with the peak over the step (nothing else is allocated)."""
+    import torch
+    import laga_inputs as li
+    from head_latent_attention_laga_amd import LagaPath, _lib
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    m0 = torch.cuda.memory_allocated()
+    x = {k: li.to_torch(t) for k, t in li.make_inputs(d, 0, backward=True).items()}
+    m_in = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    p = LagaPath(d.B, d.S, d.n_h, d.sp_size, d.sp_rank, d.d_kv, d.d_nope, d.d_rope, d.d_v, d.dtype, SPLIT, d.eps)
+    fwd = p.forward(x)
+    m_fwd = torch.cuda.memory_allocated()
+    g = p.alloc_backward()
+    m_bwd = torch.cuda.memory_allocated()
+    p.backward(x, fwd, x["d_o"], g)
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated()
+    ws = _lib.attn_bwd_workspace_bytes(p.dims)
+    del x, fwd, g
+    torch.cuda.empty_cache()
+    mb = 2.0 ** 20
+    return {"inputs_mb": round((m_in - m0) / mb, 1), "forward_kept_mb": round((m_fwd - m_in) / mb, 1),
+            "backward_workspace_mb": round(ws / mb, 1), "gradients_mb": round((m_bwd - m_fwd - ws) / mb, 1),
+            "step_peak_mb": round((peak - m0) / mb, 1), "step_peak_above_inputs_mb": round((peak - m_in) / mb, 1)}
 
 
 def main():
@@ -264,6 +360,14 @@ def main():
     fwd_ms = fper["rmsnorm_fwd"] + fper["kv_up"] + fper["attn_fwd"]
     kvb = _lib.kv_elem_bytes(path.dims)
     act = {k: round(v / 2**20, 1) for k, v in activation_bytes(d, kvb).items()}
+    act["laga_backward_workspace"] = round(_lib.attn_bwd_workspace_bytes(path.dims) / 2**20, 1)
+
+    # The other forward-only workloads, then the step's measured memory.
+    del x, fwd, grads, ffwd
+    torch.cuda.empty_cache()
+    other = {"v3_sp8_s4096_h16": time_forward("v3_sp8_s4096_h16", args.steps, args.warmup),
+             "v3_sp1_s4096_h128": time_forward("v3_sp1_s4096_h128", args.steps, args.warmup)}
+    mem = step_peak_memory(d)
     line = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
@@ -287,12 +391,12 @@ def main():
         "sclk": gpu_sclk(),
         "roofline": roofline,
         "activation_mb": act,
+        "memory_step_mb": mem,
+        "forward_other_workloads": other,
         "absorbed_form_fwd": absorbed,
         "gpu": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline:
-        del x, fwd, grads, ffwd
-        torch.cuda.empty_cache()
         line["cpu_baseline"] = cpu_baseline(d)
     else:
         line["cpu_baseline"] = None

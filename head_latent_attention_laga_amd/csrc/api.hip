@@ -205,7 +205,8 @@ laga_status laga_attn_bwd_traced(const laga_dims* dims, const void* q, const voi
   if ((e = laga::launch_attn_bwd_dkdv(s, q, k_nope, k_pe, v, lse, delta, d_o, cp, dkv, dkpe, hs)) != hipSuccess)
     return from_hip(e);
   if ((e = mark(2)) != hipSuccess) return from_hip(e);
-  if ((e = laga::launch_attn_bwd_dq(s, q, k_nope, k_pe, v, lse, delta, d_o, cp.do_shift, dq, hs)) != hipSuccess)
+  if ((e = laga::launch_attn_bwd_dq(s, q, k_nope, k_pe, v, lse, delta, d_o, cp.do_shift, s.split ? cp.osc : nullptr,
+                                    dq, hs)) != hipSuccess)
     return from_hip(e);
   if ((e = mark(3)) != hipSuccess) return from_hip(e);
   if ((e = laga::launch_head_sum(s, dkpe, d_k_pe, hs)) != hipSuccess) return from_hip(e);

@@ -255,6 +255,7 @@ struct Dq {
     State st_;
     st_.dorow = reinterpret_cast<const E*>(lds + OFF_DO + wv * DO_BYTES) + col * LDO + hf * M::KPL;
     const int g = do_shift_of(a);
+    int rsh[QH];  // per-query power of two that normalises the query's dS (see below)
 #pragma unroll
     for (int u = 0; u < QH; ++u) {
       const int64_t tq = qw + 32 * u + col;
@@ -269,7 +270,19 @@ struct Dq {
 #pragma unroll
       for (int s = 0; s < KS_V; ++s) *reinterpret_cast<F*>(dst + s * M::K) = *reinterpret_cast<const F*>(op + s * M::K);
       const int64_t si = (static_cast<int64_t>(b) * a.h + head) * a.S + tc;
-      st_.lse2[u] = a.lse[si] * kLog2e;
+      // dS of query t is linear in its dO row, whose fp16 copy carries the
+      // global factor 2^g.  A row far below the largest |dO| would give dS in
+      // fp16's subnormal range; scaling the row's P by 2^e (folded into the
+      // exponent: P 2^e = exp2(log2 P + e)), with e from the row's own
+      // magnitude (the E8M0 byte 127 - s of its e4m3 copy: max |dO| 2^s in
+      // [128, 256)), brings every row's dS near unit scale; dq is divided by
+      // 2^e at the end.
+      rsh[u] = 0;
+      if (a.osc != nullptr) {
+        const int e = 120 - a.osc[si] - g;
+        rsh[u] = e < -100 ? -100 : (e > 100 ? 100 : e);
+      }
+      st_.lse2[u] = a.lse[si] * kLog2e - static_cast<float>(rsh[u]);
       st_.dlt[u] = a.delta[si] * pow2i(g);
 #pragma unroll
       for (int n = 0; n < NQT; ++n)
@@ -285,12 +298,12 @@ struct Dq {
     }
     if (kb < nkb) step(a, kb, nkb, b, head, qw, lds, R, st_);
 
-    // dS carries dO's scale 2^g.
-    const float osc = a.scale * pow2i(-g);
+    // dS carries dO's scale 2^g and the row's 2^e.
 #pragma unroll
     for (int u = 0; u < QH; ++u) {
       const int64_t tq = qw + 32 * u + col;
       if (tq >= a.S) continue;
+      const float osc = a.scale * pow2i(-g - rsh[u]);
       float* out = a.dq + ((b * a.S + tq) * a.h + head) * DQK;
 #pragma unroll
       for (int n = 0; n < NQT; ++n)
@@ -323,11 +336,12 @@ hipError_t dq_t(const BwdArgs& a, const Shape& s, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_attn_bwd_dq(const Shape& s, const void* q, const void* k_nope, const void* k_pe, const void* v,
-                              const float* lse, const float* delta, const void* d_o, const int* do_shift, float* dq,
-                              hipStream_t st) {
+                              const float* lse, const float* delta, const void* d_o, const int* do_shift,
+                              const int* do_row_scale, float* dq, hipStream_t st) {
   BwdArgs a = make_args(s, q, k_nope, k_pe, v, lse, delta, d_o);
   a.dq = dq;
   a.do_shift = do_shift;
+  a.osc = do_row_scale;
   if (s.bf16 && s.split && s.d_nope == 128 && s.d_rope == 64 && s.d_v == 128)
     return dq_t<MmaF16, 128, 64, 128, 4, 2>(a, s, st);
   if (!s.bf16 && s.d_nope == 32 && s.d_rope == 16 && s.d_v == 32) return dq_t<MmaF32, 32, 16, 32, 4, 1>(a, s, st);

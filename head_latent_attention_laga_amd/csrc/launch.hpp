@@ -50,10 +50,11 @@ hipError_t launch_attn_bwd_dkdv(const Shape& s, const void* q, const void* k_nop
                                 const float* delta, const void* d_o, const BwdCopies& c, void* dkv,
                                 float* dk_pe_part, hipStream_t st);
 // dq, recomputing P and dS from lse and delta.  q, k_pe, d_o: the fp16 copies
-// (bfloat16 inputs) or the float32 inputs; k_nope, v: their first plane.
+// (bfloat16 inputs) or the float32 inputs; k_nope, v: their first plane;
+// do_row_scale: the E8M0 bytes of dO's e4m3 rows (BwdCopies::osc) or nullptr.
 hipError_t launch_attn_bwd_dq(const Shape& s, const void* q, const void* k_nope, const void* k_pe, const void* v,
-                              const float* lse, const float* delta, const void* d_o, const int* do_shift, float* dq,
-                              hipStream_t st);
+                              const float* lse, const float* delta, const void* d_o, const int* do_shift,
+                              const int* do_row_scale, float* dq, hipStream_t st);
 hipError_t launch_head_sum(const Shape& s, const float* part, float* out, hipStream_t st);
 // dkv: [T, h, d_nope + d_v] as bf16 hi/lo planes (bf16 inputs) or one fp32 plane.
 hipError_t launch_fold_dl(const Shape& s, const void* dkv, const void* w, float* dL, hipStream_t st);

@@ -124,3 +124,37 @@ def test_backward_gradient_magnitude(scale_exp):
     check("dk_pe/s", host(g["d_k_pe"]) / sc, ref["dk_pe"] / sc, d.dtype)
     check("d_gamma/s", host(g["d_gamma"]) / sc, ref["d_gamma"] / sc, d.dtype)
     check("d_w/s", host(g["d_w_kv_b"])[heads] / sc, ref["d_w_kv_b"][heads] / sc, d.dtype)
+
+
+def test_backward_row_varying_gradient_magnitude():
+    """dO of every odd token scaled by 2^-16 (exact in bf16), the even tokens
+    at unit scale: the global dO scale is set by the large rows, so without a
+    per-row scale the small rows' score gradients would sit in fp16's
+    subnormal range and their dq would lose most of its relative precision.
+    dq of a token is linear in that token's dO row, so each dq row is divided
+    by its own factor and held to the usual bars (relative accuracy per row);
+    the gradients that sum over queries are held to the bars as they are."""
+    d = _dims(1, 300, 16, 8, 3, li.BF16)
+    announce(f"backward with row-varying dO magnitudes dims={d}")
+    inp = li.make_inputs(d, 31, backward=True)
+    x = device_inputs(inp)
+    rs = np.ones(d.S)
+    rs[1::2] = 2.0 ** -16
+    rst = torch.tensor(rs, dtype=torch.float32, device=x["d_o"].device)[None, :, None, None]
+    x["d_o"] = (x["d_o"].float() * rst).to(torch.bfloat16)
+    path = make_path(d, SPLIT)
+    fwd = path.forward(x)
+    g = path.backward(x, fwd, x["d_o"])
+    torch.cuda.synchronize()
+    v = {k: t.value for k, t in inp.items()}
+    d_o = v["d_o"] * rs[None, :, None, None]
+    assert np.array_equal(host(x["d_o"]), d_o), "scaling dO rows by powers of two must be exact"
+    ref = oracle.backward(v["q"], v["latent"], v["k_pe"], v["w_kv_b"], v["gamma"], d_o, n_h=d.n_h,
+                          sp_size=d.sp_size, sp_rank=d.sp_rank, d_nope=d.d_nope, eps=d.eps)
+    per_row = rs[None, :, None, None]
+    check("dq/s_t", host(g["dq"]) / per_row, ref["dq"] / per_row, d.dtype)
+    check("d_latent", host(g["d_latent"]), ref["d_latent"], d.dtype)
+    check("dk_pe", host(g["d_k_pe"]), ref["dk_pe"], d.dtype)
+    check("d_gamma", host(g["d_gamma"]), ref["d_gamma"], d.dtype)
+    heads = oracle.head_shard(d.n_h, d.sp_size, d.sp_rank)
+    check("d_w_kv_b", host(g["d_w_kv_b"])[heads], ref["d_w_kv_b"][heads], d.dtype)
