@@ -19,6 +19,7 @@ LAGA_F32, LAGA_BF16 = 0, 1
 LAGA_OPERANDS_FP16, LAGA_OPERANDS_SPLIT = 0, 1
 LAGA_BWD_STAGES = 7
 LAGA_KV_LO_SHIFT = 12  # the #define of laga.h: scale exponent of the e4m3 low plane of split K/V
+LAGA_NOALLOC_SCRATCH_BYTES = 256 << 20  # the #define of laga.h: static scratch of laga_attn_bwd_noalloc
 BWD_STAGE_NAMES = ("bwd_delta", "attn_bwd_dkdv", "attn_bwd_dq", "dk_pe_head_sum", "fold_dL", "fold_dW",
                    "rmsnorm_bwd")
 STATUS = {0: "LAGA_OK", 1: "LAGA_ERR_INVALID", 2: "LAGA_ERR_UNSUPPORTED", 3: "LAGA_ERR_ALIGN",
@@ -53,6 +54,7 @@ _SIGS = {
     "laga_attn_bwd": (ctypes.c_int, [ctypes.POINTER(laga_dims)] + [_P] * 17 + [ctypes.c_size_t, _P]),
     "laga_attn_bwd_traced": (ctypes.c_int, [ctypes.POINTER(laga_dims)] + [_P] * 17
                              + [ctypes.c_size_t, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, _P]),
+    "laga_attn_bwd_noalloc": (ctypes.c_int, [ctypes.POINTER(laga_dims)] + [_P] * 17),
     "laga_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -142,6 +144,15 @@ def attn_bwd(dims, q, latent, gamma, rstd, k_nope, k_pe, v, w_kv_b, o, lse, d_o,
         _ptr(v), _ptr(w_kv_b), _ptr(o), _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(d_latent), _ptr(d_k_pe),
         _ptr(d_w_kv_b), _ptr(d_gamma), _ptr(workspace), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
         _stream(stream)))
+
+
+def attn_bwd_noalloc(dims, q, latent, gamma, rstd, k_nope, k_pe, v, w_kv_b, o, lse, d_o, dq, d_latent,
+                     d_k_pe, d_w_kv_b, d_gamma, stream=None):
+    """laga_attn_bwd on the library's static per-device scratch (no workspace argument, no allocation)."""
+    _check("laga_attn_bwd_noalloc", load().laga_attn_bwd_noalloc(
+        ctypes.byref(dims), _ptr(q), _ptr(latent), _ptr(gamma), _ptr(rstd), _ptr(k_nope), _ptr(k_pe),
+        _ptr(v), _ptr(w_kv_b), _ptr(o), _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(d_latent), _ptr(d_k_pe),
+        _ptr(d_w_kv_b), _ptr(d_gamma), _stream(stream)))
 
 
 def attn_bwd_traced(dims, q, latent, gamma, rstd, k_nope, k_pe, v, w_kv_b, o, lse, d_o, dq, d_latent,

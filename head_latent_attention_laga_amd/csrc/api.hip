@@ -4,6 +4,8 @@
 
 #include "launch.hpp"
 
+#include <mutex>
+
 namespace {
 
 using laga::Shape;
@@ -79,6 +81,33 @@ BwdLayout bwd_layout(const Shape& s) {
   return L;
 }
 
+// ------------------------------------------------ allocation-free backward
+// Scratch of laga_attn_bwd_noalloc: a device array of fixed size, one copy per
+// GPU the library runs on, held until the process ends.  Host code never uses
+// the array's name as an address (in host code it is only a stand-in for the
+// symbol): the device address comes from hipGetSymbolAddress, once per
+// device, and is what the kernels receive.
+static __device__ __align__(256) char scratch[LAGA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (LAGA_OK), looked up on the first call
+// on that device with the device current.
+laga_status current_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LAGA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return LAGA_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return LAGA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -145,11 +174,19 @@ size_t laga_attn_bwd_workspace_bytes(const laga_dims* dims) {
   return bwd_layout(s).total;
 }
 
-laga_status laga_attn_bwd_traced(const laga_dims* dims, const void* q, const void* latent, const void* gamma,
-                                 const float* rstd, const void* k_nope, const void* k_pe, const void* v,
-                                 const void* w_kv_b, const float* o, const float* lse, const void* d_o, float* dq,
-                                 float* d_latent, float* d_k_pe, float* d_w_kv_b, float* d_gamma, void* workspace,
-                                 size_t workspace_bytes, void* const* events, int n_events, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The backward behind laga_attn_bwd, laga_attn_bwd_traced and
+// laga_attn_bwd_noalloc.  With from_scratch the workspace is the device's
+// static scratch array; every argument and size is checked on the host before
+// anything touches the GPU.
+laga_status attn_bwd_impl(const laga_dims* dims, const void* q, const void* latent, const void* gamma,
+                          const float* rstd, const void* k_nope, const void* k_pe, const void* v, const void* w_kv_b,
+                          const float* o, const float* lse, const void* d_o, float* dq, float* d_latent,
+                          float* d_k_pe, float* d_w_kv_b, float* d_gamma, void* workspace, size_t workspace_bytes,
+                          bool from_scratch, void* const* events, int n_events, void* stream) {
   Shape s;
   laga_status st = check_dims(dims, &s);
   if (st != LAGA_OK) return st;
@@ -165,6 +202,11 @@ laga_status laga_attn_bwd_traced(const laga_dims* dims, const void* q, const voi
   for (const void* p : ptrs)
     if (!aligned16(p)) return LAGA_ERR_ALIGN;
   const BwdLayout L = bwd_layout(s);
+  if (from_scratch) {
+    if (L.total > LAGA_NOALLOC_SCRATCH_BYTES) return LAGA_ERR_WORKSPACE;
+    if ((st = current_scratch(&workspace)) != LAGA_OK) return st;
+    workspace_bytes = LAGA_NOALLOC_SCRATCH_BYTES;
+  }
   if (workspace == nullptr || workspace_bytes < L.total) return LAGA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return LAGA_ERR_ALIGN;
   char* ws = static_cast<char*>(workspace);
@@ -222,6 +264,19 @@ laga_status laga_attn_bwd_traced(const laga_dims* dims, const void* q, const voi
   return LAGA_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+laga_status laga_attn_bwd_traced(const laga_dims* dims, const void* q, const void* latent, const void* gamma,
+                                 const float* rstd, const void* k_nope, const void* k_pe, const void* v,
+                                 const void* w_kv_b, const float* o, const float* lse, const void* d_o, float* dq,
+                                 float* d_latent, float* d_k_pe, float* d_w_kv_b, float* d_gamma, void* workspace,
+                                 size_t workspace_bytes, void* const* events, int n_events, void* stream) {
+  return attn_bwd_impl(dims, q, latent, gamma, rstd, k_nope, k_pe, v, w_kv_b, o, lse, d_o, dq, d_latent, d_k_pe,
+                       d_w_kv_b, d_gamma, workspace, workspace_bytes, false, events, n_events, stream);
+}
+
 laga_status laga_attn_bwd(const laga_dims* dims, const void* q, const void* latent, const void* gamma,
                           const float* rstd, const void* k_nope, const void* k_pe, const void* v,
                           const void* w_kv_b, const float* o, const float* lse, const void* d_o,
@@ -229,6 +284,14 @@ laga_status laga_attn_bwd(const laga_dims* dims, const void* q, const void* late
                           void* workspace, size_t workspace_bytes, void* stream) {
   return laga_attn_bwd_traced(dims, q, latent, gamma, rstd, k_nope, k_pe, v, w_kv_b, o, lse, d_o, dq, d_latent,
                               d_k_pe, d_w_kv_b, d_gamma, workspace, workspace_bytes, nullptr, 0, stream);
+}
+
+laga_status laga_attn_bwd_noalloc(const laga_dims* dims, const void* q, const void* latent, const void* gamma,
+                                  const float* rstd, const void* k_nope, const void* k_pe, const void* v,
+                                  const void* w_kv_b, const float* o, const float* lse, const void* d_o, float* dq,
+                                  float* d_latent, float* d_k_pe, float* d_w_kv_b, float* d_gamma, void* stream) {
+  return attn_bwd_impl(dims, q, latent, gamma, rstd, k_nope, k_pe, v, w_kv_b, o, lse, d_o, dq, d_latent, d_k_pe,
+                       d_w_kv_b, d_gamma, nullptr, 0, true, nullptr, 0, stream);
 }
 
 const char* laga_status_string(laga_status status) {

@@ -215,6 +215,31 @@ laga_status laga_attn_bwd_traced(const laga_dims* dims, const void* q, const voi
                                  void* workspace, size_t workspace_bytes, void* const* events,
                                  int n_events, void* stream);
 
+/*
+ * laga_attn_bwd without a caller workspace, for callers that cannot allocate
+ * device memory (code under stream/graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The workspace is a static device array
+ * of LAGA_NOALLOC_SCRATCH_BYTES inside the library: one copy on every GPU the
+ * library runs on, held until the process ends; its address is looked up once
+ * per device (hipGetSymbolAddress) on the first call made with that device
+ * current.  The call allocates nothing.  Problems whose
+ * laga_attn_bwd_workspace_bytes exceeds LAGA_NOALLOC_SCRATCH_BYTES (at the V3
+ * head dims: more than about 5900 tokens with 16 local heads, or about 700
+ * with 128) return LAGA_ERR_WORKSPACE; that and every other argument check
+ * happen on the host before anything touches the GPU.  No part of
+ * the scratch needs to start at zero (every stage writes its region before it
+ * is read).  All calls on one GPU share its scratch: calls that can overlap
+ * in time on one GPU (different streams, or host threads) race, so the caller
+ * serialises them.  Arguments and results are those of laga_attn_bwd.
+ */
+#define LAGA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+laga_status laga_attn_bwd_noalloc(const laga_dims* dims, const void* q, const void* latent,
+                                  const void* gamma, const float* rstd, const void* k_nope,
+                                  const void* k_pe, const void* v, const void* w_kv_b,
+                                  const float* o, const float* lse, const void* d_o, float* dq,
+                                  float* d_latent, float* d_k_pe, float* d_w_kv_b, float* d_gamma,
+                                  void* stream);
+
 /* Static, human-readable text of a status code. */
 const char* laga_status_string(laga_status status);
 

@@ -134,6 +134,35 @@ def test_backward_argument_checks(lib):
     assert lib.laga_attn_bwd(ctypes.byref(d16), *args, ctypes.c_size_t(1 << 40), None) == UNSUPPORTED
 
 
+def test_noalloc_scratch_size_matches_header():
+    import re
+    text = open(_lib.HEADER).read()
+    m = re.search(r"#define\s+LAGA_NOALLOC_SCRATCH_BYTES\s+\(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.LAGA_NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_backward_checks_on_the_host(lib):
+    """The allocation-free backward rejects, before any HIP call, problems whose
+    workspace exceeds its static scratch and every argument laga_attn_bwd rejects."""
+    cap = _lib.LAGA_NOALLOC_SCRATCH_BYTES
+    args = [FAKE] * 16
+    fits = v3(S=4096, n_h=128, sp_size=8)
+    big = v3(S=8192, n_h=128, sp_size=8)
+    assert lib.laga_attn_bwd_workspace_bytes(ctypes.byref(fits)) <= cap
+    assert lib.laga_attn_bwd_workspace_bytes(ctypes.byref(big)) > cap
+    assert lib.laga_attn_bwd_noalloc(ctypes.byref(big), *args, None) == WORKSPACE
+    assert lib.laga_attn_bwd_noalloc(ctypes.byref(v3(S=1024, n_h=128, sp_size=1)), *args, None) == WORKSPACE
+    a3 = list(args)
+    a3[4] = None
+    assert lib.laga_attn_bwd_noalloc(ctypes.byref(fits), *a3, None) == INVALID
+    a4 = list(args)
+    a4[10] = MISALIGNED
+    assert lib.laga_attn_bwd_noalloc(ctypes.byref(fits), *a4, None) == ALIGN
+    assert lib.laga_attn_bwd_noalloc(ctypes.byref(v3(precision=_lib.LAGA_OPERANDS_FP16)), *args, None) == UNSUPPORTED
+    assert lib.laga_attn_bwd_noalloc(ctypes.byref(v3(S=0)), *args, None) == INVALID
+    assert lib.laga_attn_bwd_noalloc(None, *args, None) == INVALID
+
+
 def test_workspace_grows_with_sequence(lib):
     a = lib.laga_attn_bwd_workspace_bytes(ctypes.byref(v3(S=1024)))
     b = lib.laga_attn_bwd_workspace_bytes(ctypes.byref(v3(S=2048)))
