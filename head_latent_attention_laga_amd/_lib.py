@@ -50,6 +50,8 @@ _SIGS = {
     "laga_kv_up": (ctypes.c_int, [ctypes.POINTER(laga_dims), _P, _P, _P, _P, _P]),
     "laga_attn_fwd": (ctypes.c_int, [ctypes.POINTER(laga_dims), _P, _P, _P, _P, _P, _P, _P]),
     "laga_absorbed_fwd": (ctypes.c_int, [ctypes.POINTER(laga_dims)] + [_P] * 10),
+    "laga_attn_fwd_fused_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(laga_dims)]),
+    "laga_attn_fwd_fused": (ctypes.c_int, [ctypes.POINTER(laga_dims)] + [_P] * 8 + [ctypes.c_size_t, _P]),
     "laga_attn_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(laga_dims)]),
     "laga_attn_bwd": (ctypes.c_int, [ctypes.POINTER(laga_dims)] + [_P] * 17 + [ctypes.c_size_t, _P]),
     "laga_attn_bwd_traced": (ctypes.c_int, [ctypes.POINTER(laga_dims)] + [_P] * 17
@@ -131,6 +133,16 @@ def absorbed_fwd(dims, q, latent_n, k_pe, w_kv_b, q_abs, kx, acc, o, lse, stream
     _check("laga_absorbed_fwd", load().laga_absorbed_fwd(
         ctypes.byref(dims), _ptr(q), _ptr(latent_n), _ptr(k_pe), _ptr(w_kv_b), _ptr(q_abs), _ptr(kx), _ptr(acc),
         _ptr(o), _ptr(lse), _stream(stream)))
+
+
+def attn_fwd_fused_workspace_bytes(dims) -> int:
+    return int(load().laga_attn_fwd_fused_workspace_bytes(ctypes.byref(dims)))
+
+
+def attn_fwd_fused(dims, q, latent, gamma, k_pe, w_kv_b, o, lse, workspace, stream=None):
+    _check("laga_attn_fwd_fused", load().laga_attn_fwd_fused(
+        ctypes.byref(dims), _ptr(q), _ptr(latent), _ptr(gamma), _ptr(k_pe), _ptr(w_kv_b), _ptr(o), _ptr(lse),
+        _ptr(workspace), ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(stream)))
 
 
 def attn_bwd_workspace_bytes(dims) -> int:

@@ -149,6 +149,30 @@ laga_status laga_attn_fwd(const laga_dims* dims, const void* q, const void* k_no
   return from_hip(laga::launch_attn_fwd(s, q, k_nope, k_pe, v, o, lse, static_cast<hipStream_t>(stream)));
 }
 
+size_t laga_attn_fwd_fused_workspace_bytes(const laga_dims* dims) {
+  Shape s;
+  if (check_dims(dims, &s) != LAGA_OK) return 0;
+  return laga::fused_fwd_workspace_bytes(s);
+}
+
+laga_status laga_attn_fwd_fused(const laga_dims* dims, const void* q, const void* latent, const void* gamma,
+                                const void* k_pe, const void* w_kv_b, float* o, float* lse, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  Shape s;
+  laga_status st = check_dims(dims, &s);
+  if (st != LAGA_OK) return st;
+  const size_t need = laga::fused_fwd_workspace_bytes(s);
+  if (need == 0) return LAGA_ERR_UNSUPPORTED;
+  if (!q || !latent || !gamma || !k_pe || !w_kv_b || !o || !lse) return LAGA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(latent) || !aligned16(gamma) || !aligned16(k_pe) || !aligned16(w_kv_b) ||
+      !aligned16(o) || !aligned16(lse))
+    return LAGA_ERR_ALIGN;
+  if (workspace == nullptr || workspace_bytes < need) return LAGA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LAGA_ERR_ALIGN;
+  return from_hip(laga::launch_attn_fwd_fused(s, q, latent, gamma, k_pe, w_kv_b, o, lse, workspace,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 laga_status laga_absorbed_fwd(const laga_dims* dims, const void* q, const float* latent_n, const void* k_pe,
                               const void* w_kv_b, void* q_abs, void* kx, float* acc, float* o, float* lse,
                               void* stream) {

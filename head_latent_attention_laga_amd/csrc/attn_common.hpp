@@ -156,6 +156,13 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, void* lds_
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds_window), 16, voffset, 0, 0, 0);
 }
 
+// s_waitcnt vmcnt(N) with expcnt and lgkmcnt left at their maximum.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Workgroup barrier for LDS data written by ds_write only: wait for this
 // wave's LDS operations, then s_barrier, with a compiler memory barrier so no
 // LDS access moves across it.  Unlike __syncthreads it does not wait for the

@@ -368,41 +368,10 @@ struct Fwd {
     if (ALL || key0 <= qw + 31) compute_block(a, cur, key0, qw, tq, st_);
   }
 
-  __device__ static void run(const FwdArgs& a, char* lds) {
-    const int lane = threadIdx.x % kWave;
-    const int wv = threadIdx.x / kWave;
-    const int hf = lane / 32;
-    const int col = lane % 32;
-
-    // Workgroup -> (batch*head, query tile).  Workgroup ids are dealt
-    // round-robin to the 8 XCDs; heads are grouped per XCD so the workgroups
-    // streaming one head's K/V share an L2, and within an XCD the longest
-    // (latest) query tiles start first.
-    const int nbh = a.B * a.h;
-    int bh, qt_rank;
-    if (nbh % 8 == 0) {
-      const int xcd = blockIdx.x % 8, j = blockIdx.x / 8, hpx = nbh / 8;
-      bh = xcd * hpx + j % hpx;
-      qt_rank = j / hpx;
-    } else {
-      bh = blockIdx.x % nbh;
-      qt_rank = blockIdx.x / nbh;
-    }
-    const int qt = a.n_qt - 1 - qt_rank;
-    const int b = bh / a.h, head = bh % a.h;
-    const int64_t q0 = static_cast<int64_t>(qt) * BM;
-    const int64_t qw = q0 + wv * 32;
-    const int64_t tq = qw + col;
-    const bool qvalid = tq < a.S;
-
-    int64_t kend = q0 + BM;
-    if (kend > a.S) kend = a.S;
-    const int nkb = static_cast<int>((kend + BN - 1) / BN);
-    Regs R;
-    load_block(a, b, head, 0, R);
-
-    // Q fragments (B operand): query tq, dims hf*KPL + s*K + [0, KPL).
-    State st_;
+  // Q fragments (B operand) of query tq -- dims hf*KPL + s*K + [0, KPL) -- and
+  // an empty accumulator.
+  __device__ static void begin(const FwdArgs& a, int b, int head, int64_t tq, bool qvalid, State& st_) {
+    const int hf = (threadIdx.x % kWave) / 32;
     const InT* qp = static_cast<const InT*>(a.q) + ((b * a.S + (qvalid ? tq : 0)) * a.h + head) * (DN + DR);
 #pragma unroll
     for (int s = 0; s < KS_N; ++s) {
@@ -447,11 +416,68 @@ struct Fwd {
       for (int r = 0; r < 16; ++r) st_.o[n][r] = 0.f;
     st_.m_run = -INFINITY;
     st_.l_run = 0.f;
+  }
 
-    // Blocks with key0 <= q0 + 31 are computed by every wavefront; the last
-    // few (above the lower wavefronts' diagonals) are skipped per wavefront.
-    int nall = static_cast<int>((q0 + 31) / BN) + 1;
-    if (nall > nkb) nall = nkb;
+  // o = O / l and lse of query tq.
+  __device__ static void finish(const FwdArgs& a, int b, int head, int64_t tq, bool qvalid, const State& st_) {
+    if (!qvalid) return;
+    const int hf = (threadIdx.x % kWave) / 32;
+    const float inv = 1.0f / st_.l_run;
+    float* op = a.o + ((b * a.S + tq) * a.h + head) * DV;
+#pragma unroll
+    for (int n = 0; n < NO; ++n)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 w = {st_.o[n][4 * g] * inv, st_.o[n][4 * g + 1] * inv, st_.o[n][4 * g + 2] * inv,
+                   st_.o[n][4 * g + 3] * inv};
+        *reinterpret_cast<f32x4*>(op + n * 32 + 8 * g + 4 * hf) = w;
+      }
+    if (hf == 0)
+      a.lse[(static_cast<int64_t>(b) * a.h + head) * a.S + tq] = (st_.m_run + log2f(st_.l_run)) * 0.69314718055994531f;
+  }
+
+  // Blocks with key0 <= q0 + 31 are computed by every wavefront; the last few
+  // (above the lower wavefronts' diagonals) are skipped per wavefront.
+  __device__ static int blocks_for_all(int64_t q0, int nkb) {
+    const int nall = static_cast<int>((q0 + 31) / BN) + 1;
+    return nall < nkb ? nall : nkb;
+  }
+
+  __device__ static void run(const FwdArgs& a, char* lds) {
+    const int lane = threadIdx.x % kWave;
+    const int wv = threadIdx.x / kWave;
+    const int col = lane % 32;
+
+    // Workgroup -> (batch*head, query tile).  Workgroup ids are dealt
+    // round-robin to the 8 XCDs; heads are grouped per XCD so the workgroups
+    // streaming one head's K/V share an L2, and within an XCD the longest
+    // (latest) query tiles start first.
+    const int nbh = a.B * a.h;
+    int bh, qt_rank;
+    if (nbh % 8 == 0) {
+      const int xcd = blockIdx.x % 8, j = blockIdx.x / 8, hpx = nbh / 8;
+      bh = xcd * hpx + j % hpx;
+      qt_rank = j / hpx;
+    } else {
+      bh = blockIdx.x % nbh;
+      qt_rank = blockIdx.x / nbh;
+    }
+    const int qt = a.n_qt - 1 - qt_rank;
+    const int b = bh / a.h, head = bh % a.h;
+    const int64_t q0 = static_cast<int64_t>(qt) * BM;
+    const int64_t qw = q0 + wv * 32;
+    const int64_t tq = qw + col;
+    const bool qvalid = tq < a.S;
+
+    int64_t kend = q0 + BM;
+    if (kend > a.S) kend = a.S;
+    const int nkb = static_cast<int>((kend + BN - 1) / BN);
+    Regs R;
+    load_block(a, b, head, 0, R);
+    State st_;
+    begin(a, b, head, tq, qvalid, st_);
+
+    const int nall = blocks_for_all(q0, nkb);
     int kb = 0;
     // Unrolled by two so that each step names its buffer as a constant offset
     // and the LDS addresses fold into immediates (single-term operands only:
@@ -464,22 +490,59 @@ struct Fwd {
     }
     for (; kb < nall; ++kb) step<true>(a, kb, nkb, b, head, qw, tq, lds + (kb & 1) * BUF_BYTES, R, st_);
     for (; kb < nkb; ++kb) step<false>(a, kb, nkb, b, head, qw, tq, lds + (kb & 1) * BUF_BYTES, R, st_);
+    finish(a, b, head, tq, qvalid, st_);
+  }
 
-    if (qvalid) {
-      const float inv = 1.0f / st_.l_run;
-      float* op = a.o + ((b * a.S + tq) * a.h + head) * DV;
-#pragma unroll
-      for (int n = 0; n < NO; ++n)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x4 w = {st_.o[n][4 * g] * inv, st_.o[n][4 * g + 1] * inv, st_.o[n][4 * g + 2] * inv,
-                     st_.o[n][4 * g + 3] * inv};
-          *reinterpret_cast<f32x4*>(op + n * 32 + 8 * g + 4 * hf) = w;
-        }
-      if (hf == 0)
-        a.lse[(static_cast<int64_t>(b) * a.h + head) * a.S + tq] =
-            (st_.m_run + log2f(st_.l_run)) * 0.69314718055994531f;
+  // ------------------------------------------------ key blocks given as LDS images
+  // The fused forward's attention: key block kb of (b, head) is a ready-made
+  // image of the LDS buffer (K, rope band and V rows, padded and swizzled as
+  // store_block leaves them) at img + kb * BUF_BYTES, so each block is one
+  // contiguous global -> LDS copy (1 KB per wavefront instruction, no staging
+  // registers), issued one block ahead into the other buffer.
+  static constexpr int IMG_LOADS = BUF_BYTES / 1024;
+  static_assert(BUF_BYTES % 1024 == 0, "whole 1 KB copies");
+
+  __device__ static void issue_image(const char* img_block, char* buf, int wv) {
+    const int lane = threadIdx.x % kWave;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(img_block), 0, BUF_BYTES, 0x00020000);
+    for (int j = wv; j < IMG_LOADS; j += NW) load_lds16(rs, buf + j * 1024, j * 1024 + 16 * lane);
+  }
+
+  template <bool ALL>
+  __device__ static void image_step(const FwdArgs& a, const char* img, int kb, int nkb, int wv, int64_t qw,
+                                    int64_t tq, char* cur, char* nxt, State& st_) {
+    dma_barrier();  // block kb has landed in `cur`; every wavefront is done with `nxt`
+    if (kb + 1 < nkb) issue_image(img + static_cast<int64_t>(kb + 1) * BUF_BYTES, nxt, wv);
+    const int64_t key0 = static_cast<int64_t>(kb) * BN;
+    if (ALL || key0 <= qw + 31) compute_block(a, cur, key0, qw, tq, st_);
+  }
+
+  // Query tile qt of (b, head) against the images at img (that head's block 0).
+  __device__ static void run_images(const FwdArgs& a, const char* img, int b, int head, int qt, char* lds) {
+    static_assert(!LO8, "images hold single-plane K and V");
+    const int lane = threadIdx.x % kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    const int64_t q0 = static_cast<int64_t>(qt) * BM;
+    const int64_t qw = q0 + wv * 32;
+    const int64_t tq = qw + lane % 32;
+    const bool qvalid = tq < a.S;
+    int64_t kend = q0 + BM;
+    if (kend > a.S) kend = a.S;
+    const int nkb = static_cast<int>((kend + BN - 1) / BN);
+    issue_image(img, lds, wv);
+    State st_;
+    begin(a, b, head, tq, qvalid, st_);
+    const int nall = blocks_for_all(q0, nkb);
+    int kb = 0;
+    for (; kb + 1 < nall; kb += 2) {
+      image_step<true>(a, img, kb, nkb, wv, qw, tq, lds, lds + BUF_BYTES, st_);
+      image_step<true>(a, img, kb + 1, nkb, wv, qw, tq, lds + BUF_BYTES, lds, st_);
     }
+    for (; kb < nkb; ++kb)
+      image_step<false>(a, img, kb, nkb, wv, qw, tq, lds + (kb & 1) * BUF_BYTES, lds + ((kb + 1) & 1) * BUF_BYTES,
+                        st_);
+    finish(a, b, head, tq, qvalid, st_);
   }
 };
 
@@ -509,6 +572,323 @@ hipError_t fwd_t(const Shape& s, const void* q, const void* kn, const void* kp, 
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ fused forward
+// The up-projection fused with the attention, in one launch [LAGA §4.7
+// Limitations, fused up-projection kernel; §8 Discussion, open direction (i)].
+// Operands are fp16 (the forward-only precision mode): a prep kernel writes
+// the normalised latent L (RMSNorm of §2.1, rounded to fp16) and the head
+// shard W_r of W_kv_b converted to fp16; then every workgroup of the fused
+// kernel takes a ticket from an atomic counter and runs one task:
+//  * producer (tickets first): K/V of 256 keys x one head, C^T = W_r[head] L^T
+//    (fp16 matrix-core products, both operands copied global -> LDS through a
+//    ring of three stages), written -- with the keys' k_pe rows -- as four
+//    images of the attention's LDS key-block buffer, then counted as done for
+//    that head (release at device scope);
+//  * consumer (tickets after every producer ticket): the attention of one
+//    256-query tile of one head, heaviest tiles first, which waits until every
+//    producer of its head is done (acquire) and then streams the images with
+//    plain global -> LDS copies.
+// A consumer waits only for producer tasks, and every producer ticket is
+// handed out before any consumer ticket, so each producer a consumer waits
+// for is already running on some CU, and producers wait for nothing: every
+// wait ends.  A bounded spin backs that up: past it the consumer writes NaN
+// outputs and sets the error word instead of spinning on.  The tickets are
+// split into 8 independent queues by workgroup id modulo 8 (when the batch
+// x heads count allows), one per XCD under the round-robin dispatch, so one
+// head's producers and consumers share an L2.
+typedef Fwd<bf16_t, MmaF16, MmaBf16, 1, 128, 64, 128, 8> FusedAttn;
+constexpr int kFusedKeys = 256;          // keys per producer task
+constexpr unsigned kSpinLimit = 1u << 20;  // polls (about 0.2 us apart) before a consumer gives up
+
+struct FusedArgs {
+  FwdArgs f;  // q, o, lse, sizes and the score scale of the attention
+  const half_t* l16;   // [T, 512] fp16 normalised latent
+  const half_t* w16;   // [h, 256, 512] fp16 head shard of W_kv_b
+  const bf16_t* k_pe;  // [T, 64]
+  char* img;           // [B*h][nkb_img][BUF_BYTES] key-block images
+  int* tickets;        // [8]
+  int* err;            // set when a consumer gave up waiting
+  int* done;           // [B*h] producer tasks finished per head
+  int n_kt, nkb_img, parts, hpp, prod_pp;
+};
+
+template <int BKP, int NSTP>
+struct KvProducerT {
+  typedef FusedAttn Kn;
+  static constexpr int DKV = 512, C = 256;
+  static constexpr int LINE = BKP * 2;       // bytes of one source row per step
+  static constexpr int SPR = LINE / 16;      // 16-byte slots per row and step
+  static constexpr int OPB = 256 * LINE;     // one operand per stage: W rows, then L rows
+  static constexpr int STAGE = 2 * OPB;
+  static constexpr int LDS_BYTES = NSTP * STAGE;
+  static constexpr int NSTEP = DKV / BKP;
+  static constexpr int ROWB = DKV * 2;       // bytes of one source row
+  static constexpr int IPO = OPB / 1024 / 8; // 1 KB copies per wavefront, operand and stage
+  static constexpr int IPS = 2 * IPO;
+  static_assert(IPO * 8 * 1024 == OPB, "whole copies for every wavefront");
+  static_assert(SPR == 4 || SPR == 8, "64- or 128-byte rows");
+  // 16-byte slot c of LDS row r holds source chunk c ^ swz(r): a half-wavefront
+  // reading 32 rows at one k offset then spreads over all banks.
+  __device__ static int swz(int r) { return SPR == 4 ? (r >> 2) & 3 : (r >> 1) & 7; }
+
+  __device__ static void run(const FusedArgs& a, int b, int head, int kt, char* lds) {
+    const int lane = threadIdx.x % kWave, hf = lane / 32;
+    const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    const int wo = wv / 4, wk = wv % 4;  // outputs wo*128 + [0,128), keys wk*64 + [0,64)
+    const int64_t key_lo = static_cast<int64_t>(kt) * kFusedKeys;
+    const int nvalid = static_cast<int>(a.f.S - key_lo < kFusedKeys ? a.f.S - key_lo : kFusedKeys);
+    const char* wsrc = reinterpret_cast<const char*>(a.w16 + static_cast<int64_t>(head) * C * DKV);
+    const char* lsrc = reinterpret_cast<const char*>(a.l16 + (static_cast<int64_t>(b) * a.f.S + key_lo) * DKV);
+    int voff[IPO];
+#pragma unroll
+    for (int i = 0; i < IPO; ++i) {
+      const int q = (i * 8 + wv) * kWave + lane, row = q / SPR;
+      voff[i] = row * ROWB + ((q % SPR) ^ swz(row)) * 16;
+    }
+    // Step `it` into stage sb; steps past the end copy nothing (empty range)
+    // so that every step issues the same number of copies.
+    auto issue = [&](int it, char* sb) {
+      const bool live = it < NSTEP;
+      const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(wsrc + (live ? it * LINE : 0)), 0, live ? 256 * ROWB : 0, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(lsrc + (live ? it * LINE : 0)), 0, live ? nvalid * ROWB : 0, 0x00020000);
+#pragma unroll
+      for (int i = 0; i < IPO; ++i) load_lds16(rw, sb + (i * 8 + wv) * 1024, voff[i]);
+#pragma unroll
+      for (int i = 0; i < IPO; ++i) load_lds16(rl, sb + OPB + (i * 8 + wv) * 1024, voff[i]);
+    };
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.f;
+    // Fragment rows: W row wo*128 + 32 x + lane%32, L row wk*64 + 32 y + lane%32,
+    // k = 16 s + 8 hf + [0, 8) of the step: slot 2 s + hf.
+    const int sw = swz(lane % 32);
+    const int oa = (wo * 128 + lane % 32) * LINE, ob = OPB + (wk * 64 + lane % 32) * LINE;
+    auto compute = [&](const char* st) {
+#pragma unroll
+      for (int s = 0; s < BKP / 16; ++s) {
+        const int slot = ((2 * s + hf) ^ sw) * 16;
+        half8 af[4], bfr[2];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) af[x] = *reinterpret_cast<const half8*>(st + oa + x * 32 * LINE + slot);
+#pragma unroll
+        for (int y = 0; y < 2; ++y) bfr[y] = *reinterpret_cast<const half8*>(st + ob + y * 32 * LINE + slot);
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+          for (int y = 0; y < 2; ++y) acc[x][y] = MmaF16::mma(af[x], bfr[y], acc[x][y]);
+      }
+    };
+
+#pragma unroll
+    for (int it = 0; it < NSTP - 1; ++it) issue(it, lds + it * STAGE);
+    for (int it0 = 0; it0 < NSTEP; it0 += NSTP) {
+#pragma unroll
+      for (int j = 0; j < NSTP; ++j) {
+        const int it = it0 + j;
+        if (it >= NSTEP) break;
+        wait_vmcnt<(NSTP - 2) * IPS>();  // this wavefront's copies of step `it` have landed
+        __syncthreads();                 // so have every wavefront's; stage (it - 1) % NSTP is free
+        issue(it + NSTP - 1, lds + ((j + NSTP - 1) % NSTP) * STAGE);
+        compute(lds + j * STAGE);
+      }
+    }
+    wait_vmcnt<0>();  // no copy into LDS outlives the task
+
+    // acc[x][y][r]: output wo*128 + 32 x + 8 (r/4) + 4 hf + r%4, key wk*64 + 32 y + lane%32.
+    // The four block images are assembled in LDS two at a time (keys
+    // 128 p .. 128 p + 127): four consecutive outputs of one key go in as one
+    // 8-byte write into the K rows (padded) or the V rows (16-byte chunks
+    // swizzled), the keys' k_pe rows into the rope band; then the two images,
+    // contiguous in global memory, leave as whole 16-byte-per-lane stores.
+    static_assert(2 * Kn::BUF_BYTES <= LDS_BYTES, "two images fit in the stage ring");
+    char* img = a.img + ((static_cast<int64_t>(b) * a.f.h + head) * a.nkb_img + kt * (kFusedKeys / BN)) *
+                            static_cast<int64_t>(Kn::BUF_BYTES);
+    const bf16_t* kp = a.k_pe + (static_cast<int64_t>(b) * a.f.S + key_lo) * 64;
+    __syncthreads();  // every wavefront is done reading the stages
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      if (wk / 2 == p) {
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+          const int key = (wk % 2) * 64 + 32 * y + lane % 32;  // within this pair of blocks
+          char* blk = lds + (key / BN) * Kn::BUF_BYTES;
+          const int row = key % BN;
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int o = 32 * x + 8 * g + 4 * hf;  // within this wavefront's 128 outputs
+              typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+              const half4 h4 = {static_cast<half_t>(acc[x][y][4 * g]), static_cast<half_t>(acc[x][y][4 * g + 1]),
+                                static_cast<half_t>(acc[x][y][4 * g + 2]), static_cast<half_t>(acc[x][y][4 * g + 3])};
+              char* dst = wo == 0 ? blk + (row * Kn::LDK + o) * 2
+                                  : blk + Kn::OFF_V + row * Kn::LDV * 2 + swz_block(row, o / 8) * 16 + (o % 8) * 2;
+              *reinterpret_cast<half4*>(dst) = h4;
+            }
+        }
+      }
+      // The rope band of the pair: 128 keys x 8 chunks (zeros past the sequence).
+#pragma unroll
+      for (int i = 0; i < 128 * 8 / 512; ++i) {
+        const int c = i * 512 + static_cast<int>(threadIdx.x), key = c / 8, ch = c % 8;
+        const int gk = p * 128 + key;
+        const u32x4 v = gk < nvalid ? *reinterpret_cast<const u32x4*>(kp + gk * 64 + ch * 8) : u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(lds + (key / BN) * Kn::BUF_BYTES + Kn::OFF_R + (key % BN) * Kn::LDR * 2 + ch * 16) =
+            v;
+      }
+      __syncthreads();
+      char* gdst = img + static_cast<int64_t>(2 * p) * Kn::BUF_BYTES;
+      constexpr int NCH = 2 * Kn::BUF_BYTES / 16;
+      for (int c = static_cast<int>(threadIdx.x); c < NCH; c += 512)
+        *reinterpret_cast<u32x4*>(gdst + c * 16) = *reinterpret_cast<const u32x4*>(lds + c * 16);
+      __syncthreads();  // the LDS images are free again
+    }
+    // Every store of this task is complete before the head's count goes up.
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    __syncthreads();
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_add(a.done + b * a.f.h + head, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+};
+
+typedef KvProducerT<32, 3> KvProducer;
+constexpr int kFusedLds = KvProducer::LDS_BYTES > 2 * FusedAttn::BUF_BYTES ? KvProducer::LDS_BYTES
+                                                                           : 2 * FusedAttn::BUF_BYTES;
+
+__global__ __launch_bounds__(8 * kWave, 2) void attn_fwd_fused_kernel(FusedArgs a) {
+  // One shared array for everything, the ticket words at its end: with a
+  // second __shared__ object the compiler starts tracking the global -> LDS
+  // copies itself and waits for each stage's copies right after issuing them
+  // (the explicit waits before each barrier order them here).
+  __shared__ __attribute__((aligned(1024))) char lds[kFusedLds + 16];
+  int* sh = reinterpret_cast<int*>(lds + kFusedLds);
+  const int part = a.parts == 8 ? static_cast<int>(blockIdx.x % 8) : 0;
+  if (threadIdx.x == 0)
+    sh[0] = __hip_atomic_fetch_add(a.tickets + part, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int t = __builtin_amdgcn_readfirstlane(sh[0]);
+  const int bh0 = part * a.hpp;
+  // Producers in key-tile order over the queue's heads (the heads of one key
+  // tile share its latent rows in L2); consumers heaviest tile first,
+  // interleaved over the heads.
+  if (t < a.prod_pp) {
+    const int bh = bh0 + t % a.hpp;
+    KvProducer::run(a, bh / a.f.h, bh % a.f.h, t / a.hpp, lds);
+    return;
+  }
+  const int c = t - a.prod_pp;
+  const int bh = bh0 + c % a.hpp, qt = a.f.n_qt - 1 - c / a.hpp;
+  const int b = bh / a.f.h, head = bh % a.f.h;
+  if (threadIdx.x == 0) {
+    int ok = 1;
+    unsigned spins = 0;
+    // Relaxed polls, then one acquire fence: the caches are invalidated once,
+    // not on every poll.
+    while (__hip_atomic_load(a.done + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.n_kt) {
+      if (++spins > kSpinLimit) {
+        ok = 0;
+        __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    sh[1] = ok;
+  }
+  __syncthreads();
+  if (!sh[1]) {  // never expected: mark the tile's outputs instead of hanging
+    const int64_t q0 = static_cast<int64_t>(qt) * FusedAttn::BM;
+    for (int i = threadIdx.x; i < FusedAttn::BM * 128; i += 8 * kWave) {
+      const int64_t tq = q0 + i / 128;
+      if (tq >= a.f.S) continue;
+      a.f.o[((b * a.f.S + tq) * a.f.h + head) * 128 + i % 128] = __builtin_nanf("");
+      if (i % 128 == 0) a.f.lse[(static_cast<int64_t>(b) * a.f.h + head) * a.f.S + tq] = __builtin_nanf("");
+    }
+    return;
+  }
+  FusedAttn::run_images(a.f, a.img + static_cast<int64_t>(bh) * a.nkb_img * FusedAttn::BUF_BYTES, b, head, qt,
+                        lds);
+}
+
+// The fused forward's prep: workgroups [0, nb_norm) normalise 4 latent rows
+// each into fp16 (one wavefront per row, the RMSNorm of the plain forward);
+// the next nb_w convert 2048 elements each of the W_kv_b head shard to fp16;
+// the last one clears the tickets, the error word and the per-head counts.
+__global__ __launch_bounds__(256) void fused_prep_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ gamma,
+                                                         half_t* __restrict__ l16, int64_t T, float eps, int nb_norm,
+                                                         const bf16_t* __restrict__ w, half_t* __restrict__ w16,
+                                                         int64_t n_w8, int nb_w, int* __restrict__ counters,
+                                                         int n_cnt) {
+  const int blk = static_cast<int>(blockIdx.x);
+  if (blk < nb_norm) {
+    const int lane = threadIdx.x % kWave;
+    const int64_t t = static_cast<int64_t>(blk) * 4 + threadIdx.x / kWave;
+    if (t >= T) return;
+    const u16x8 xr = *reinterpret_cast<const u16x8*>(x + t * 512 + lane * 8);
+    const u16x8 gr = *reinterpret_cast<const u16x8*>(gamma + lane * 8);
+    float v[8];
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      v[j] = bf16_to_f32(xr[j]);
+      ss += v[j] * v[j];
+    }
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / 512.0f + eps);
+    half8 out;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) out[j] = static_cast<half_t>(bf16_to_f32(gr[j]) * (v[j] * r));
+    *reinterpret_cast<half8*>(l16 + t * 512 + lane * 8) = out;
+  } else if (blk < nb_norm + nb_w) {
+    const int64_t i = static_cast<int64_t>(blk - nb_norm) * 256 + threadIdx.x;
+    if (i >= n_w8) return;
+    const u16x8 wr = *reinterpret_cast<const u16x8*>(w + i * 8);
+    half8 out;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) out[j] = static_cast<half_t>(bf16_to_f32(wr[j]));
+    *reinterpret_cast<half8*>(w16 + i * 8) = out;
+  } else {
+    for (int i = threadIdx.x; i < n_cnt; i += 256) counters[i] = 0;
+  }
+}
+
+// Workspace of the fused forward: counters | L16 | W16 | images.
+struct FusedLayout {
+  size_t cnt, l16, w16, img, total;
+  int n_cnt, n_kt, nkb_img;
+};
+
+size_t r256(size_t b) { return (b + 255) & ~size_t(255); }
+
+FusedLayout fused_layout(const Shape& s) {
+  FusedLayout L;
+  L.n_kt = static_cast<int>((s.S + kFusedKeys - 1) / kFusedKeys);
+  L.nkb_img = L.n_kt * (kFusedKeys / BN);
+  L.n_cnt = 16 + static_cast<int>(s.B) * s.h;
+  size_t off = 0;
+  L.cnt = off;
+  off += r256(static_cast<size_t>(L.n_cnt) * 4);
+  L.l16 = off;
+  off += r256(static_cast<size_t>(s.T) * 512 * 2);
+  L.w16 = off;
+  off += r256(static_cast<size_t>(s.h) * 256 * 512 * 2);
+  L.img = off;
+  off += static_cast<size_t>(s.B) * s.h * L.nkb_img * FusedAttn::BUF_BYTES;
+  L.total = off;
+  return L;
+}
+
+bool fused_supported(const Shape& s) {
+  return s.bf16 && !s.split && s.d_kv == 512 && s.d_nope == 128 && s.d_rope == 64 && s.d_v == 128;
+}
+
 }  // namespace
 
 hipError_t launch_attn_fwd(const Shape& s, const void* q, const void* kn, const void* kp, const void* v,
@@ -520,6 +900,54 @@ hipError_t launch_attn_fwd(const Shape& s, const void* q, const void* kn, const 
   if (!s.bf16 && s.d_nope == 32 && s.d_rope == 16 && s.d_v == 32)
     return fwd_t<float, MmaF32, MmaF32, 1, 32, 16, 32, 4>(s, q, kn, kp, v, o, lse, st);
   return hipErrorInvalidValue;
+}
+
+}  // namespace laga
+
+namespace laga {
+
+size_t fused_fwd_workspace_bytes(const Shape& s) { return fused_supported(s) ? fused_layout(s).total : 0; }
+
+hipError_t launch_attn_fwd_fused(const Shape& s, const void* q, const void* latent, const void* gamma,
+                                 const void* k_pe, const void* w, float* o, float* lse, void* workspace,
+                                 hipStream_t st) {
+  if (!fused_supported(s)) return hipErrorNotSupported;
+  const FusedLayout L = fused_layout(s);
+  char* ws = static_cast<char*>(workspace);
+  int* counters = reinterpret_cast<int*>(ws + L.cnt);
+  half_t* l16 = reinterpret_cast<half_t*>(ws + L.l16);
+  half_t* w16 = reinterpret_cast<half_t*>(ws + L.w16);
+  const int nb_norm = static_cast<int>((s.T + 3) / 4);
+  const int64_t n_w8 = static_cast<int64_t>(s.h) * 256 * 512 / 8;
+  const int nb_w = static_cast<int>((n_w8 + 255) / 256);
+  const bf16_t* wr = static_cast<const bf16_t*>(w) + static_cast<int64_t>(s.head_lo) * 256 * 512;
+  hipLaunchKernelGGL(fused_prep_kernel, dim3(static_cast<unsigned>(nb_norm + nb_w + 1)), dim3(256), 0, st,
+                     static_cast<const bf16_t*>(latent), static_cast<const bf16_t*>(gamma), l16, s.T, s.eps, nb_norm,
+                     wr, w16, n_w8, nb_w, counters, L.n_cnt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  FusedArgs a;
+  a.f.q = q; a.f.k_nope = nullptr; a.f.k_pe = nullptr; a.f.v = nullptr; a.f.o = o; a.f.lse = lse;
+  a.f.S = s.S; a.f.B = static_cast<int>(s.B); a.f.h = s.h;
+  a.f.plane_k = 0; a.f.plane_v = 0;
+  a.f.n_qt = static_cast<int>((s.S + FusedAttn::BM - 1) / FusedAttn::BM);
+  a.f.scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(s.d_nope + s.d_rope));
+  a.l16 = l16; a.w16 = w16; a.k_pe = static_cast<const bf16_t*>(k_pe);
+  a.img = ws + L.img;
+  a.tickets = counters;
+  a.err = counters + 8;
+  a.done = counters + 16;
+  a.n_kt = L.n_kt;
+  a.nkb_img = L.nkb_img;
+  const int nbh = static_cast<int>(s.B) * s.h;
+  a.parts = nbh % 8 == 0 ? 8 : 1;
+  a.hpp = nbh / a.parts;
+  a.prod_pp = a.hpp * a.n_kt;
+  const int64_t grid = static_cast<int64_t>(a.parts) * a.hpp * (a.n_kt + a.f.n_qt);
+  if (grid >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attn_fwd_fused_kernel, dim3(static_cast<unsigned>(grid)), dim3(8 * kWave), 0, st, a);
+  return hipGetLastError();
 }
 
 }  // namespace laga

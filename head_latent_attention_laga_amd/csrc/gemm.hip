@@ -421,12 +421,6 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, void* lds, int 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(lds), 16, voff, soff, 0, 0);
 }
 
-// s_waitcnt vmcnt(N) with expcnt and lgkmcnt left at their maximum.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 // k-contiguous operand: NP planes of Src, ROWS rows per tile.
 template <int NP_, class Src, int ROWS_>

@@ -26,6 +26,15 @@ hipError_t launch_kv_up(const Shape& s, const float* L, const void* w, void* k_n
 hipError_t launch_attn_fwd(const Shape& s, const void* q, const void* k_nope, const void* k_pe,
                            const void* v, float* o, float* lse, hipStream_t st);
 
+// Fused forward (fp16 operands, bfloat16 inputs at the V3 head dims): the
+// latent's RMSNorm, the head-shard up-projection and the attention in two
+// launches, K/V passing through `workspace` as key-block images.  The error
+// word (int at workspace + 32) is set if a consumer ever gave up waiting.
+size_t fused_fwd_workspace_bytes(const Shape& s);  // 0: unsupported shape
+hipError_t launch_attn_fwd_fused(const Shape& s, const void* q, const void* latent, const void* gamma,
+                                 const void* k_pe, const void* w, float* o, float* lse, void* workspace,
+                                 hipStream_t st);
+
 // Backward pieces.  Workspace carving lives in the API layer.
 // Copies of the bfloat16 inputs that the backward kernels read: exact fp16
 // q16 [T,h,d_qk], do16 [T,h,d_v], kpe16 [T,d_rope] (taken in place of the

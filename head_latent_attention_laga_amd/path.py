@@ -65,6 +65,23 @@ class LagaPath:
         _lib.attn_fwd(self.dims, x["q"], out["k_nope"], x["k_pe"], out["v"], out["o"], out["lse"], stream)
         return out
 
+    def alloc_fused(self):
+        """Outputs and workspace of the fused forward (fp16 operands, bf16 V3 dims only)."""
+        B, S, h = self.B, self.S, self.h
+        ws = _lib.attn_fwd_fused_workspace_bytes(self.dims)
+        if ws == 0:
+            raise _lib.LagaError("laga_attn_fwd_fused_workspace_bytes", 2, "dims rejected by the fused forward")
+        return dict(o=self._empty((B, S, h, self.d_v)), lse=self._empty((B, h, S)),
+                    workspace=torch.empty((ws,), dtype=torch.uint8, device=self.device))
+
+    def forward_fused(self, x, out=None, stream=None):
+        """o and lse from one laga_attn_fwd_fused call (norm, up-projection and
+        attention fused; K/V never leave the library's workspace)."""
+        out = out or self.alloc_fused()
+        _lib.attn_fwd_fused(self.dims, x["q"], x["latent"], x["gamma"], x["k_pe"], x["w_kv_b"], out["o"],
+                            out["lse"], out["workspace"], stream)
+        return out
+
     def alloc_absorbed(self):
         """Buffers of the absorbed-form (B2) forward: its n_h*d_kv-wide intermediates
         q_abs (fp16) and acc (float32), the fp16 key rows kx, and o, lse."""

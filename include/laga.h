@@ -141,6 +141,32 @@ laga_status laga_attn_fwd(const laga_dims* dims, const void* q, const void* k_no
                           const void* k_pe, const void* v, float* o, float* lse, void* stream);
 
 /*
+ * The forward with the up-projection fused into the attention [LAGA §4.7
+ * Limitations, fused up-projection kernel; §8 Discussion, open direction (i)]:
+ * o and lse as laga_latent_norm + laga_kv_up + laga_attn_fwd compute them,
+ * from the raw latent, without materialising k_nope / v in their own layout.
+ * Only for LAGA_BF16 inputs at the V3 head dims with LAGA_OPERANDS_FP16 (the
+ * forward-only mode: the normalised latent and W_kv_b's head shard are rounded
+ * to fp16, so |gamma * latent / rms| and |W_kv_b| must stay below 65504);
+ * anything else returns LAGA_ERR_UNSUPPORTED.
+ * Layouts: q [B,S,h,d_qk], latent [B,S,d_kv], gamma [d_kv], k_pe [B,S,d_rope],
+ * w_kv_b [n_h, d_nope+d_v, d_kv] (all bfloat16; rows r*h .. r*h+h-1 of w_kv_b
+ * read); o [B,S,h,d_v] and lse [B,h,S] float32.
+ * workspace: device memory of at least
+ * laga_attn_fwd_fused_workspace_bytes(dims) bytes (16-byte aligned), owned by
+ * the caller, whose contents need no initialisation and are overwritten:
+ * 672 bytes per token and local head (K, V and rope rows, padded as the
+ * attention's LDS tiles) with S rounded up to 256, 1 KB per token and 256 KB
+ * per local head (197 MB at S = 16384, h = 16).  Two launches on `stream`; calls that share a
+ * workspace must not overlap in time.
+ */
+size_t laga_attn_fwd_fused_workspace_bytes(const laga_dims* dims);
+laga_status laga_attn_fwd_fused(const laga_dims* dims, const void* q, const void* latent,
+                                const void* gamma, const void* k_pe, const void* w_kv_b,
+                                float* o, float* lse, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
  * Absorbed form (B2) forward of the h local heads, the baseline that the
  * pages port from inference to training [LAGA §3.2 (B2), Fig. 2; §4.3 the
  * memory it costs].  W_kv_b's K half is folded into the query, attention runs

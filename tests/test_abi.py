@@ -134,6 +134,39 @@ def test_backward_argument_checks(lib):
     assert lib.laga_attn_bwd(ctypes.byref(d16), *args, ctypes.c_size_t(1 << 40), None) == UNSUPPORTED
 
 
+def test_fused_forward_checks_on_the_host(lib):
+    """laga_attn_fwd_fused: fp16 operands at the bf16 V3 dims only, and every
+    pointer, alignment and workspace check before any HIP call."""
+    d = v3(precision=_lib.LAGA_OPERANDS_FP16)
+    need = lib.laga_attn_fwd_fused_workspace_bytes(ctypes.byref(d))
+    assert need > 0
+    assert lib.laga_attn_fwd_fused_workspace_bytes(ctypes.byref(v3())) == 0          # split operands
+    assert lib.laga_attn_fwd_fused_workspace_bytes(ctypes.byref(tiny())) == 0        # float32 dims
+    assert lib.laga_attn_fwd_fused_workspace_bytes(ctypes.byref(v3(S=0))) == 0       # invalid dims
+    args = [FAKE] * 7
+    ok = (FAKE, ctypes.c_size_t(need), None)
+    assert lib.laga_attn_fwd_fused(ctypes.byref(v3()), *args, *ok) == UNSUPPORTED
+    assert lib.laga_attn_fwd_fused(ctypes.byref(tiny()), *args, *ok) == UNSUPPORTED
+    assert lib.laga_attn_fwd_fused(None, *args, *ok) == INVALID
+    for slot in range(7):
+        a = list(args)
+        a[slot] = None
+        assert lib.laga_attn_fwd_fused(ctypes.byref(d), *a, *ok) == INVALID
+        a[slot] = MISALIGNED
+        assert lib.laga_attn_fwd_fused(ctypes.byref(d), *a, *ok) == ALIGN
+    assert lib.laga_attn_fwd_fused(ctypes.byref(d), *args, FAKE, ctypes.c_size_t(need - 1), None) == WORKSPACE
+    assert lib.laga_attn_fwd_fused(ctypes.byref(d), *args, None, ctypes.c_size_t(need), None) == WORKSPACE
+    assert lib.laga_attn_fwd_fused(ctypes.byref(d), *args, MISALIGNED, ctypes.c_size_t(need), None) == ALIGN
+
+
+def test_fused_workspace_is_linear_in_the_sequence(lib):
+    def ws(S, **kw):
+        return lib.laga_attn_fwd_fused_workspace_bytes(ctypes.byref(v3(S=S, precision=_lib.LAGA_OPERANDS_FP16, **kw)))
+    a, b, c = ws(4096), ws(8192), ws(12288)
+    assert b - a == c - b > 0
+    assert ws(16384, n_h=128, sp_size=8) < 200e6
+
+
 def test_noalloc_scratch_size_matches_header():
     import re
     text = open(_lib.HEADER).read()
