@@ -103,6 +103,220 @@ def calibration_copy(nbytes: int = 256 << 20, reps: int = 3):
     del src, dst
 
 
+# ------------------------------------------------------------ profile summaries
+# Bench stage -> (alternatives, each a list of substrings that must all appear in the
+# profiler's kernel name: demangled, or mangled where the profiler could not demangle it;
+# source file).
+_N = "head_latent_attention_laga_amd/csrc/"
+PROFILE_KERNELS = {
+    "rmsnorm_fwd": ([["rmsnorm_fwd_kernel"]], _N + "norm.hip"),
+    "kv_up": ([["gemm_dma_kernel", "EpiKvUp<_Float16, 2"], ["gemm_dma_kernel", "EpiKvUpIDF16_Li2E"]], _N + "gemm.hip"),
+    "kv_up_fp16": ([["gemm_dma_kernel", "EpiKvUp<_Float16, 1"], ["gemm_dma_kernel", "EpiKvUpIDF16_Li1E"]],
+                   _N + "gemm.hip"),
+    "attn_fwd": ([["attn_fwd_kernel<", "MmaBf16, 2, 128"]], _N + "attn_fwd.hip"),
+    "attn_fwd_fp16": ([["attn_fwd_kernel<", "MmaBf16, 1, 128"]], _N + "attn_fwd.hip"),
+    "fused_prep": ([["fused_prep_kernel"]], _N + "attn_fwd.hip"),
+    "attn_fwd_fused": ([["attn_fwd_fused_kernel"]], _N + "attn_fwd.hip"),
+    "bwd_delta": ([["bwd_prep_kernel"]], _N + "attn_bwd.hip"),
+    "do_convert": ([["do_convert_kernel"]], _N + "attn_bwd.hip"),
+    "attn_bwd_dkdv": ([["dkdv_kernel<"], ["dkdv_kernelIDF16_NS_6MmaF16ELi2"]], _N + "attn_bwd.hip"),
+    "attn_bwd_dq": ([["dq_kernel<"]], _N + "attn_bwd_dq.hip"),
+    "fold_dL": ([["gemm_dma_kernel<", "DKC<2, unsigned short, 64>"]], _N + "gemm.hip"),
+    "fold_dW": ([["gemm_dma_kernel<", "DRC<2, 128>, laga::(anonymous namespace)::DRC<2, 128>"]], _N + "gemm.hip"),
+    "rmsnorm_bwd": ([["rmsnorm_bwd_kernel"]], _N + "norm.hip"),
+    "absorb_q": ([["gemm_dma_kernel<", "EpiHalf"]], _N + "gemm.hip"),
+    "absorbed_attn": ([["absorbed_attn_kernel"]], _N + "absorbed.hip"),
+    "unabsorb_o": ([["gemm_dma_kernel<", "DKC<1, float, 256>"]], _N + "gemm.hip"),
+}
+# Kernels of the forward-only path run once per forward-only workload; their grid
+# (work-items) tells the workloads apart.
+FWD_ONLY_GRIDS = {
+    "kv_up_fp16": {1048576: "S=16384 h=16", 262144: "S=4096 h=16", 2097152: "S=4096 h=128"},
+    "attn_fwd_fp16": {524288: "S=16384 h=16", 131072: "S=4096 h=16", 1048576: "S=4096 h=128"},
+    "attn_fwd_fused": {1048576: "S=16384 h=16", 262144: "S=4096 h=16", 2097152: "S=4096 h=128"},
+    "fused_prep": {2359552: "S=16384 h=16", 524544: "S=4096 h=16", 1310976: "S=4096 h=128"},
+    "rmsnorm_fwd": {1048576: "S=16384", 262144: "S=4096"},
+}
+
+
+PROFILE_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 {opts} --output-format csv "
+               "-d $GRAFT_REPO_ROOT/gpurun_out/{d} -o {o} -- python3 $GRAFT_REPO_ROOT/bench.py {args}")
+PMC_ARGS = "--steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy"
+KT_ARGS = "--steps 10 --warmup 5 --no-cpu-baseline"
+COUNTER_PASSES = {
+    "pmc_a": "SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_VALU "
+             "SQ_ACTIVE_INST_LDS SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE",
+    "pmc_b": "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_SALU "
+             "SQ_WAVES GRBM_GUI_ACTIVE",
+}
+
+
+def profile_stage(kernel_name: str):
+    for stage, (alts, _) in PROFILE_KERNELS.items():
+        if any(all(x in kernel_name for x in subs) for subs in alts):
+            return stage
+    return None
+
+
+def stage_label(stage: str, grid: int) -> str:
+    w = FWD_ONLY_GRIDS.get(stage, {}).get(grid)
+    return f"{stage} ({w})" if w else stage
+
+
+def read_counters(path: str):
+    """Per stage label: per dispatch {counter: value} with the dispatch's duration in ns."""
+    import csv
+    import collections
+    disp = collections.defaultdict(dict)
+    for r in csv.DictReader(open(path)):
+        key = (r["Kernel_Name"], r["Dispatch_Id"])
+        disp[key][r["Counter_Name"]] = float(r["Counter_Value"])
+        disp[key]["_ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+        disp[key]["_grid"] = int(r["Grid_Size"])
+    per = collections.defaultdict(list)
+    copies = []
+    stages = {}
+    for (name, _), c in disp.items():
+        if name == "__amd_rocclr_copyBuffer" and c["_grid"] == 131072:
+            copies.append(c)
+        if name not in stages:
+            stages[name] = profile_stage(name)
+        if stages[name]:
+            per[stage_label(stages[name], c["_grid"])].append(c)
+    return per, copies
+
+
+def label_order(per) -> list:
+    order = {st: i for i, st in enumerate(PROFILE_KERNELS)}
+    return sorted(per, key=lambda lb: (order[lb.split(" (")[0]], lb))
+
+
+def summarize_profiles(out_root: str):
+    """Writes profiles/*.md and profiles/traffic.json from the rocprofv3 csv output of
+    the commands named in each summary (kt: kernel trace, pmc_fetch / pmc_write: HBM
+    bytes, pmc_a / pmc_b: instruction and cycle counters), plus bench.json, the JSON
+    line of an unprofiled `python bench.py` on the same box."""
+    import csv
+    import hashlib
+    prof = os.path.join(ROOT, "profiles")
+    title = "B=1 S=16384 h=16 (n_h=128, SP=8), V3 dims, bf16 inputs"
+
+    # Kernel trace: per dispatch, grouped by stage and workload.
+    import collections
+    disp = collections.defaultdict(list)
+    stages = {}
+    for r in csv.DictReader(open(os.path.join(out_root, "kt", "kt_kernel_trace.csv"))):
+        nm = r["Kernel_Name"]
+        if nm not in stages:
+            stages[nm] = profile_stage(nm)
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        lb = stage_label(stages[nm], grid) if stages[nm] else nm.replace("laga::(anonymous namespace)::", "")[:60]
+        disp[lb].append((int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    # The bench line that the profiled run itself printed (kt.log), and its timed launches:
+    # each step kernel runs `warmup` times, then `steps` timed times, then once more
+    # for the step's memory measurement.
+    line = [ln for ln in open(os.path.join(out_root, "kt.log")) if ln.startswith('{"metric"')]
+    prun = json.loads(line[-1]) if line else None
+    L = [f"# Kernel trace: LAGA training step, fp16-operand forward (unfused and fused) and absorbed-form (B2) "
+         f"forward, {title}", "", "Command (on the GPU box):", "", "```",
+         PROFILE_CMD.format(opts="--kernel-trace --stats", d="kt", o="kt", args=KT_ARGS), "```", "",
+         "Per launch, from the trace (`kt_kernel_trace.csv`), in us. For the step's kernels, 'timed' is the mean "
+         "over the launches inside bench.py's timed region and 'bench' the HIP-event mean that the same run "
+         "printed in its JSON line.", "",
+         "| stage | launches | mean | median | min | max | timed | bench |", "|---|---|---|---|---|---|---|---|"]
+    order = {st: i for i, st in enumerate(PROFILE_KERNELS)}
+    for lb in sorted(disp, key=lambda x: (order.get(x.split(" (")[0], 99), x)):
+        v = [d for _, d in sorted(disp[lb])]
+        timed = bench_ms = ""
+        if prun and lb in prun["kernels_ms"]:
+            w, k = prun["warmup"], prun["steps"]
+            if len(v) >= w + k:
+                timed = f"{statistics.mean(v[w:w + k]):.1f}"
+            bench_ms = f"{prun['kernels_ms'][lb] * 1e3:.1f}"
+        L.append(f"| {lb} | {len(v)} | {statistics.mean(v):.1f} | {statistics.median(v):.1f} | {min(v):.1f} | "
+                 f"{max(v):.1f} | {timed} | {bench_ms} |")
+    bench = json.loads(open(os.path.join(out_root, "bench.json")).read().strip().splitlines()[-1])
+    L += ["", "The profiled run's own JSON line (roofline and step):", "", "```",
+          json.dumps({k: prun[k] for k in ("ms_per_step", "value", "tflops_step", "roofline")}) if prun else "none",
+          "```", "", "An unprofiled `python bench.py --no-cpu-baseline` on the same box:", "", "```",
+          "step kernels (ms): " + json.dumps(bench["kernels_ms"]),
+          "forward fp16: " + json.dumps(bench["forward_fp16_operands"]),
+          "absorbed form forward: " + json.dumps(bench.get("absorbed_form_fwd")),
+          f"step {bench['ms_per_step']} ms, {bench['value']} tokens/s, {bench['tflops_step']} TFLOP/s; "
+          f"roofline {json.dumps(bench['roofline'])}", "```", ""]
+    open(os.path.join(prof, "step_v3_s16384_h16_kernel_trace.md"), "w").write("\n".join(L))
+
+    # HBM bytes: FETCH_SIZE and WRITE_SIZE, each scaled by the same counter on the copies.
+    fe, cf = read_counters(os.path.join(out_root, "pmc_fetch", "pmc_counter_collection.csv"))
+    wr, cw = read_counters(os.path.join(out_root, "pmc_write", "pmc_counter_collection.csv"))
+    copy_kib = 256 * 1024
+    sf = copy_kib / statistics.mean(c["FETCH_SIZE"] for c in cf)
+    sw = copy_kib / statistics.mean(c["WRITE_SIZE"] for c in cw)
+    L = [f"# HBM traffic per kernel launch: {title}", "",
+         "Two counter passes (FETCH_SIZE, then WRITE_SIZE), each on its own run:", "", "```",
+         PROFILE_CMD.format(opts="--pmc FETCH_SIZE", d="pmc_fetch", o="pmc", args=PMC_ARGS),
+         PROFILE_CMD.format(opts="--pmc WRITE_SIZE", d="pmc_write", o="pmc", args=PMC_ARGS), "```", "",
+         f"Calibration: `--calibrate-copy` first runs three 256 MiB device copies (`__amd_rocclr_copyBuffer`); per "
+         f"copy FETCH_SIZE read {copy_kib / sf:.1f} KiB and WRITE_SIZE {copy_kib / sw:.1f} KiB against {copy_kib} KiB "
+         f"moved each way, so the scale factors are fetch x{sf:.4f}, write x{sw:.4f}. GB/s divides the scaled bytes "
+         f"by the dispatch's duration in the same (counter-collecting) run.", "",
+         "| stage | launches | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled MB per launch (read + write) | GB/s |",
+         "|---|---|---|---|---|---|"]
+    js = {"copy_scale": {"fetch": sf, "write": sw}, "kernels": {}}
+    for st in label_order(fe):
+        if st not in wr:
+            continue
+        src = PROFILE_KERNELS[st.split(" (")[0]][1]
+        f = statistics.mean(c["FETCH_SIZE"] for c in fe[st])
+        w = statistics.mean(c["WRITE_SIZE"] for c in wr[st])
+        ns = statistics.mean([c["_ns"] for c in fe[st]] + [c["_ns"] for c in wr[st]])
+        b = (f * sf + w * sw) * 1024
+        L.append(f"| {st} | {len(fe[st])} | {f:.1f} | {w:.1f} | {f * sf * 1024 / 1e6:.1f} + {w * sw * 1024 / 1e6:.1f} = "
+                 f"{b / 1e6:.1f} | {b / ns:.0f} |")
+        js["kernels"][st] = {"bytes_per_launch": round(b), "fetch_kib": f, "write_kib": w, "source": src,
+                             "source_sha256": source_digest(src)}
+    open(os.path.join(prof, "hbm_traffic_v3_s16384_h16.md"), "w").write("\n".join(L) + "\n")
+    with open(os.path.join(prof, "traffic.json"), "w") as fh:
+        json.dump(js, fh, indent=1)
+
+    # Instruction and cycle counters.
+    pa, _ = read_counters(os.path.join(out_root, "pmc_a", "pmc_counter_collection.csv"))
+    pb, _ = read_counters(os.path.join(out_root, "pmc_b", "pmc_counter_collection.csv"))
+    L = [f"# Instruction and cycle counters per kernel launch: {title}", "",
+         "Two passes, each on its own run:", "", "```"]
+    for d, cs in COUNTER_PASSES.items():
+        L.append(PROFILE_CMD.format(opts=f"--pmc {cs}", d=d, o="pmc", args=PMC_ARGS))
+    L += ["```", "",
+          "Columns (means over the launches): MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 "
+          "SIMDs), the share of SIMD cycles the matrix cores were busy; clock = GRBM_GUI_ACTIVE / 8 / duration; "
+          "VALU, LDS and any-instruction active and the wait shares are per wave cycle (SQ_ACTIVE_INST_*, "
+          "SQ_WAIT_ANY, SQ_WAIT_INST_ANY over SQ_WAVE_CYCLES); instruction counts are per launch (G = 1e9); "
+          "bank conflicts = SQ_LDS_BANK_CONFLICT cycles, with their share of SQ_LDS_IDX_ACTIVE. Durations are "
+          "those of the counter-collecting run; the clock is left out for launches under 100 us, where the "
+          "counter's window is not the kernel's. Kernels without a workload in parentheses belong to the "
+          "training step (S=16384, h=16) or the absorbed form's forward at that shape.", "",
+          "| stage | launches | us | clock GHz | MFMA busy | MFMA insts | VALU insts | LDS insts | VALU active | "
+          "LDS active | waits (any) | waits (instr.) | bank-conflict cycles |",
+          "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for st in label_order(pa):
+        if st not in pb:
+            continue
+        a = {k: statistics.mean(c[k] for c in pa[st]) for k in pa[st][0]}
+        bb = {k: statistics.mean(c[k] for c in pb[st]) for k in pb[st][0]}
+        cyc = a["GRBM_GUI_ACTIVE"] / 8
+        wc = a["SQ_WAVE_CYCLES"]
+        lds_conf = bb["SQ_LDS_BANK_CONFLICT"]
+        lds_act = bb["SQ_LDS_IDX_ACTIVE"]
+        clock = f"{cyc / a['_ns']:.2f}" if a["_ns"] > 1e5 else "-"
+        L.append(f"| {st} | {len(pa[st])} | {a['_ns'] / 1e3:.1f} | {clock} | "
+                 f"{100 * a['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * 1024):.1f}% | {bb['SQ_INSTS_MFMA'] / 1e9:.3f} G | "
+                 f"{bb['SQ_INSTS_VALU'] / 1e9:.3f} G | {bb['SQ_INSTS_LDS'] / 1e9:.3f} G | "
+                 f"{100 * a['SQ_ACTIVE_INST_VALU'] / wc:.1f}% | {100 * a['SQ_ACTIVE_INST_LDS'] / wc:.1f}% | "
+                 f"{100 * a['SQ_WAIT_ANY'] / wc:.1f}% | {100 * a['SQ_WAIT_INST_ANY'] / wc:.1f}% | "
+                 f"{lds_conf:.3g} ({100 * lds_conf / lds_act if lds_act else 0:.1f}%) |")
+    open(os.path.join(prof, "counters_v3_s16384_h16.md"), "w").write("\n".join(L) + "\n")
+
+
 def host_info() -> dict:
     """CPU model, logical CPU count and the BLAS numpy's oracle runs on."""
     model = None
@@ -261,7 +475,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a 256 MiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write profiles/*.md and profiles/traffic.json from the rocprofv3 output in DIR, then exit")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU's share of the SP group; runs on more than one GPU "
               "are not part of this path (use --gpus 1).", file=sys.stderr)
