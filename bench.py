@@ -121,12 +121,12 @@ PROFILE_KERNELS = {
     "do_convert": ([["do_convert_kernel"]], _N + "attn_bwd.hip"),
     "attn_bwd_dkdv": ([["dkdv_kernel<"], ["dkdv_kernelIDF16_NS_6MmaF16ELi2"]], _N + "attn_bwd.hip"),
     "attn_bwd_dq": ([["dq_kernel<"]], _N + "attn_bwd_dq.hip"),
-    "fold_dL": ([["gemm_dma_kernel<", "DKC<2, unsigned short, 64>"]], _N + "gemm.hip"),
+    "fold_dL": ([["gemm_dma_kernel<", "DKC<2, unsigned short, 64"]], _N + "gemm.hip"),
     "fold_dW": ([["gemm_dma_kernel<", "DRC<2, 128>, laga::(anonymous namespace)::DRC<2, 128>"]], _N + "gemm.hip"),
     "rmsnorm_bwd": ([["rmsnorm_bwd_kernel"]], _N + "norm.hip"),
     "absorb_q": ([["gemm_dma_kernel<", "EpiHalf"]], _N + "gemm.hip"),
     "absorbed_attn": ([["absorbed_attn_kernel"]], _N + "absorbed.hip"),
-    "unabsorb_o": ([["gemm_dma_kernel<", "DKC<1, float, 256>"]], _N + "gemm.hip"),
+    "unabsorb_o": ([["gemm_dma_kernel<", "DKC<1, float, 256, false"]], _N + "gemm.hip"),
 }
 # Kernels of the forward-only path run once per forward-only workload; their grid
 # (work-items) tells the workloads apart.

@@ -509,18 +509,37 @@ struct Fwd {
     for (int j = wv; j < IMG_LOADS; j += NW) load_lds16(rs, buf + j * 1024, j * 1024 + 16 * lane);
   }
 
-  template <bool ALL>
+  // Waits until this wavefront's copies of the current block have landed,
+  // leaving those of the next block (if any) in flight: the copies return in
+  // issue order, and a wavefront issues IMG_HI or IMG_HI - 1 of them per block.
+  static constexpr int IMG_HI = (IMG_LOADS + NW - 1) / NW;
+  static constexpr int IMG_NHI = IMG_LOADS % NW == 0 ? NW : IMG_LOADS % NW;  // wavefronts issuing IMG_HI
+  __device__ static void wait_image(bool next_in_flight, int wv) {
+    if (!next_in_flight) wait_vmcnt<0>();
+    else if (wv < IMG_NHI) wait_vmcnt<IMG_HI>();
+    else wait_vmcnt<IMG_HI - 1>();
+  }
+
+  // One key block with NBUF buffers: block kb is in `cur`; block kb + NBUF - 1
+  // goes into `ahead` (the buffer of block kb - 1, free once every wavefront
+  // has passed this step's barrier).
+  template <bool ALL, int NBUF>
   __device__ static void image_step(const FwdArgs& a, const char* img, int kb, int nkb, int wv, int64_t qw,
-                                    int64_t tq, char* cur, char* nxt, State& st_) {
-    dma_barrier();  // block kb has landed in `cur`; every wavefront is done with `nxt`
-    if (kb + 1 < nkb) issue_image(img + static_cast<int64_t>(kb + 1) * BUF_BYTES, nxt, wv);
+                                    int64_t tq, char* cur, char* ahead, State& st_) {
+    if constexpr (NBUF == 2) wait_vmcnt<0>();
+    else wait_image(kb + 1 < nkb, wv);
+    __syncthreads();
+    if (kb + NBUF - 1 < nkb) issue_image(img + static_cast<int64_t>(kb + NBUF - 1) * BUF_BYTES, ahead, wv);
     const int64_t key0 = static_cast<int64_t>(kb) * BN;
     if (ALL || key0 <= qw + 31) compute_block(a, cur, key0, qw, tq, st_);
   }
 
-  // Query tile qt of (b, head) against the images at img (that head's block 0).
+  // Query tile qt of (b, head) against the images at img (that head's block 0),
+  // NBUF image buffers at lds.
+  template <int NBUF>
   __device__ static void run_images(const FwdArgs& a, const char* img, int b, int head, int qt, char* lds) {
     static_assert(!LO8, "images hold single-plane K and V");
+    static_assert(NBUF == 2 || NBUF == 3, "double or triple buffering");
     const int lane = threadIdx.x % kWave;
     const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int64_t q0 = static_cast<int64_t>(qt) * BM;
@@ -530,18 +549,23 @@ struct Fwd {
     int64_t kend = q0 + BM;
     if (kend > a.S) kend = a.S;
     const int nkb = static_cast<int>((kend + BN - 1) / BN);
-    issue_image(img, lds, wv);
     State st_;
-    begin(a, b, head, tq, qvalid, st_);
+    begin(a, b, head, tq, qvalid, st_);  // q loads first: the block waits below count only image copies after them
+#pragma unroll
+    for (int k = 0; k < NBUF - 1; ++k)
+      if (k < nkb) issue_image(img + static_cast<int64_t>(k) * BUF_BYTES, lds + k * BUF_BYTES, wv);
     const int nall = blocks_for_all(q0, nkb);
     int kb = 0;
-    for (; kb + 1 < nall; kb += 2) {
-      image_step<true>(a, img, kb, nkb, wv, qw, tq, lds, lds + BUF_BYTES, st_);
-      image_step<true>(a, img, kb + 1, nkb, wv, qw, tq, lds + BUF_BYTES, lds, st_);
+    // Unrolled by NBUF so that each step names its buffers as constant offsets.
+    for (; kb + NBUF - 1 < nall; kb += NBUF) {
+#pragma unroll
+      for (int j = 0; j < NBUF; ++j)
+        image_step<true, NBUF>(a, img, kb + j, nkb, wv, qw, tq, lds + j * BUF_BYTES,
+                               lds + ((j + NBUF - 1) % NBUF) * BUF_BYTES, st_);
     }
     for (; kb < nkb; ++kb)
-      image_step<false>(a, img, kb, nkb, wv, qw, tq, lds + (kb & 1) * BUF_BYTES, lds + ((kb + 1) & 1) * BUF_BYTES,
-                        st_);
+      image_step<false, NBUF>(a, img, kb, nkb, wv, qw, tq, lds + (kb % NBUF) * BUF_BYTES,
+                              lds + ((kb + NBUF - 1) % NBUF) * BUF_BYTES, st_);
     finish(a, b, head, tq, qvalid, st_);
   }
 };
@@ -759,8 +783,9 @@ struct KvProducerT {
 };
 
 typedef KvProducerT<32, 3> KvProducer;
-constexpr int kFusedLds = KvProducer::LDS_BYTES > 2 * FusedAttn::BUF_BYTES ? KvProducer::LDS_BYTES
-                                                                           : 2 * FusedAttn::BUF_BYTES;
+constexpr int kImageBufs = 2;  // key-block image buffers (a third, two blocks in flight, measured no faster)
+constexpr int kFusedLds = KvProducer::LDS_BYTES > kImageBufs * FusedAttn::BUF_BYTES ? KvProducer::LDS_BYTES
+                                                                                   : kImageBufs * FusedAttn::BUF_BYTES;
 
 __global__ __launch_bounds__(8 * kWave, 2) void attn_fwd_fused_kernel(FusedArgs a) {
   // One shared array for everything, the ticket words at its end: with a
@@ -813,7 +838,7 @@ __global__ __launch_bounds__(8 * kWave, 2) void attn_fwd_fused_kernel(FusedArgs 
     }
     return;
   }
-  FusedAttn::run_images(a.f, a.img + static_cast<int64_t>(bh) * a.nkb_img * FusedAttn::BUF_BYTES, b, head, qt,
+  FusedAttn::run_images<kImageBufs>(a.f, a.img + static_cast<int64_t>(bh) * a.nkb_img * FusedAttn::BUF_BYTES, b, head, qt,
                         lds);
 }
 

@@ -15,7 +15,9 @@
 //  * gemm_dma_kernel (every bf16 product): operand slabs go from global memory
 //    straight into a ring of LDS stages (no staging registers); the fp32
 //    normalised latent of the up-projection (and the absorbed form's fp32
-//    accumulator) is split into bf16 hi + lo as it is read from LDS.  Short
+//    accumulator) is split into bf16 hi + lo as it is read from LDS, or, for
+//    fp16 K/V storage, rounded to fp16 and multiplied by W converted to fp16
+//    in a single fp16 product.  Short
 //    steps (K = 512 for the up-projection) make load latency the limit, so
 //    the tiles are small enough for 2-3 workgroups per CU.
 //  * gemm_kernel (the float32 test dims): slabs move global -> registers ->
@@ -422,13 +424,18 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, void* lds, int 
 }
 
 
-// k-contiguous operand: NP planes of Src, ROWS rows per tile.
-template <int NP_, class Src, int ROWS_>
+// k-contiguous operand: NP planes of Src, ROWS rows per tile.  HALF: the
+// operand enters fp16 products as one fp16 term (fp32 rounded, or bf16
+// converted, as it is read from LDS) instead of bf16 terms.
+template <int NP_, class Src, int ROWS_, bool HALF_ = false>
 struct DKC {
   static constexpr int ROWS = ROWS_, NP = NP_;
+  static constexpr bool HALF = HALF_;
   static constexpr bool F32 = std::is_same<Src, float>::value;
+  static constexpr bool SRC_F32 = F32;  // stored as fp32 in memory
   static_assert(!F32 || NP == 1, "one fp32 plane, split when read");
-  static constexpr int NT = F32 ? 2 : NP;  // bf16 terms per element
+  static_assert(!HALF || NP == 1, "one plane converted to fp16");
+  static constexpr int NT = HALF ? 1 : (F32 ? 2 : NP);  // 16-bit terms per element
   static constexpr int LINE = BK * static_cast<int>(sizeof(Src));  // 64 or 128 bytes
   static constexpr int SPL = LINE / 16;
   static constexpr int PLANE = ROWS * LINE;
@@ -465,10 +472,23 @@ struct DKC {
     }
     return L;
   }
-  // The bf16 terms of the fragment of atom `a` (rows row0 + 32 a ..) at k step s.
+  // The 16-bit terms of the fragment of atom `a` (rows row0 + 32 a ..) at k step s.
   __device__ static void frag(const char* st, const Lane& L, int a, int s, u16x8* out) {
     const char* base = st + a * 32 * LINE;
-    if constexpr (F32) {
+    if constexpr (HALF && F32) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(base + L.o[s][0]);
+      const f32x4 y = *reinterpret_cast<const f32x4*>(base + L.o[s][1]);
+      const half8 h = {static_cast<half_t>(x[0]), static_cast<half_t>(x[1]), static_cast<half_t>(x[2]),
+                       static_cast<half_t>(x[3]), static_cast<half_t>(y[0]), static_cast<half_t>(y[1]),
+                       static_cast<half_t>(y[2]), static_cast<half_t>(y[3])};
+      out[0] = __builtin_bit_cast(u16x8, h);
+    } else if constexpr (HALF) {  // bf16 -> fp16, exact within fp16's normal range
+      const u16x8 x = *reinterpret_cast<const u16x8*>(base + L.o[s][0]);
+      half8 h;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) h[j] = static_cast<half_t>(bf16_to_f32(x[j]));
+      out[0] = __builtin_bit_cast(u16x8, h);
+    } else if constexpr (F32) {
       const f32x4 x = *reinterpret_cast<const f32x4*>(base + L.o[s][0]);
       const f32x4 y = *reinterpret_cast<const f32x4*>(base + L.o[s][1]);
       uint32_t h[4], l[4];
@@ -490,6 +510,7 @@ struct DKC {
 template <int NP_, int ROWS_>
 struct DRC {
   static constexpr int ROWS = ROWS_, NP = NP_, NT = NP_;
+  static constexpr bool HALF = false, SRC_F32 = false;
   static constexpr int LINE = ROWS * 2;  // one k-line
   static constexpr int SPL = LINE / 16;
   static_assert(LINE % 256 == 0, "k-lines span whole bank windows");
@@ -544,11 +565,12 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(Operand<bf16_t>
                                                                  Operand<bf16_t> B, EPI epi, int64_t k_chunk,
                                                                  int64_t K, int nchunks, int gx, int gy, int gz) {
   static_assert(OA::ROWS == 64 * TM && OB::ROWS == 64 * TN, "operand rows match the tile");
+  static_assert(OA::HALF == OB::HALF, "both operands fp16 or both bf16 terms");
   constexpr int STAGE = OA::BYTES + OB::BYTES;
   constexpr int IPS = OA::IPW * OA::NP + OB::IPW * OB::NP;  // loads per wavefront and stage
   static_assert((NST - 2) * IPS < 64, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) char lds[NST * STAGE];
-  constexpr bool A_F32 = OA::KC && OA::NT == 2 && OA::NP == 1;  // fp32 A (split when read)
+  constexpr bool A_F32 = OA::SRC_F32;  // fp32 A (split or rounded when read)
 
   const int total = gx * gy * gz;
   const int id = static_cast<int>(blockIdx.x);
@@ -640,8 +662,15 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_dma_kernel(Operand<bf16_t>
           for (int a = 0; a < TM; ++a)
 #pragma unroll
             for (int b = 0; b < TN; ++b) {
-              if constexpr (EPI::TRANS) acc[a][b] = MmaBf16::mma(bfr[b][tb], af[a][ta], acc[a][b]);
-              else acc[a][b] = MmaBf16::mma(af[a][ta], bfr[b][tb], acc[a][b]);
+              if constexpr (OA::HALF) {
+                const half8 x = __builtin_bit_cast(half8, af[a][ta]), y = __builtin_bit_cast(half8, bfr[b][tb]);
+                if constexpr (EPI::TRANS) acc[a][b] = MmaF16::mma(y, x, acc[a][b]);
+                else acc[a][b] = MmaF16::mma(x, y, acc[a][b]);
+              } else if constexpr (EPI::TRANS) {
+                acc[a][b] = MmaBf16::mma(bfr[b][tb], af[a][ta], acc[a][b]);
+              } else {
+                acc[a][b] = MmaBf16::mma(af[a][ta], bfr[b][tb], acc[a][b]);
+              }
             }
         }
     }
@@ -743,21 +772,24 @@ hipError_t launch_kv_up(const Shape& s, const float* L, const void* w, void* k_n
   Operand<float> A{L, s.d_kv, 0, s.T, s.d_kv};
   if (s.bf16 && s.d_nope == 128 && s.d_v == 128) {
     // L as bf16 hi + lo (formed as it is read from LDS), W exact in bf16:
-    // K / V to about 2^-16 relative, then stored as split planes or fp16.
-    // 64 x 256 tiles, two stages, three workgroups per CU: with K = 512 the
-    // steps are short and the loads of the other workgroups cover each
-    // one's latency (measured best of 1-3 workgroups per CU, 2-4 stages).
-    typedef DKC<1, float, 64> OA;
-    typedef DKC<1, bf16_t, 256> OB;
+    // K / V to about 2^-16 relative, then stored as split planes.  With
+    // K = 512 the steps are short, so the tiles are sized for two workgroups
+    // per CU whose loads cover each other's latency (measured against 64-
+    // to 256-row tiles, 2-4 stages and 1-3 workgroups per CU).
     Operand<bf16_t> B{static_cast<const bf16_t*>(w) + w0, s.d_kv, 0, N, s.d_kv};
     if (s.split) {
       EpiKvUp<half_t, 2, 128, 128> e{static_cast<half_t*>(k_nope), static_cast<half_t*>(v), s.T,
                                      static_cast<int>(N), s.h, pk, pv};
-      return run_gemm_dma<OA, OB, 1, 4, 2, 3>(Operand<bf16_t>{}, A, B, e, s.T, N, s.d_kv, 1, st);
+      return run_gemm_dma<DKC<1, float, 128>, DKC<1, bf16_t, 256>, 2, 4, 2, 2>(Operand<bf16_t>{}, A, B, e, s.T, N,
+                                                                               s.d_kv, 1, st);
     }
+    // Single fp16 storage: one fp16 product of L and W, both rounded to fp16
+    // as they are read from LDS (K / V to about 2^-11 relative before their
+    // own fp16 rounding), half the matrix-core work of the hi/lo form.
     EpiKvUp<half_t, 1, 128, 128> e{static_cast<half_t*>(k_nope), static_cast<half_t*>(v), s.T, static_cast<int>(N),
                                    s.h, pk, pv};
-    return run_gemm_dma<OA, OB, 1, 4, 2, 3>(Operand<bf16_t>{}, A, B, e, s.T, N, s.d_kv, 1, st);
+    return run_gemm_dma<DKC<1, float, 256, true>, DKC<1, bf16_t, 128, true>, 4, 2, 2, 2>(Operand<bf16_t>{}, A, B, e,
+                                                                                         s.T, N, s.d_kv, 1, st);
   }
   if (s.bf16 || s.d_nope != 32 || s.d_v != 32) return hipErrorNotSupported;
   typedef Side<MmaF32, 1, true, 128, float> SA;
