@@ -4,6 +4,7 @@ Only tests, the smoke check and the benchmark's CPU-baseline leg import this
 package.  It shares no code with the HIP library.
 """
 from .laga_oracle import (  # noqa: F401
+    absorbed_backward,
     absorbed_forward_rows,
     absorbed_scores_and_out,
     attention_bwd,

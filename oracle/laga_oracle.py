@@ -316,3 +316,60 @@ def absorbed_forward_rows(q, L, k_pe, w_kv_b, heads, d_nope, rows):
                 O[b, j, i] = Wv @ a
                 lse[b, i, j] = m + np.log(l)
     return q_abs, acc, O, lse
+
+
+def absorbed_backward(q, latent, k_pe, w_kv_b, gamma, d_o, *, n_h, sp_size, sp_rank, d_nope, eps=1e-6):
+    """Gradients of sum(d_o * O) for B2's forward [LAGA §3.2 (B2), Fig. 2], by the
+    chain rule through B2's own steps (absorb, latent attention, un-absorb), one
+    head at a time.  With P the causal softmax of the latent-space scores:
+
+      d_acc   = dO W^v                    (the un-absorb's input gradient, d_kv wide)
+      dW^v    = dO^T acc
+      dP      = d_acc L^T,  dS = P * (dP - rowsum(P * dP))
+      d_q_abs = dS L / sqrt(d_qk),  dq_rope = dS k_pe / sqrt(d_qk)
+      dL     += P^T d_acc + dS^T q_abs / sqrt(d_qk)   (L is both the values and the keys)
+      dk_pe  += dS^T q_rope / sqrt(d_qk)
+      dq_nope = d_q_abs W^k^T,  dW^k = q_nope^T d_q_abs
+
+    then the norm's backward.  Same outputs as backward() (the two forms are the
+    same function), plus the two n_h * d_kv-wide gradients d_acc and d_q_abs.
+    """
+    heads = head_shard(n_h, sp_size, sp_rank)
+    W = np.asarray(w_kv_b, dtype=np.float64)[heads]
+    L, rstd = latent_rmsnorm(latent, gamma, eps)
+    B, S, h, d_qk = q.shape
+    d_kv = L.shape[-1]
+    allowed = np.tril(np.ones((S, S), dtype=bool))
+    scale = 1.0 / np.sqrt(d_qk)
+    dq = np.empty((B, S, h, d_qk))
+    dL = np.zeros(L.shape)
+    dk_pe = np.zeros(np.shape(k_pe))
+    dW_shard = np.zeros(W.shape)
+    d_acc_all = np.empty((B, S, h, d_kv))
+    d_q_abs_all = np.empty((B, S, h, d_kv))
+    for b in range(B):
+        for i in range(h):
+            Wk, Wv = W[i, :d_nope], W[i, d_nope:]
+            q_nope, q_rope = q[b, :, i, :d_nope], q[b, :, i, d_nope:]
+            q_abs = q_nope @ Wk                                        # absorb
+            s = np.where(allowed, (q_abs @ L[b].T + q_rope @ k_pe[b].T) * scale, -np.inf)
+            e = np.exp(s - s.max(axis=1, keepdims=True))
+            P = e / e.sum(axis=1, keepdims=True)
+            acc = P @ L[b]                                             # latent accumulator
+            dO = d_o[b, :, i]
+            d_acc = dO @ Wv                                            # through the un-absorb
+            dW_shard[i, d_nope:] += dO.T @ acc
+            dP = d_acc @ L[b].T
+            dS = P * (dP - np.sum(P * dP, axis=1, keepdims=True))
+            d_q_abs = (dS @ L[b]) * scale
+            dq[b, :, i, d_nope:] = (dS @ k_pe[b]) * scale
+            dL[b] += P.T @ d_acc + (dS.T @ q_abs) * scale
+            dk_pe[b] += (dS.T @ q_rope) * scale
+            dq[b, :, i, :d_nope] = d_q_abs @ Wk.T                      # through the absorb
+            dW_shard[i, :d_nope] += q_nope.T @ d_q_abs
+            d_acc_all[b, :, i], d_q_abs_all[b, :, i] = d_acc, d_q_abs
+    d_latent, d_gamma = latent_rmsnorm_bwd(dL, latent, gamma, rstd)
+    dW = np.zeros(np.shape(w_kv_b))
+    dW[heads] = dW_shard
+    return dict(dq=dq, dk_pe=dk_pe, dL=dL, d_latent=d_latent, d_w_kv_b=dW, d_gamma=d_gamma,
+                d_acc=d_acc_all, d_q_abs=d_q_abs_all)

@@ -220,6 +220,52 @@ def test_absorbed_forward_matches_explicit_and_definitions():
                                atol=1e-13)
 
 
+@pytest.mark.parametrize("shape", [
+    dict(S=7, n_h=4, sp_size=2, sp_rank=0, d_kv=6, d_nope=5, d_rope=3, d_v=4, B=2, seed=1),
+    dict(S=1, n_h=2, sp_size=1, sp_rank=0, d_kv=5, d_nope=4, d_rope=2, d_v=3, B=1, seed=2),
+    dict(S=10, n_h=6, sp_size=3, sp_rank=2, d_kv=7, d_nope=4, d_rope=3, d_v=5, B=1, seed=4)])
+def test_absorbed_backward_matches_explicit(shape):
+    """B2's backward, taken through its own steps, equals the explicit backward
+    (pinned by finite differences and autograd above): the two forms are one
+    function, so every gradient agrees to rounding."""
+    d, kw = tiny(**shape)
+    ref = bwd(d, kw)
+    got = oracle.absorbed_backward(d["q"], d["latent"], d["k_pe"], d["w_kv_b"], d["gamma"], d["d_o"], **kw)
+    for key in ("dq", "dk_pe", "dL", "d_latent", "d_w_kv_b", "d_gamma"):
+        np.testing.assert_allclose(got[key], ref[key], rtol=1e-10, atol=1e-12, err_msg=key)
+
+
+def test_absorbed_backward_intermediates():
+    """d_acc against its contraction written as loops; d_q_abs against central
+    differences of the loss with q_abs as a free input of the latent attention."""
+    d, kw = tiny(S=4, n_h=2, sp_size=1, sp_rank=0, d_kv=3, d_nope=2, d_rope=2, d_v=2, B=1, seed=5)
+    g = oracle.absorbed_backward(d["q"], d["latent"], d["k_pe"], d["w_kv_b"], d["gamma"], d["d_o"], **kw)
+    W = d["w_kv_b"]
+    for t in range(4):
+        for i in range(2):
+            for c in range(3):
+                ref = sum(d["d_o"][0, t, i, j] * W[i, 2 + j, c] for j in range(2))
+                assert abs(g["d_acc"][0, t, i, c] - ref) < 1e-12
+    L, _ = oracle.latent_rmsnorm(d["latent"], d["gamma"])
+
+    def loss_from_q_abs(qa, i):
+        s = (qa @ L[0].T + d["q"][0, :, i, 2:] @ d["k_pe"][0].T) / math.sqrt(4)
+        s = np.where(np.tril(np.ones((4, 4), dtype=bool)), s, -np.inf)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        return float(np.sum(d["d_o"][0, :, i] * ((p @ L[0]) @ W[i, 2:].T)))
+
+    for i in range(2):
+        qa = d["q"][0, :, i, :2] @ W[i, :2]
+        for t in range(4):
+            for c in range(3):
+                qp, qm = qa.copy(), qa.copy()
+                qp[t, c] += 1e-6
+                qm[t, c] -= 1e-6
+                fd = (loss_from_q_abs(qp, i) - loss_from_q_abs(qm, i)) / 2e-6
+                assert abs(fd - g["d_q_abs"][0, t, i, c]) < 1e-7
+
+
 # ------------------------------------------------------------ softmax and lse
 def test_softmax_rows_sum_to_one():
     d, kw = tiny(S=11, d_kv=6)
