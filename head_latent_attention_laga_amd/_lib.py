@@ -51,6 +51,8 @@ _SIGS = {
     "laga_attn_fwd": (ctypes.c_int, [ctypes.POINTER(laga_dims), _P, _P, _P, _P, _P, _P, _P]),
     "laga_absorbed_fwd": (ctypes.c_int, [ctypes.POINTER(laga_dims)] + [_P] * 10),
     "laga_attn_fwd_fused_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(laga_dims)]),
+    "laga_absorbed_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(laga_dims)]),
+    "laga_absorbed_bwd": (ctypes.c_int, [ctypes.POINTER(laga_dims)] + [_P] * 13 + [ctypes.c_size_t, _P]),
     "laga_attn_fwd_fused": (ctypes.c_int, [ctypes.POINTER(laga_dims)] + [_P] * 8 + [ctypes.c_size_t, _P]),
     "laga_attn_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(laga_dims)]),
     "laga_attn_bwd": (ctypes.c_int, [ctypes.POINTER(laga_dims)] + [_P] * 17 + [ctypes.c_size_t, _P]),
@@ -143,6 +145,18 @@ def attn_fwd_fused(dims, q, latent, gamma, k_pe, w_kv_b, o, lse, workspace, stre
     _check("laga_attn_fwd_fused", load().laga_attn_fwd_fused(
         ctypes.byref(dims), _ptr(q), _ptr(latent), _ptr(gamma), _ptr(k_pe), _ptr(w_kv_b), _ptr(o), _ptr(lse),
         _ptr(workspace), ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(stream)))
+
+
+def absorbed_bwd_workspace_bytes(dims) -> int:
+    return int(load().laga_absorbed_bwd_workspace_bytes(ctypes.byref(dims)))
+
+
+def absorbed_bwd(dims, q, latent, gamma, rstd, k_pe, w_kv_b, d_o, dq, d_latent, d_k_pe, d_w_kv_b, d_gamma,
+                 workspace, stream=None):
+    _check("laga_absorbed_bwd", load().laga_absorbed_bwd(
+        ctypes.byref(dims), _ptr(q), _ptr(latent), _ptr(gamma), _ptr(rstd), _ptr(k_pe), _ptr(w_kv_b), _ptr(d_o),
+        _ptr(dq), _ptr(d_latent), _ptr(d_k_pe), _ptr(d_w_kv_b), _ptr(d_gamma), _ptr(workspace),
+        ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(stream)))
 
 
 def attn_bwd_workspace_bytes(dims) -> int:

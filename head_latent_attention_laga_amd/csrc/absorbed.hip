@@ -301,7 +301,359 @@ __global__ __launch_bounds__(256) void absorbed_pack_kernel(const float* __restr
   *reinterpret_cast<half8*>(kx + t * DQ + c) = h;
 }
 
+// ------------------------------------------------------------------ backward
+// Elementwise pieces of the absorbed form's backward (products in gemm.hip).
+constexpr int B2_CHUNK_CAP_MB = 1024;  // per-chunk S, dP, P and c.dS buffers
+
+__device__ __forceinline__ void split8(const float* x, u16x8& hi, u16x8& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) split_bf16_pair(x[2 * j], x[2 * j + 1], h[j], l[j]);
+  hi = __builtin_bit_cast(u16x8, u32x4{h[0], h[1], h[2], h[3]});
+  lo = __builtin_bit_cast(u16x8, u32x4{l[0], l[1], l[2], l[3]});
+}
+
+// Row statistics of one chunk from its scores S and dP = d_acc . L (fp32,
+// row pitch ldu), over the row's keys u <= its token: lse = ln sum_u exp(S c)
+// and delta = sum_u P dP (= sum_j dO o for this P).  One wavefront per row,
+// each lane an online (max, sum, weighted dP sum) over a strided set of keys,
+// merged across the wavefront.
+__global__ __launch_bounds__(256) void b2_rowstat_kernel(const float* __restrict__ S, const float* __restrict__ dP,
+                                                         int64_t ldu, int64_t nrows, int64_t nkeys, int64_t s0, int h,
+                                                         float scale, float* __restrict__ lse,
+                                                         float* __restrict__ delta) {
+  constexpr int UNR = 4;  // float4 loads of S and dP per lane in flight: 1024 keys per wave step
+  const int64_t rr = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
+  if (rr >= nrows) return;
+  const int lane = threadIdx.x % kWave;
+  const int64_t st = s0 + rr / h;
+  const int64_t nk = st + 1 < nkeys ? st + 1 : nkeys;
+  const float c2 = scale * 1.4426950408889634f;  // log2 units
+  const float* srow = S + rr * ldu;
+  const float* drow = dP + rr * ldu;
+  float m = -INFINITY, l = 0.f, dsum = 0.f;
+  // ldu is a multiple of 32 >= nk, so a float4 that starts below nk lies inside the row;
+  // its elements at or past nk (never written) are masked by selection, not arithmetic.
+  for (int64_t base = 4 * lane; base < nk; base += 4 * kWave * UNR) {
+    f32x4 xs[UNR], dps[UNR];
+#pragma unroll
+    for (int k = 0; k < UNR; ++k) {
+      const int64_t u = base + 4 * kWave * k;
+      xs[k] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      dps[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (u < nk) {
+        xs[k] = *reinterpret_cast<const f32x4*>(srow + u);
+        dps[k] = *reinterpret_cast<const f32x4*>(drow + u);
+      }
+    }
+    float mx = m;
+#pragma unroll
+    for (int k = 0; k < UNR; ++k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool ok = base + 4 * kWave * k + j < nk;
+        xs[k][j] = ok ? xs[k][j] * c2 : -INFINITY;
+        dps[k][j] = ok ? dps[k][j] : 0.f;
+        mx = fmaxf(mx, xs[k][j]);
+      }
+    // mx is finite: the element at base is valid.
+    const float a = __builtin_amdgcn_exp2f(m - mx);
+    l *= a;
+    dsum *= a;
+    m = mx;
+#pragma unroll
+    for (int k = 0; k < UNR; ++k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float e = __builtin_amdgcn_exp2f(xs[k][j] - m);
+        l += e;
+        dsum += e * dps[k][j];
+      }
+  }
+  float mw = m;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mw = fmaxf(mw, __shfl_xor(mw, o, kWave));
+  const float a = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mw);
+  l = wave_sum(l * a);
+  dsum = wave_sum(dsum * a);
+  if (lane == 0) {
+    lse[rr] = (mw + log2f(l)) * 0.69314718055994531f;
+    delta[rr] = dsum / l;
+  }
+}
+
+// kxp[p][t] = L[t] || k_pe[t] as bf16 hi (p = 0) / lo (p = 1) planes, L = gamma x rstd
+// (the forward's normalisation); rows t in [T, Tp) are zero.  One thread per 8 elements.
+__global__ __launch_bounds__(256) void b2_kxp_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ gamma,
+                                                     const float* __restrict__ rstd, const bf16_t* __restrict__ k_pe,
+                                                     bf16_t* __restrict__ kxp, int64_t T, int64_t Tp) {
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (j >= Tp * (DQ / 8)) return;
+  const int64_t t = j / (DQ / 8);
+  const int c = static_cast<int>(j % (DQ / 8)) * 8;
+  u16x8 hi = {}, lo = {};
+  if (t < T && c < DL) {
+    const u16x8 xr = *reinterpret_cast<const u16x8*>(x + t * DL + c);
+    const u16x8 gr = *reinterpret_cast<const u16x8*>(gamma + c);
+    const float r = rstd[t];
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = bf16_to_f32(gr[k]) * (bf16_to_f32(xr[k]) * r);
+    split8(v, hi, lo);
+  } else if (t < T) {
+    hi = *reinterpret_cast<const u16x8*>(k_pe + t * DR + (c - DL));
+  }
+  *reinterpret_cast<u16x8*>(kxp + t * DQ + c) = hi;
+  *reinterpret_cast<u16x8*>(kxp + Tp * DQ + t * DQ + c) = lo;
+}
+
+// qx[p][r][512 ..] = q_rope[r] (hi plane), 0 (lo plane).
+__global__ __launch_bounds__(256) void b2_qrope_kernel(const bf16_t* __restrict__ q, bf16_t* __restrict__ qx,
+                                                       int64_t rows) {
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (j >= rows * (DR / 8)) return;
+  const int64_t r = j / (DR / 8);
+  const int c = static_cast<int>(j % (DR / 8)) * 8;
+  *reinterpret_cast<u16x8*>(qx + r * DQ + DL + c) = *reinterpret_cast<const u16x8*>(q + r * (DNQ + DR) + DNQ + c);
+  *reinterpret_cast<u16x8*>(qx + rows * DQ + r * DQ + DL + c) = u16x8{};
+}
+
+// One chunk of rows (tokens s0 .. of one sequence, all heads): from the scores
+// S and dP = d_acc . L (fp32, row pitch ldu) and the rows' lse and delta,
+// P = exp(S c - lse) and c.dS = c P (dP - delta) on keys u <= the row's token,
+// zero on the others and on u in [nkeys, kpad); written as bf16 hi / lo planes
+// (plane pitch pplane).  One thread per 8 keys.
+__global__ __launch_bounds__(256) void b2_pds_kernel(const float* __restrict__ S, const float* __restrict__ dP,
+                                                     const float* __restrict__ lse, const float* __restrict__ delta,
+                                                     bf16_t* __restrict__ pp, bf16_t* __restrict__ dsp,
+                                                     int64_t pplane, int64_t ldu, int64_t nrows, int64_t nkeys,
+                                                     int64_t kpad, int64_t s0, int h, float scale) {
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t per_row = kpad / 8;
+  if (j >= nrows * per_row) return;
+  const int64_t rr = j / per_row;
+  const int64_t u0 = (j % per_row) * 8;
+  const int64_t st = s0 + rr / h;  // the row's token within its sequence
+  const float lse2 = lse[rr] * 1.4426950408889634f;
+  const float dl = delta[rr];
+  const float sc2 = scale * 1.4426950408889634f;
+  float p[8], ds[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int64_t u = u0 + k;
+    p[k] = 0.f;
+    ds[k] = 0.f;
+    if (u < nkeys && u <= st) {
+      p[k] = __builtin_amdgcn_exp2f(fmaf(S[rr * ldu + u], sc2, -lse2));
+      ds[k] = scale * p[k] * (dP[rr * ldu + u] - dl);
+    }
+  }
+  u16x8 h8, l8;
+  split8(p, h8, l8);
+  *reinterpret_cast<u16x8*>(pp + rr * ldu + u0) = h8;
+  *reinterpret_cast<u16x8*>(pp + pplane + rr * ldu + u0) = l8;
+  split8(ds, h8, l8);
+  *reinterpret_cast<u16x8*>(dsp + rr * ldu + u0) = h8;
+  *reinterpret_cast<u16x8*>(dsp + pplane + rr * ldu + u0) = l8;
+}
+
+// acc planes of a chunk: out[r][c] (hi) and out[plane + r][c] (lo) from the sum over the
+// K-chunk partials part[k][r][c], k = 0 .. nch - 1 in order.  One thread per 8 columns.
+__global__ __launch_bounds__(256) void b2_ksum_planes_kernel(const float* __restrict__ part, int nch, int64_t nrows,
+                                                             bf16_t* __restrict__ out, int64_t plane) {
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (j >= nrows * (DL / 8)) return;
+  const int64_t e = j * 8;  // = r * 512 + c
+  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < nch; ++k) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(part + k * nrows * DL + e);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(part + k * nrows * DL + e + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] += a[i];
+      v[4 + i] += b[i];
+    }
+  }
+  u16x8 hi, lo;
+  split8(v, hi, lo);
+  *reinterpret_cast<u16x8*>(out + e) = hi;
+  *reinterpret_cast<u16x8*>(out + plane + e) = lo;
+}
+
+// out[e] = sum over k in order of part[k * n + e], four elements per thread (n % 4 == 0).
+__global__ __launch_bounds__(256) void b2_ksum_kernel(const float* __restrict__ part, int nch, int64_t n,
+                                                      float* __restrict__ out) {
+  const int64_t e = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (e >= n) return;
+  f32x4 v = *reinterpret_cast<const f32x4*>(part + e);
+  for (int k = 1; k < nch; ++k) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(part + k * n + e);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] += a[i];
+  }
+  *reinterpret_cast<f32x4*>(out + e) = v;
+}
+
+// out planes [2][rows][512] = bf16 hi / lo of in[r][0 .. 512) (row pitch ld_in).
+__global__ __launch_bounds__(256) void b2_planes_kernel(const float* __restrict__ in, int64_t ld_in,
+                                                        bf16_t* __restrict__ out, int64_t rows) {
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (j >= rows * (DL / 8)) return;
+  const int64_t r = j / (DL / 8);
+  const int c = static_cast<int>(j % (DL / 8)) * 8;
+  const f32x4 a = *reinterpret_cast<const f32x4*>(in + r * ld_in + c);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(in + r * ld_in + c + 4);
+  const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  u16x8 hi, lo;
+  split8(v, hi, lo);
+  *reinterpret_cast<u16x8*>(out + r * DL + c) = hi;
+  *reinterpret_cast<u16x8*>(out + rows * DL + r * DL + c) = lo;
+}
+
+// dq[r][128 + j] = dqx[r][512 + j] (the rope part of dq).
+__global__ __launch_bounds__(256) void b2_dq_rope_kernel(const float* __restrict__ dqx, float* __restrict__ dq,
+                                                         int64_t rows) {
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (j >= rows * (DR / 4)) return;
+  const int64_t r = j / (DR / 4);
+  const int c = static_cast<int>(j % (DR / 4)) * 4;
+  *reinterpret_cast<f32x4*>(dq + r * (DNQ + DR) + DNQ + c) = *reinterpret_cast<const f32x4*>(dqx + r * DQ + DL + c);
+}
+
+__global__ __launch_bounds__(256) void b2_zero_kernel(float* __restrict__ p, int64_t n) {
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (j < n) p[j] = 0.f;
+}
+
+unsigned blocks_for(int64_t n) { return static_cast<unsigned>((n + 255) / 256); }
+
+// Workspace of laga_absorbed_bwd, regions 256-byte aligned.
+struct B2Layout {
+  int64_t R, Tp, ldu, tc, rc_max;
+  size_t qx, dacc, kxp, accp, dqx, dL, sbuf, dpbuf, pp, dsp, rlse, rdelta, kpart, dw, dg, total;
+};
+
+B2Layout b2_layout(const Shape& s) {
+  B2Layout L;
+  L.R = s.T * s.h;
+  L.Tp = s.T + 32;
+  L.ldu = (s.S + 31) / 32 * 32;
+  const int64_t per_token = 16 * static_cast<int64_t>(s.h) * L.ldu;  // S, dP (fp32), P, c.dS (2 bf16 planes)
+  int64_t tc = (static_cast<int64_t>(B2_CHUNK_CAP_MB) << 20) / per_token / 32 * 32;
+  if (tc < 32) tc = 32;
+  if (tc > L.ldu) tc = L.ldu;
+  L.tc = tc;
+  L.rc_max = tc * s.h;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += (bytes + 255) & ~size_t(255);
+    return at;
+  };
+  L.qx = take(static_cast<size_t>(2) * L.R * DQ * 2);
+  L.dacc = take(static_cast<size_t>(2) * L.R * DL * 2);
+  L.kxp = take(static_cast<size_t>(2) * L.Tp * DQ * 2);
+  L.accp = take(static_cast<size_t>(2) * L.R * DL * 2);
+  L.dqx = take(static_cast<size_t>(L.R) * DQ * 4);
+  L.dL = take(static_cast<size_t>(s.T) * DL * 4);
+  L.sbuf = take(static_cast<size_t>(L.rc_max) * L.ldu * 4);
+  L.dpbuf = take(static_cast<size_t>(L.rc_max) * L.ldu * 4);
+  L.pp = take(static_cast<size_t>(2) * L.rc_max * L.ldu * 2);
+  L.dsp = take(static_cast<size_t>(2) * L.rc_max * L.ldu * 2);
+  L.rlse = take(static_cast<size_t>(L.rc_max) * 4);
+  L.rdelta = take(static_cast<size_t>(L.rc_max) * 4);
+  L.kpart = take(static_cast<size_t>(B2_KSPLIT) * L.rc_max * DQ * 4);
+  L.dw = take(b2_dw_partial_floats(s) * 4);
+  L.dg = take(norm_bwd_partial_floats(s) * 4);
+  L.total = off;
+  return L;
+}
+
+bool b2_supported(const Shape& s) { return s.bf16 && s.d_kv == DL && s.d_rope == DR && s.d_nope == DNQ && s.d_v == DNQ; }
+
 }  // namespace
+
+size_t absorbed_bwd_workspace_bytes(const Shape& s) { return b2_supported(s) ? b2_layout(s).total : 0; }
+
+hipError_t launch_absorbed_bwd(const Shape& s, const void* q, const void* latent, const void* gamma,
+                               const float* rstd, const void* k_pe, const void* w, const void* d_o, float* dq,
+                               float* d_latent, float* d_k_pe, float* d_w, float* d_gamma, void* workspace,
+                               hipStream_t st) {
+  if (!b2_supported(s)) return hipErrorNotSupported;
+  const B2Layout L = b2_layout(s);
+  char* ws = static_cast<char*>(workspace);
+  bf16_t* qx = reinterpret_cast<bf16_t*>(ws + L.qx);
+  bf16_t* dacc = reinterpret_cast<bf16_t*>(ws + L.dacc);
+  bf16_t* kxp = reinterpret_cast<bf16_t*>(ws + L.kxp);
+  bf16_t* accp = reinterpret_cast<bf16_t*>(ws + L.accp);
+  float* rlse = reinterpret_cast<float*>(ws + L.rlse);
+  float* rdelta = reinterpret_cast<float*>(ws + L.rdelta);
+  float* kpart = reinterpret_cast<float*>(ws + L.kpart);
+  float* dqx = reinterpret_cast<float*>(ws + L.dqx);
+  float* dL = reinterpret_cast<float*>(ws + L.dL);
+  float* sbuf = reinterpret_cast<float*>(ws + L.sbuf);
+  float* dpbuf = reinterpret_cast<float*>(ws + L.dpbuf);
+  bf16_t* pp = reinterpret_cast<bf16_t*>(ws + L.pp);
+  bf16_t* dsp = reinterpret_cast<bf16_t*>(ws + L.dsp);
+  float* dwp = reinterpret_cast<float*>(ws + L.dw);
+  float* dgp = reinterpret_cast<float*>(ws + L.dg);
+  const bf16_t* qb = static_cast<const bf16_t*>(q);
+  const int64_t R = L.R, dq_ld = static_cast<int64_t>(s.h) * (DNQ + DR), do_ld = static_cast<int64_t>(s.h) * DNQ;
+  const int64_t qx_plane = R * DQ, dacc_plane = R * DL, kxp_plane = L.Tp * DQ, pplane = L.rc_max * L.ldu;
+  const float scale = 1.0f / sqrtf(static_cast<float>(DNQ + DR));
+  hipError_t e;
+#define B2_TRY(x) \
+  if ((e = (x)) != hipSuccess) return e
+  // Operands: q_abs, d_acc as planes; the rope columns of qx; L || k_pe; zeroed accumulators.
+  B2_TRY(launch_b2_planes(s, q, dq_ld, DNQ + DR, 0, w, qx, qx_plane, DQ, st));
+  B2_TRY(launch_b2_planes(s, d_o, do_ld, DNQ, DNQ, w, dacc, dacc_plane, DL, st));
+  hipLaunchKernelGGL(b2_qrope_kernel, dim3(blocks_for(R * (DR / 8))), dim3(256), 0, st, qb, qx, R);
+  hipLaunchKernelGGL(b2_kxp_kernel, dim3(blocks_for(L.Tp * (DQ / 8))), dim3(256), 0, st,
+                     static_cast<const bf16_t*>(latent), static_cast<const bf16_t*>(gamma), rstd,
+                     static_cast<const bf16_t*>(k_pe), kxp, s.T, L.Tp);
+  hipLaunchKernelGGL(b2_zero_kernel, dim3(blocks_for(s.T * DL)), dim3(256), 0, st, dL, s.T * DL);
+  hipLaunchKernelGGL(b2_zero_kernel, dim3(blocks_for(s.T * DR)), dim3(256), 0, st, d_k_pe, s.T * DR);
+  B2_TRY(hipGetLastError());
+  // Row chunks of tc tokens x all heads against their keys 0 .. chunk end.
+  for (int64_t b = 0; b < s.B; ++b) {
+    for (int64_t s0 = 0; s0 < s.S; s0 += L.tc) {
+      const int64_t s1 = s0 + L.tc < s.S ? s0 + L.tc : s.S;
+      const int64_t r0 = (b * s.S + s0) * s.h, nrows = (s1 - s0) * s.h;
+      const int64_t nkeys = s1, kpad = (s1 + 31) / 32 * 32;
+      const bf16_t* keys = kxp + b * s.S * DQ;
+      B2_TRY(launch_b2_rows_keys(qx + r0 * DQ, qx_plane, DQ, nrows, keys, kxp_plane, nkeys, DQ, sbuf, L.ldu, st));
+      B2_TRY(launch_b2_rows_keys(dacc + r0 * DL, dacc_plane, DL, nrows, keys, kxp_plane, nkeys, DL, dpbuf, L.ldu, st));
+      hipLaunchKernelGGL(b2_rowstat_kernel, dim3(static_cast<unsigned>((nrows + 3) / 4)), dim3(256), 0, st, sbuf,
+                         dpbuf, L.ldu, nrows, nkeys, s0, s.h, scale, rlse, rdelta);
+      hipLaunchKernelGGL(b2_pds_kernel, dim3(blocks_for(nrows * (kpad / 8))), dim3(256), 0, st, sbuf, dpbuf, rlse,
+                         rdelta, pp, dsp, pplane, L.ldu, nrows, nkeys, kpad, s0, s.h, scale);
+      B2_TRY(hipGetLastError());
+      // acc = P L (as planes), then dL, dk_pe from P and c.dS, then d_q_abs || dq_rope = c.dS kx.
+      B2_TRY(launch_b2_rows_by_keys(pp, pplane, L.ldu, nrows, kpad, keys, kxp_plane, DL, kpart, st));
+      const int nca = b2_key_chunks(nrows, DL, kpad);
+      hipLaunchKernelGGL(b2_ksum_planes_kernel, dim3(blocks_for(nrows * (DL / 8))), dim3(256), 0, st, kpart, nca,
+                         nrows, accp + r0 * DL, R * DL);
+      B2_TRY(hipGetLastError());
+      B2_TRY(launch_b2_key_grads(pp, dsp, pplane, L.ldu, nrows, nkeys, dacc + r0 * DL, dacc_plane, qx + r0 * DQ,
+                                 qx_plane, dL + b * s.S * DL, d_k_pe + b * s.S * DR, st));
+      B2_TRY(launch_b2_rows_by_keys(dsp, pplane, L.ldu, nrows, kpad, keys, kxp_plane, DQ, kpart, st));
+      const int ncq = b2_key_chunks(nrows, DQ, kpad);
+      hipLaunchKernelGGL(b2_ksum_kernel, dim3(blocks_for(nrows * (DQ / 4))), dim3(256), 0, st, kpart, ncq,
+                         nrows * DQ, dqx + r0 * DQ);
+      B2_TRY(hipGetLastError());
+    }
+  }
+  // dq = [d_q_abs W^k^T || dq_rope]; dW^k from q_nope and d_q_abs, dW^v from dO and acc; the norm's backward.
+  B2_TRY(launch_b2_dq_nope(s, dqx, w, dq, st));
+  hipLaunchKernelGGL(b2_dq_rope_kernel, dim3(blocks_for(R * (DR / 4))), dim3(256), 0, st, dqx, dq, R);
+  hipLaunchKernelGGL(b2_planes_kernel, dim3(blocks_for(R * (DL / 8))), dim3(256), 0, st, dqx, DQ, qx, R);
+  B2_TRY(hipGetLastError());
+  B2_TRY(launch_b2_dw(s, q, dq_ld, DNQ + DR, qx, R * DL, dwp, d_w, 0, st));
+  B2_TRY(launch_b2_dw(s, d_o, do_ld, DNQ, accp, R * DL, dwp, d_w, DNQ, st));
+  B2_TRY(launch_norm_bwd(s, dL, latent, gamma, rstd, d_latent, dgp, d_gamma, st));
+#undef B2_TRY
+  return hipSuccess;
+}
 
 hipError_t launch_absorbed_pack(const Shape& s, const float* L, const void* k_pe, void* kx, hipStream_t st) {
   if (!(s.bf16 && s.d_kv == DL && s.d_rope == DR && s.d_nope == DNQ)) return hipErrorNotSupported;

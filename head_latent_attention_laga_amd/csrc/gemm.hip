@@ -245,6 +245,34 @@ struct EpiStore {  // out[z * chunk_stride + m * ld + n] (z: batch * chunks + K 
   }
 };
 
+// out as bf16 hi + lo planes (x = hi + lo to about 2^-16), four consecutive n at
+// a time: hi at p[z * zstride + m * ld + n], lo at the same place + plane.
+struct EpiPlanes {
+  static constexpr bool TRANS = true;
+  bf16_t* p; int64_t plane, M; int N; int64_t ld, zstride;
+  __device__ void store4(int64_t m, int n, f32x4 val, int z) const {
+    if (m >= M || n >= N) return;
+    uint32_t h0, l0, h1, l1;
+    split_bf16_pair(val[0], val[1], h0, l0);
+    split_bf16_pair(val[2], val[3], h1, l1);
+    const int64_t e = z * zstride + m * ld + n;
+    *reinterpret_cast<u32x2*>(p + e) = u32x2{h0, h1};
+    *reinterpret_cast<u32x2*>(p + plane + e) = u32x2{l0, l1};
+  }
+};
+
+// out[m * ld + n] += val; columns n >= n0 go to out1[m * ld1 + n - n0] instead
+// (one product whose output spans two accumulators).
+struct EpiAccum {
+  static constexpr bool TRANS = false;
+  float* p; int64_t ld; float* p1; int64_t ld1; int64_t M; int N, n0;
+  __device__ void operator()(int64_t m, int n, float val, int /*z*/) const {
+    if (m >= M || n >= N) return;
+    if (n < n0) p[m * ld + n] += val;
+    else p1[m * ld1 + (n - n0)] += val;
+  }
+};
+
 // ------------------------------------------------------------------- kernel
 // Tiles (x = N tile, y = M tile, z = batch * nchunks + K chunk) come from a
 // 1-D launch.  Workgroup ids are dealt round-robin to the 8 XCDs, each with
@@ -869,6 +897,142 @@ hipError_t launch_fold_dw(const Shape& s, const void* dkv, const void* lplanes, 
   const int64_t n = Mr * s.d_kv;
   hipLaunchKernelGGL(chunk_sum_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st,
                      partial, d_w + static_cast<int64_t>(s.head_lo) * s.C() * s.d_kv, n, chunks);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------ absorbed form (B2), backward
+// Products of laga_absorbed_bwd (absorbed.hip sequences them).  Every operand
+// that is not exact in bf16 enters as bf16 hi + lo planes, and the products
+// keep the term pairs hi.hi, hi.lo, lo.hi: fp32-class results.  Plane
+// buffers: qx [2][R][576] (q_abs || q_rope, R = T h rows r = t h + i), dacc
+// [2][R][512], kxp [2][Tp][576] (L || k_pe); per chunk of rows r0 .. r0 + Rc:
+// P and c.dS as [2][Rc][ldu] planes, S and dP as fp32 [Rc][ldu].
+namespace {
+constexpr int B2_DQ = 576, B2_DL = 512;
+}
+
+hipError_t launch_b2_planes(const Shape& s, const void* x, int64_t x_ld, int64_t x_z, int64_t w_row0,
+                            const void* w, void* out, int64_t out_plane, int64_t out_ld, hipStream_t st) {
+  // out[t h + i][c] = sum_n x[t][i][n] W[head_lo + i][w_row0 + n][c], n < 128, as bf16 hi/lo planes
+  // (x: token pitch x_ld, head pitch x_z elements; out: row pitch out_ld).
+  const int64_t w0 = static_cast<int64_t>(s.head_lo) * s.C() * s.d_kv + w_row0 * s.d_kv;
+  Operand<bf16_t> A{static_cast<const bf16_t*>(x), x_ld, 0, s.T, 128, x_z};
+  Operand<bf16_t> B{static_cast<const bf16_t*>(w) + w0, s.d_kv, 0, s.d_kv, 128, static_cast<int64_t>(s.C()) * s.d_kv};
+  EpiPlanes e{static_cast<bf16_t*>(out), out_plane, s.T, s.d_kv, static_cast<int64_t>(s.h) * out_ld, out_ld};
+  return run_gemm_dma<DKC<1, bf16_t, 128>, DRC<1, 256>, 2, 4, 4, 1>(A, Operand<float>{}, B, e, s.T, s.d_kv, 128, 1,
+                                                                     st, s.h);
+}
+
+hipError_t launch_b2_rows_keys(const void* rows, int64_t rows_plane, int64_t rows_ld, int64_t nrows, const void* keys,
+                               int64_t keys_plane, int64_t nkeys, int64_t kdim, float* out, int64_t out_ld,
+                               hipStream_t st) {
+  // out[r][u] = sum_k rows[r][k] keys[u][k], k < kdim (keys' row pitch 576).
+  Operand<bf16_t> A{static_cast<const bf16_t*>(rows), rows_ld, rows_plane, nrows, kdim};
+  Operand<bf16_t> B{static_cast<const bf16_t*>(keys), B2_DQ, keys_plane, nkeys, kdim};
+  EpiStore e{out, nrows, static_cast<int>(nkeys), out_ld, 0};
+  return run_gemm_dma<DKC<2, bf16_t, 128>, DKC<2, bf16_t, 128>, 2, 2, 2, 2>(A, Operand<float>{}, B, e, nrows, nkeys,
+                                                                             kdim, 1, st);
+}
+
+hipError_t launch_b2_key_grads(const void* pp, const void* dsp, int64_t p_plane, int64_t ldu, int64_t nrows,
+                               int64_t nkeys, const void* dacc_rows, int64_t dacc_plane, const void* qx_rows,
+                               int64_t qx_plane, float* dL, float* dkpe, hipStream_t st) {
+  // dL[u][c] += sum_r P[r][u] dacc[r][c]; (dL || dk_pe)[u][c] += sum_r cdS[r][u] qx[r][c].
+  typedef DRC<2, 128> OA;  // P / cdS [r][u] read as A(row = u, k = r)
+  typedef DRC<2, 128> OB;  // dacc / qx [r][c] read as B(row = c, k = r)
+  Operand<bf16_t> Ap{static_cast<const bf16_t*>(pp), ldu, p_plane, nkeys, nrows};
+  Operand<bf16_t> Bd{static_cast<const bf16_t*>(dacc_rows), B2_DL, dacc_plane, B2_DL, nrows};
+  EpiAccum e1{dL, B2_DL, dkpe, 64, nkeys, B2_DL, B2_DL};
+  hipError_t err = run_gemm_dma<OA, OB, 2, 2, 2, 2>(Ap, Operand<float>{}, Bd, e1, nkeys, B2_DL, nrows, 1, st);
+  if (err != hipSuccess) return err;
+  Operand<bf16_t> As{static_cast<const bf16_t*>(dsp), ldu, p_plane, nkeys, nrows};
+  Operand<bf16_t> Bq{static_cast<const bf16_t*>(qx_rows), B2_DQ, qx_plane, B2_DQ, nrows};
+  EpiAccum e2{dL, B2_DL, dkpe, 64, nkeys, B2_DQ, B2_DL};
+  return run_gemm_dma<OA, OB, 2, 2, 2, 2>(As, Operand<float>{}, Bq, e2, nkeys, B2_DQ, nrows, 1, st);
+}
+
+int b2_key_chunks(int64_t nrows, int ncols, int64_t kpad) {
+  // K chunks so that about 512 workgroups run (two per CU at this tile's
+  // occupancy), at most B2_KSPLIT and at least 256 keys each.
+  const int64_t tiles = ((ncols + 127) / 128) * ((nrows + 127) / 128);
+  int64_t c = (512 + tiles - 1) / tiles;
+  if (c > B2_KSPLIT) c = B2_KSPLIT;
+  if (c > kpad / 256) c = kpad / 256;
+  if (c < 1) c = 1;
+  // The count run_gemm_dma produces for this request.
+  const int64_t per = ((kpad + c - 1) / c + BK - 1) / BK * BK;
+  return static_cast<int>((kpad + per - 1) / per);
+}
+
+hipError_t launch_b2_rows_by_keys(const void* ap, int64_t p_plane, int64_t ldu, int64_t nrows, int64_t kpad,
+                                  const void* keys, int64_t keys_plane, int ncols, float* part, hipStream_t st) {
+  // part[c][r][n] = sum over u in K chunk c of A[r][u] kxp[u][n], n < ncols, u < kpad (A is P or
+  // c.dS as bf16 hi/lo planes, zero past the chunk's keys); c < b2_key_chunks(nrows, ncols, kpad).
+  Operand<bf16_t> A{static_cast<const bf16_t*>(ap), ldu, p_plane, nrows, kpad};
+  Operand<bf16_t> B{static_cast<const bf16_t*>(keys), B2_DQ, keys_plane, ncols, kpad};
+  EpiStore e{part, nrows, ncols, ncols, nrows * ncols};
+  return run_gemm_dma<DKC<2, bf16_t, 128>, DRC<2, 128>, 2, 2, 2, 2>(A, Operand<float>{}, B, e, nrows, ncols, kpad,
+                                                                     b2_key_chunks(nrows, ncols, kpad), st);
+}
+
+hipError_t launch_b2_dq_nope(const Shape& s, const float* dqx, const void* w, float* dq, hipStream_t st) {
+  // dq[t][i][n] = sum_c d_q_abs[t h + i][c] W^k[head_lo + i][n][c].
+  const int64_t w0 = static_cast<int64_t>(s.head_lo) * s.C() * s.d_kv;
+  Operand<float> A{dqx, static_cast<int64_t>(s.h) * B2_DQ, 0, s.T, B2_DL, B2_DQ};
+  Operand<bf16_t> B{static_cast<const bf16_t*>(w) + w0, s.d_kv, 0, s.d_nope, s.d_kv,
+                    static_cast<int64_t>(s.C()) * s.d_kv};
+  EpiStore e{dq, s.T, s.d_nope, static_cast<int64_t>(s.h) * s.d_qk(), s.d_qk()};
+  return run_gemm_dma<DKC<1, float, 256>, DKC<1, bf16_t, 128>, 4, 2, 3, 1>(Operand<bf16_t>{}, A, B, e, s.T, s.d_nope,
+                                                                             B2_DL, 1, st, s.h);
+}
+
+int b2_dw_chunks(const Shape& s) {
+  const int64_t tiles = static_cast<int64_t>(s.h) * (128 / 128) * (B2_DL / 128);
+  int64_t c = (DW_TARGET + tiles - 1) / tiles;
+  const int64_t kmax = (s.T + BK - 1) / BK;
+  if (c > kmax) c = kmax;
+  if (c < 1) c = 1;
+  const int64_t per = ((s.T + c - 1) / c + BK - 1) / BK * BK;
+  return static_cast<int>((s.T + per - 1) / per);
+}
+
+size_t b2_dw_partial_floats(const Shape& s) {
+  return static_cast<size_t>(b2_dw_chunks(s)) * s.h * 128 * B2_DL;
+}
+
+namespace {
+// dW[head_lo + i][row0 + n][c] = sum over the K chunks of part[i][chunk][n][c], in order.
+__global__ __launch_bounds__(256) void b2_dw_sum_kernel(const float* __restrict__ part, float* __restrict__ dw,
+                                                        int h, int chunks, int64_t head_stride, int64_t row0) {
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  constexpr int64_t X = 128 * B2_DL;
+  if (j >= h * X) return;
+  const int64_t i = j / X, e = j % X;
+  const float* pp = part + i * chunks * X + e;
+  float acc = 0.f;
+#pragma unroll 8
+  for (int c = 0; c < chunks; ++c) acc += pp[c * X];
+  dw[i * head_stride + row0 * B2_DL + e] = acc;
+}
+}  // namespace
+
+hipError_t launch_b2_dw(const Shape& s, const void* x, int64_t x_ld, int64_t x_z, const void* yp, int64_t y_plane,
+                        float* partial, float* d_w, int64_t row0, hipStream_t st) {
+  // dW[head_lo + i][row0 + n][c] = sum_t x[t][i][n] y[t h + i][c] (x: q_nope or dO, bf16 exact,
+  // token pitch x_ld and head pitch x_z elements; y: d_q_abs or acc as bf16 hi/lo planes
+  // [2][R][512]); K split into chunks, summed in order.
+  const int chunks = b2_dw_chunks(s);
+  typedef DRC<1, 128> OA;  // x[t][i][n] read as A(row = n, k = t)
+  typedef DRC<2, 128> OB;  // y[t h + i][c] read as B(row = c, k = t)
+  Operand<bf16_t> A{static_cast<const bf16_t*>(x), x_ld, 0, 128, s.T, x_z};
+  Operand<bf16_t> B{static_cast<const bf16_t*>(yp), static_cast<int64_t>(s.h) * B2_DL, y_plane, B2_DL, s.T, B2_DL};
+  EpiStore e{partial, 128, B2_DL, B2_DL, 128 * B2_DL};
+  hipError_t err = run_gemm_dma<OA, OB, 2, 2, 2, 2>(A, Operand<float>{}, B, e, 128, B2_DL, s.T, chunks, st, s.h);
+  if (err != hipSuccess) return err;
+  const int64_t n = static_cast<int64_t>(s.h) * 128 * B2_DL;
+  hipLaunchKernelGGL(b2_dw_sum_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, partial,
+                     d_w + static_cast<int64_t>(s.head_lo) * s.C() * s.d_kv, s.h, chunks,
+                     static_cast<int64_t>(s.C()) * s.d_kv, row0);
   return hipGetLastError();
 }
 

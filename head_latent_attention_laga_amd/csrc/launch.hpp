@@ -84,6 +84,35 @@ hipError_t launch_absorbed_pack(const Shape& s, const float* L, const void* k_pe
 hipError_t launch_absorbed_attn(const Shape& s, const void* q_abs, const void* q, const void* kx, float* acc,
                                 float* lse, hipStream_t st);
 hipError_t launch_unabsorb_o(const Shape& s, const float* acc, const void* w, float* o, hipStream_t st);
+// Absorbed form (B2) backward: gradients of sum(dO * o) for laga_absorbed_fwd's
+// output, every product in split (fp32-class) precision, the S x S quantities
+// materialised one chunk of query rows at a time; lse, delta and acc are
+// recomputed from the chunk's own scores (workspace sized by
+// absorbed_bwd_workspace_bytes; 0: unsupported).
+size_t absorbed_bwd_workspace_bytes(const Shape& s);
+hipError_t launch_absorbed_bwd(const Shape& s, const void* q, const void* latent, const void* gamma,
+                               const float* rstd, const void* k_pe, const void* w, const void* d_o, float* dq,
+                               float* d_latent, float* d_k_pe, float* d_w, float* d_gamma, void* workspace,
+                               hipStream_t st);
+// Its products (gemm.hip).
+hipError_t launch_b2_planes(const Shape& s, const void* x, int64_t x_ld, int64_t x_z, int64_t w_row0,
+                            const void* w, void* out, int64_t out_plane, int64_t out_ld, hipStream_t st);
+hipError_t launch_b2_rows_keys(const void* rows, int64_t rows_plane, int64_t rows_ld, int64_t nrows, const void* keys,
+                               int64_t keys_plane, int64_t nkeys, int64_t kdim, float* out, int64_t out_ld,
+                               hipStream_t st);
+hipError_t launch_b2_key_grads(const void* pp, const void* dsp, int64_t p_plane, int64_t ldu, int64_t nrows,
+                               int64_t nkeys, const void* dacc_rows, int64_t dacc_plane, const void* qx_rows,
+                               int64_t qx_plane, float* dL, float* dkpe, hipStream_t st);
+// Products that contract over a chunk's keys run in at most B2_KSPLIT K
+// chunks, each to its own fp32 partial, summed in a fixed order afterwards.
+constexpr int B2_KSPLIT = 4;
+int b2_key_chunks(int64_t nrows, int ncols, int64_t kpad);
+hipError_t launch_b2_rows_by_keys(const void* ap, int64_t p_plane, int64_t ldu, int64_t nrows, int64_t kpad,
+                                  const void* keys, int64_t keys_plane, int ncols, float* part, hipStream_t st);
+hipError_t launch_b2_dq_nope(const Shape& s, const float* dqx, const void* w, float* dq, hipStream_t st);
+size_t b2_dw_partial_floats(const Shape& s);
+hipError_t launch_b2_dw(const Shape& s, const void* x, int64_t x_ld, int64_t x_z, const void* yp, int64_t y_plane,
+                        float* partial, float* d_w, int64_t row0, hipStream_t st);
 hipError_t launch_norm_bwd(const Shape& s, const float* dL, const void* latent, const void* gamma,
                            const float* rstd, float* d_latent, float* dgamma_part, float* d_gamma,
                            hipStream_t st);

@@ -101,9 +101,17 @@ class LagaPath:
                           out["acc"], out["o"], out["lse"], stream)
         return out
 
-    def alloc_backward(self):
+    def absorbed_backward(self, x, absf, d_o, grads=None, stream=None):
+        """The absorbed form's backward for the output of absorbed_forward(x) (absf: its rstd is used;
+        the backward recomputes q_abs, lse and acc itself)."""
+        g = grads or self.alloc_backward(workspace_bytes=_lib.absorbed_bwd_workspace_bytes(self.dims))
+        _lib.absorbed_bwd(self.dims, x["q"], x["latent"], x["gamma"], absf["rstd"], x["k_pe"], x["w_kv_b"], d_o,
+                          g["dq"], g["d_latent"], g["d_k_pe"], g["d_w_kv_b"], g["d_gamma"], g["workspace"], stream)
+        return g
+
+    def alloc_backward(self, workspace_bytes=None):
         B, S, h = self.B, self.S, self.h
-        ws = _lib.attn_bwd_workspace_bytes(self.dims)
+        ws = _lib.attn_bwd_workspace_bytes(self.dims) if workspace_bytes is None else workspace_bytes
         return dict(
             dq=self._empty((B, S, h, self.d_nope + self.d_rope)), d_latent=self._empty((B, S, self.d_kv)),
             d_k_pe=self._empty((B, S, self.d_rope)),

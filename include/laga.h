@@ -266,6 +266,38 @@ laga_status laga_attn_bwd_noalloc(const laga_dims* dims, const void* q, const vo
                                   float* d_latent, float* d_k_pe, float* d_w_kv_b, float* d_gamma,
                                   void* stream);
 
+/*
+ * Backward of the absorbed form (B2) [LAGA §3.2 (B2), Fig. 2; the baseline
+ * whose training cost §4.3-4.4 measure]: gradients of sum(d_o * o) for the o
+ * of laga_absorbed_fwd, taken through B2's own steps (un-absorb, latent
+ * attention, absorb):
+ *   d_acc = dO W^v,  dP = d_acc L^T,  dS = P (dP - rowsum(P dP)),
+ *   d_q_abs = dS L / sqrt(d_qk),  dq_rope = dS k_pe / sqrt(d_qk),
+ *   dL = P^T d_acc + dS^T q_abs / sqrt(d_qk),  dk_pe = sum over heads dS^T q_rope / sqrt(d_qk),
+ *   dq_nope = d_q_abs W^k^T,  dW^k = q_nope^T d_q_abs,  dW^v = dO^T acc,
+ * then the RMSNorm's backward.  The outputs equal laga_attn_bwd's (the two
+ * forms are the same function): dq [B,S,h,d_qk], d_latent [B,S,d_kv], d_k_pe
+ * [B,S,d_rope], the rows r*h .. r*h+h-1 of d_w_kv_b [n_h,C,d_kv] (other rows
+ * untouched) and d_gamma [d_kv], all float32.  Inputs (bfloat16 unless noted):
+ * q, latent, gamma, rstd (float32, from laga_latent_norm), k_pe, w_kv_b and
+ * d_o [B,S,h,d_v].  Every product keeps bf16 hi + lo terms (fp32-class
+ * accuracy); the S x S scores, probabilities and score gradients are
+ * materialised one chunk of query rows at a time, and q_abs, lse, delta and
+ * acc are recomputed from that chunk's scores at this accuracy rather than
+ * taken from the fp16-operand forward (whose rounding of acc alone would cost
+ * the dW_kv_b bar).  LAGA_BF16 inputs at the V3 head dims only (else
+ * LAGA_ERR_UNSUPPORTED).  workspace: at least laga_absorbed_bwd_workspace_bytes
+ * (dims) bytes (16-byte aligned, owned by the caller, contents irrelevant):
+ * about 8.7 KB per token and local head, 4.4 KB per token, and up to 1 GiB of
+ * chunk buffers (3.5 GB at S = 16384, h = 16).
+ */
+size_t laga_absorbed_bwd_workspace_bytes(const laga_dims* dims);
+laga_status laga_absorbed_bwd(const laga_dims* dims, const void* q, const void* latent,
+                              const void* gamma, const float* rstd, const void* k_pe,
+                              const void* w_kv_b, const void* d_o, float* dq, float* d_latent,
+                              float* d_k_pe, float* d_w_kv_b, float* d_gamma, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 /* Static, human-readable text of a status code. */
 const char* laga_status_string(laga_status status);
 

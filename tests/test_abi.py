@@ -167,6 +167,25 @@ def test_fused_workspace_is_linear_in_the_sequence(lib):
     assert ws(16384, n_h=128, sp_size=8) < 200e6
 
 
+def test_absorbed_backward_checks_on_the_host(lib):
+    d = v3()
+    need = lib.laga_absorbed_bwd_workspace_bytes(ctypes.byref(d))
+    assert need > 0
+    assert lib.laga_absorbed_bwd_workspace_bytes(ctypes.byref(tiny())) == 0
+    args = [FAKE] * 12
+    ok = (FAKE, ctypes.c_size_t(need), None)
+    assert lib.laga_absorbed_bwd(ctypes.byref(tiny()), *args, *ok) == UNSUPPORTED
+    assert lib.laga_absorbed_bwd(None, *args, *ok) == INVALID
+    for slot in (0, 3, 6, 11):
+        a = list(args)
+        a[slot] = None
+        assert lib.laga_absorbed_bwd(ctypes.byref(d), *a, *ok) == INVALID
+        a[slot] = MISALIGNED
+        assert lib.laga_absorbed_bwd(ctypes.byref(d), *a, *ok) == ALIGN
+    assert lib.laga_absorbed_bwd(ctypes.byref(d), *args, FAKE, ctypes.c_size_t(need - 1), None) == WORKSPACE
+    assert lib.laga_absorbed_bwd(ctypes.byref(d), *args, None, ctypes.c_size_t(need), None) == WORKSPACE
+
+
 def test_noalloc_scratch_size_matches_header():
     import re
     text = open(_lib.HEADER).read()

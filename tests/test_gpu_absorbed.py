@@ -13,6 +13,7 @@ import torch
 import laga_inputs as li
 import oracle
 from gpu_util import FP16, announce, check, device_inputs, host, make_path, sample_rows
+from head_latent_attention_laga_amd import _lib
 
 pytestmark = pytest.mark.gpu
 
@@ -89,3 +90,73 @@ def test_absorbed_forward_is_deterministic():
         torch.cuda.synchronize()
         for k in first:
             assert torch.equal(first[k], b[k]), k
+
+
+# ------------------------------------------------------------------ backward
+def _b2_step(d: li.Dims, seed: int):
+    inp = li.make_inputs(d, seed, backward=True)
+    x = device_inputs(inp)
+    path = make_path(d, FP16)
+    absf = path.absorbed_forward(x)
+    g = path.alloc_backward(workspace_bytes=_lib.absorbed_bwd_workspace_bytes(path.dims))
+    for k in ("dq", "d_latent", "d_k_pe", "d_gamma"):
+        g[k].fill_(float("nan"))
+    g["d_w_kv_b"].fill_(-7.0)  # rows outside this rank's shard must stay untouched
+    path.absorbed_backward(x, absf, x["d_o"], g)
+    torch.cuda.synchronize()
+    return inp, path, x, absf, g
+
+
+@pytest.mark.parametrize("B,S,n_h,P,r", [(1, 300, 16, 8, 3), (2, 130, 64, 8, 7), (1, 1, 16, 8, 0),
+                                         (1, 257, 128, 32, 5), (1, 1000, 16, 8, 2)])
+def test_absorbed_backward_shapes(B, S, n_h, P, r):
+    """Every gradient against the oracle's B2 backward (itself equal to the explicit backward)."""
+    d = li.Dims(B=B, S=S, n_h=n_h, sp_size=P, sp_rank=r, d_kv=512, d_nope=128, d_rope=64, d_v=128,
+                dtype=li.BF16)
+    announce(f"absorbed backward dims={d}")
+    inp, _, _, _, g = _b2_step(d, seed=S + 11 * r)
+    v = {k: t.value for k, t in inp.items()}
+    ref = oracle.absorbed_backward(v["q"], v["latent"], v["k_pe"], v["w_kv_b"], v["gamma"], v["d_o"], n_h=d.n_h,
+                                   sp_size=d.sp_size, sp_rank=d.sp_rank, d_nope=d.d_nope, eps=d.eps)
+    check("dq", host(g["dq"]), ref["dq"], d.dtype)
+    check("d_latent", host(g["d_latent"]), ref["d_latent"], d.dtype)
+    check("dk_pe", host(g["d_k_pe"]), ref["dk_pe"], d.dtype)
+    check("d_gamma", host(g["d_gamma"]), ref["d_gamma"], d.dtype)
+    heads = oracle.head_shard(d.n_h, d.sp_size, d.sp_rank)
+    dW = host(g["d_w_kv_b"])
+    check("d_w_kv_b", dW[heads], ref["d_w_kv_b"][heads], d.dtype)
+    others = np.ones(d.n_h, dtype=bool)
+    others[heads] = False
+    assert np.all(dW[others] == -7.0), "rows outside the head shard were written"
+
+
+def test_absorbed_backward_training_workload_against_golden():
+    """S=16384, 16 local heads: the query rows run in many chunks; sampled rows of
+    dq, d_latent, dk_pe and sampled rows of dW, and all of dgamma, against the
+    fp64 oracle's values for this workload (tests/golden)."""
+    import os
+    gold = np.load(os.path.join(os.path.dirname(__file__), "golden", "train_v3_sp8_s16384_h16.npz"),
+                   allow_pickle=False)
+    d, _ = li.workload("v3_sp8_s16384_h16_train")
+    announce(f"absorbed backward, training workload dims={d}")
+    _, path, _, _, g = _b2_step(d, seed=0)
+    rows = gold["rows"]
+    check("dq[rows]", host(g["dq"])[:, rows], gold["dq"], d.dtype)
+    check("d_latent", host(g["d_latent"])[:, rows], gold["d_latent"], d.dtype)
+    check("dk_pe", host(g["d_k_pe"])[:, rows], gold["dk_pe"], d.dtype)
+    heads = oracle.head_shard(d.n_h, d.sp_size, d.sp_rank)
+    dW = host(g["d_w_kv_b"])[heads].reshape(-1, d.d_kv)
+    check("d_w_kv_b", dW[gold["w_rows"]], gold["d_w"], d.dtype)
+    check("d_gamma", host(g["d_gamma"]), gold["d_gamma"], d.dtype)
+
+
+def test_absorbed_backward_is_deterministic():
+    d = li.Dims(B=1, S=700, n_h=16, sp_size=8, sp_rank=1, d_kv=512, d_nope=128, d_rope=64, d_v=128, dtype=li.BF16)
+    announce(f"absorbed backward determinism dims={d}")
+    _, path, x, absf, g = _b2_step(d, seed=9)
+    first = {k: t.clone() for k, t in g.items() if k != "workspace"}
+    for _ in range(2):
+        path.absorbed_backward(x, absf, x["d_o"], g)
+        torch.cuda.synchronize()
+        for k in first:
+            assert torch.equal(first[k], g[k]), k
