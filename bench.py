@@ -14,7 +14,8 @@ Prints one JSON line with tokens/s, algorithmic TFLOP/s, per-kernel times
 (HIP events on the launch stream), the roofline of the dominant kernel, the
 fp64 oracle timed on a bounded sample on the host cores, the forward alone at
 the other DeepSeek-V3 workloads (S=4096 with 16 local heads, and S=4096 with
-all 128 heads on one device), and memory: analytic activation bytes of LAGA
+all 128 heads on one device), the absorbed form (B2) forward and backward on
+the step's inputs with its own FLOPs, and memory: analytic activation bytes of LAGA
 against the explicit and absorbed forms, the backward workspace, and the peak
 that torch's allocator records over one training step.
 """
@@ -59,6 +60,17 @@ def absorbed_flops(d) -> float:
     T = d.B * d.S
     return (2 * T * d.h * d.d_nope * d.d_kv + 2 * pairs * (2 * d.d_kv + d.d_rope) * d.h * d.B
             + 2 * T * d.h * d.d_kv * d.d_v)
+
+
+def absorbed_bwd_flops(d) -> float:
+    """The absorbed form's (B2) own backward FLOPs, each product once (no recompute of the
+    scores, P or acc): per causal pair dP = d_acc L^T and dL += P^T d_acc (width d_kv),
+    d_q_abs || dq_rope = dS (L || k_pe) and dL || dk_pe += dS^T q (width d_kv + d_rope);
+    per token and head d_acc = dO W^v, dq_nope = d_q_abs W^k^T, dW^k and dW^v."""
+    pairs = d.S * (d.S + 1) / 2
+    T = d.B * d.S
+    return (2 * pairs * (4 * d.d_kv + 2 * d.d_rope) * d.h * d.B
+            + 2 * T * d.h * d.d_kv * (2 * d.d_v + 2 * d.d_nope))
 
 
 def activation_bytes(d, kv_bytes: int) -> dict:
@@ -122,11 +134,23 @@ PROFILE_KERNELS = {
     "attn_bwd_dkdv": ([["dkdv_kernel<"], ["dkdv_kernelIDF16_NS_6MmaF16ELi2"]], _N + "attn_bwd.hip"),
     "attn_bwd_dq": ([["dq_kernel<"]], _N + "attn_bwd_dq.hip"),
     "fold_dL": ([["gemm_dma_kernel<", "DKC<2, unsigned short, 64"]], _N + "gemm.hip"),
-    "fold_dW": ([["gemm_dma_kernel<", "DRC<2, 128>, laga::(anonymous namespace)::DRC<2, 128>"]], _N + "gemm.hip"),
+    "fold_dW": ([["gemm_dma_kernel<", "DRC<2, 128>, laga::(anonymous namespace)::DRC<2, 128>", "EpiStore"]],
+                _N + "gemm.hip"),
     "rmsnorm_bwd": ([["rmsnorm_bwd_kernel"]], _N + "norm.hip"),
     "absorb_q": ([["gemm_dma_kernel<", "EpiHalf"]], _N + "gemm.hip"),
     "absorbed_attn": ([["absorbed_attn_kernel"]], _N + "absorbed.hip"),
+    # o = acc W^v in the forward and dq_nope = d_q_abs W^k^T in the backward: one kernel at one shape.
     "unabsorb_o": ([["gemm_dma_kernel<", "DKC<1, float, 256, false"]], _N + "gemm.hip"),
+    "b2_planes": ([["gemm_dma_kernel<", "EpiPlanes"]], _N + "gemm.hip"),
+    "b2_scores": ([["gemm_dma_kernel<", "DKC<2, unsigned short, 128, false>, laga::(anonymous namespace)::DKC<2"]],
+                  _N + "gemm.hip"),
+    "b2_rowstat": ([["b2_rowstat_kernel"]], _N + "absorbed.hip"),
+    "b2_pds": ([["b2_pds_kernel"]], _N + "absorbed.hip"),
+    "b2_rows_by_keys": ([["gemm_dma_kernel<", "DKC<2, unsigned short, 128, false>, laga::(anonymous namespace)::DRC<2"]],
+                        _N + "gemm.hip"),
+    "b2_key_grads": ([["gemm_dma_kernel<", "DRC<2, 128>, laga::(anonymous namespace)::DRC<2, 128>", "EpiAccum"]],
+                     _N + "gemm.hip"),
+    "b2_dw": ([["gemm_dma_kernel<", "DRC<1, 128>, laga::(anonymous namespace)::DRC<2, 128>"]], _N + "gemm.hip"),
 }
 # Kernels of the forward-only path run once per forward-only workload; their grid
 # (work-items) tells the workloads apart.
@@ -241,7 +265,7 @@ def summarize_profiles(out_root: str):
           "```", "", "An unprofiled `python bench.py --no-cpu-baseline` on the same box:", "", "```",
           "step kernels (ms): " + json.dumps(bench["kernels_ms"]),
           "forward fp16: " + json.dumps(bench["forward_fp16_operands"]),
-          "absorbed form forward: " + json.dumps(bench.get("absorbed_form_fwd")),
+          "absorbed form: " + json.dumps(bench.get("absorbed_form")),
           f"step {bench['ms_per_step']} ms, {bench['value']} tokens/s, {bench['tflops_step']} TFLOP/s; "
           f"roofline {json.dumps(bench['roofline'])}", "```", ""]
     open(os.path.join(prof, "step_v3_s16384_h16_kernel_trace.md"), "w").write("\n".join(L))
@@ -571,7 +595,7 @@ def main():
     fused_ms = time_fused(fast, x, args.steps, args.warmup)
     fsum = forward_summary(d, fper, fused_ms)
 
-    # The absorbed form (B2) on the same inputs, forward only, and the device memory
+    # The absorbed form (B2) on the same inputs: its forward, and the device memory
     # each form's forward allocates for its outputs and kept intermediates (what a
     # training step holds until the backward), read from torch's allocator.
     m0 = torch.cuda.memory_allocated()
@@ -590,11 +614,35 @@ def main():
         ae[i][1].record()
     torch.cuda.synchronize()
     abs_ms = statistics.mean(ae[i][0].elapsed_time(ae[i][1]) for i in range(args.steps))
-    del absb
+    # Its backward (every product with bf16 hi + lo terms, like the step's split operands),
+    # which recomputes q_abs, the scores, lse and acc from the inputs one chunk of query
+    # rows at a time.
+    absg = fast.alloc_backward(workspace_bytes=_lib.absorbed_bwd_workspace_bytes(fast.dims))
+    be = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for _ in range(max(1, args.warmup // 2)):
+        fast.absorbed_backward(x, absb, x["d_o"], absg)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        be[i][0].record()
+        fast.absorbed_backward(x, absb, x["d_o"], absg)
+        be[i][1].record()
+    torch.cuda.synchronize()
+    absb_ms = statistics.mean(be[i][0].elapsed_time(be[i][1]) for i in range(args.steps))
+    del absb, absg
+    abs_step = abs_ms + absb_ms
+    abs_step_fl = absorbed_flops(d) + absorbed_bwd_flops(d)
     absorbed = {
-        "ms": round(abs_ms, 4), "tokens_s": round(d.B * d.S / (abs_ms / 1e3), 1),
-        "tflops_own": round(absorbed_flops(d) / (abs_ms / 1e3) / 1e12, 2),
-        "time_vs_laga_fwd_fp16": round(abs_ms / min(fused_ms, fper["rmsnorm_fwd"] + fper["kv_up"] + fper["attn_fwd"]), 3),
+        "fwd_ms": round(abs_ms, 4), "fwd_tokens_s": round(d.B * d.S / (abs_ms / 1e3), 1),
+        "fwd_tflops_own": round(absorbed_flops(d) / (abs_ms / 1e3) / 1e12, 2),
+        "fwd_time_vs_laga_fwd_fp16": round(abs_ms / min(fused_ms, fper["rmsnorm_fwd"] + fper["kv_up"]
+                                                        + fper["attn_fwd"]), 3),
+        "bwd_ms": round(absb_ms, 4), "bwd_tflops_own": round(absorbed_bwd_flops(d) / (absb_ms / 1e3) / 1e12, 2),
+        "step_ms": round(abs_step, 4), "step_tokens_s": round(d.B * d.S / (abs_step / 1e3), 1),
+        "step_tflops_own": round(abs_step_fl / (abs_step / 1e3) / 1e12, 2),
+        "step_frac_peak_own": round(abs_step_fl / (abs_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "step_flops_vs_laga": round(abs_step_fl / fl["step"], 3),
+        "step_time_vs_laga": round(abs_step / ms_step, 3),
+        "bwd_workspace_mb": round(_lib.absorbed_bwd_workspace_bytes(fast.dims) / 2**20, 1),
         "forward_buffers_mb": {"laga_split": round((m1 - m0) / 2**20, 1), "absorbed": round((m2 - m1) / 2**20, 1)},
     }
 
@@ -642,7 +690,7 @@ def main():
         "activation_mb": act,
         "memory_step_mb": mem,
         "forward_other_workloads": other,
-        "absorbed_form_fwd": absorbed,
+        "absorbed_form": absorbed,
         "gpu": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline:
