@@ -52,6 +52,7 @@ _SIGS = {
     "laga_absorbed_fwd": (ctypes.c_int, [ctypes.POINTER(laga_dims)] + [_P] * 10),
     "laga_attn_fwd_fused_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(laga_dims)]),
     "laga_absorbed_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(laga_dims)]),
+    "laga_absorbed_bwd_min_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(laga_dims)]),
     "laga_absorbed_bwd": (ctypes.c_int, [ctypes.POINTER(laga_dims)] + [_P] * 13 + [ctypes.c_size_t, _P]),
     "laga_attn_fwd_fused": (ctypes.c_int, [ctypes.POINTER(laga_dims)] + [_P] * 8 + [ctypes.c_size_t, _P]),
     "laga_attn_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(laga_dims)]),
@@ -149,6 +150,10 @@ def attn_fwd_fused(dims, q, latent, gamma, k_pe, w_kv_b, o, lse, workspace, stre
 
 def absorbed_bwd_workspace_bytes(dims) -> int:
     return int(load().laga_absorbed_bwd_workspace_bytes(ctypes.byref(dims)))
+
+
+def absorbed_bwd_min_workspace_bytes(dims) -> int:
+    return int(load().laga_absorbed_bwd_min_workspace_bytes(ctypes.byref(dims)))
 
 
 def absorbed_bwd(dims, q, latent, gamma, rstd, k_pe, w_kv_b, d_o, dq, d_latent, d_k_pe, d_w_kv_b, d_gamma,

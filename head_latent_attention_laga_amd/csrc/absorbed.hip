@@ -533,13 +533,17 @@ struct B2Layout {
   size_t qx, dacc, kxp, accp, dqx, dL, sbuf, dpbuf, pp, dsp, rlse, rdelta, kpart, dw, dg, total;
 };
 
-B2Layout b2_layout(const Shape& s) {
+// tc: tokens per chunk of query rows (a multiple of 32); 0 picks the default,
+// the largest whose chunk buffers fit B2_CHUNK_CAP_MB.
+B2Layout b2_layout(const Shape& s, int64_t tc = 0) {
   B2Layout L;
   L.R = s.T * s.h;
   L.Tp = s.T + 32;
   L.ldu = (s.S + 31) / 32 * 32;
-  const int64_t per_token = 16 * static_cast<int64_t>(s.h) * L.ldu;  // S, dP (fp32), P, c.dS (2 bf16 planes)
-  int64_t tc = (static_cast<int64_t>(B2_CHUNK_CAP_MB) << 20) / per_token / 32 * 32;
+  if (tc <= 0) {
+    const int64_t per_token = 16 * static_cast<int64_t>(s.h) * L.ldu;  // S, dP (fp32), P, c.dS (2 bf16 planes)
+    tc = (static_cast<int64_t>(B2_CHUNK_CAP_MB) << 20) / per_token / 32 * 32;
+  }
   if (tc < 32) tc = 32;
   if (tc > L.ldu) tc = L.ldu;
   L.tc = tc;
@@ -574,13 +578,31 @@ bool b2_supported(const Shape& s) { return s.bf16 && s.d_kv == DL && s.d_rope ==
 }  // namespace
 
 size_t absorbed_bwd_workspace_bytes(const Shape& s) { return b2_supported(s) ? b2_layout(s).total : 0; }
+size_t absorbed_bwd_min_workspace_bytes(const Shape& s) { return b2_supported(s) ? b2_layout(s, 32).total : 0; }
+
+namespace {
+// The layout a call runs with: the default chunk size, or for a smaller
+// workspace the largest chunk (in steps of 32 tokens) whose layout fits.
+B2Layout b2_layout_for(const Shape& s, size_t bytes) {
+  B2Layout L = b2_layout(s);
+  if (L.total <= bytes) return L;
+  int64_t lo = 32, hi = L.tc;  // layout(lo) fits (checked by the caller), layout(hi) does not
+  while (hi - lo > 32) {
+    const int64_t mid = (lo + hi) / 64 * 32;
+    if (b2_layout(s, mid).total <= bytes) lo = mid;
+    else hi = mid;
+  }
+  return b2_layout(s, lo);
+}
+}  // namespace
 
 hipError_t launch_absorbed_bwd(const Shape& s, const void* q, const void* latent, const void* gamma,
                                const float* rstd, const void* k_pe, const void* w, const void* d_o, float* dq,
                                float* d_latent, float* d_k_pe, float* d_w, float* d_gamma, void* workspace,
-                               hipStream_t st) {
+                               size_t workspace_bytes, hipStream_t st) {
   if (!b2_supported(s)) return hipErrorNotSupported;
-  const B2Layout L = b2_layout(s);
+  if (workspace_bytes < absorbed_bwd_min_workspace_bytes(s)) return hipErrorInvalidValue;
+  const B2Layout L = b2_layout_for(s, workspace_bytes);
   char* ws = static_cast<char*>(workspace);
   bf16_t* qx = reinterpret_cast<bf16_t*>(ws + L.qx);
   bf16_t* dacc = reinterpret_cast<bf16_t*>(ws + L.dacc);

@@ -179,6 +179,12 @@ size_t laga_absorbed_bwd_workspace_bytes(const laga_dims* dims) {
   return laga::absorbed_bwd_workspace_bytes(s);
 }
 
+size_t laga_absorbed_bwd_min_workspace_bytes(const laga_dims* dims) {
+  Shape s;
+  if (check_dims(dims, &s) != LAGA_OK) return 0;
+  return laga::absorbed_bwd_min_workspace_bytes(s);
+}
+
 laga_status laga_absorbed_bwd(const laga_dims* dims, const void* q, const void* latent, const void* gamma,
                               const float* rstd, const void* k_pe, const void* w_kv_b, const void* d_o, float* dq,
                               float* d_latent, float* d_k_pe, float* d_w_kv_b, float* d_gamma, void* workspace,
@@ -186,7 +192,7 @@ laga_status laga_absorbed_bwd(const laga_dims* dims, const void* q, const void* 
   Shape s;
   laga_status st = check_dims(dims, &s);
   if (st != LAGA_OK) return st;
-  const size_t need = laga::absorbed_bwd_workspace_bytes(s);
+  const size_t need = laga::absorbed_bwd_min_workspace_bytes(s);
   if (need == 0) return LAGA_ERR_UNSUPPORTED;
   const void* ptrs[] = {q, latent, gamma, rstd, k_pe, w_kv_b, d_o, dq, d_latent, d_k_pe, d_w_kv_b, d_gamma};
   for (const void* p : ptrs)
@@ -196,7 +202,8 @@ laga_status laga_absorbed_bwd(const laga_dims* dims, const void* q, const void* 
   if (workspace == nullptr || workspace_bytes < need) return LAGA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return LAGA_ERR_ALIGN;
   return from_hip(laga::launch_absorbed_bwd(s, q, latent, gamma, rstd, k_pe, w_kv_b, d_o, dq, d_latent, d_k_pe,
-                                            d_w_kv_b, d_gamma, workspace, static_cast<hipStream_t>(stream)));
+                                            d_w_kv_b, d_gamma, workspace, workspace_bytes,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 laga_status laga_absorbed_fwd(const laga_dims* dims, const void* q, const float* latent_n, const void* k_pe,

@@ -87,13 +87,15 @@ hipError_t launch_unabsorb_o(const Shape& s, const float* acc, const void* w, fl
 // Absorbed form (B2) backward: gradients of sum(dO * o) for laga_absorbed_fwd's
 // output, every product in split (fp32-class) precision, the S x S quantities
 // materialised one chunk of query rows at a time; lse, delta and acc are
-// recomputed from the chunk's own scores (workspace sized by
-// absorbed_bwd_workspace_bytes; 0: unsupported).
+// recomputed from the chunk's own scores.  Workspace: absorbed_bwd_workspace_bytes
+// for the default chunks; any size down to absorbed_bwd_min_workspace_bytes
+// (32-token chunks) runs with the largest chunks that fit (0: unsupported).
 size_t absorbed_bwd_workspace_bytes(const Shape& s);
+size_t absorbed_bwd_min_workspace_bytes(const Shape& s);
 hipError_t launch_absorbed_bwd(const Shape& s, const void* q, const void* latent, const void* gamma,
                                const float* rstd, const void* k_pe, const void* w, const void* d_o, float* dq,
                                float* d_latent, float* d_k_pe, float* d_w, float* d_gamma, void* workspace,
-                               hipStream_t st);
+                               size_t workspace_bytes, hipStream_t st);
 // Its products (gemm.hip).
 hipError_t launch_b2_planes(const Shape& s, const void* x, int64_t x_ld, int64_t x_z, int64_t w_row0,
                             const void* w, void* out, int64_t out_plane, int64_t out_ld, hipStream_t st);

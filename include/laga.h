@@ -286,12 +286,17 @@ laga_status laga_attn_bwd_noalloc(const laga_dims* dims, const void* q, const vo
  * acc are recomputed from that chunk's scores at this accuracy rather than
  * taken from the fp16-operand forward (whose rounding of acc alone would cost
  * the dW_kv_b bar).  LAGA_BF16 inputs at the V3 head dims only (else
- * LAGA_ERR_UNSUPPORTED).  workspace: at least laga_absorbed_bwd_workspace_bytes
- * (dims) bytes (16-byte aligned, owned by the caller, contents irrelevant):
- * about 8.7 KB per token and local head, 4.4 KB per token, and up to 1 GiB of
- * chunk buffers (3.5 GB at S = 16384, h = 16).
+ * LAGA_ERR_UNSUPPORTED).  workspace (16-byte aligned, owned by the caller,
+ * contents irrelevant): laga_absorbed_bwd_workspace_bytes(dims) bytes give the
+ * default chunks, about 8.7 KB per token and local head, 4.4 KB per token, and
+ * up to 1 GiB of chunk buffers (3.5 GB at S = 16384, h = 16).  A smaller
+ * workspace, down to laga_absorbed_bwd_min_workspace_bytes(dims) (chunks of 32
+ * tokens), runs with the largest chunks that fit it: less memory, more
+ * launches; below the minimum the call returns LAGA_ERR_WORKSPACE.  Results of
+ * different chunkings agree to rounding (the order of the sums over chunks).
  */
 size_t laga_absorbed_bwd_workspace_bytes(const laga_dims* dims);
+size_t laga_absorbed_bwd_min_workspace_bytes(const laga_dims* dims);
 laga_status laga_absorbed_bwd(const laga_dims* dims, const void* q, const void* latent,
                               const void* gamma, const float* rstd, const void* k_pe,
                               const void* w_kv_b, const void* d_o, float* dq, float* d_latent,

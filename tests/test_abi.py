@@ -182,8 +182,26 @@ def test_absorbed_backward_checks_on_the_host(lib):
         assert lib.laga_absorbed_bwd(ctypes.byref(d), *a, *ok) == INVALID
         a[slot] = MISALIGNED
         assert lib.laga_absorbed_bwd(ctypes.byref(d), *a, *ok) == ALIGN
-    assert lib.laga_absorbed_bwd(ctypes.byref(d), *args, FAKE, ctypes.c_size_t(need - 1), None) == WORKSPACE
+    # Smaller workspaces run with smaller chunks, down to 32-token chunks.
+    least = lib.laga_absorbed_bwd_min_workspace_bytes(ctypes.byref(d))
+    assert 0 < least < need
+    assert lib.laga_absorbed_bwd_min_workspace_bytes(ctypes.byref(tiny())) == 0
+    assert lib.laga_absorbed_bwd(ctypes.byref(d), *args, FAKE, ctypes.c_size_t(least - 1), None) == WORKSPACE
     assert lib.laga_absorbed_bwd(ctypes.byref(d), *args, None, ctypes.c_size_t(need), None) == WORKSPACE
+
+
+def test_absorbed_backward_workspace_sizes():
+    """Default and minimum workspaces: at S=16384, 16 heads the default holds 1 GiB
+    of chunk buffers beside the per-row planes; the minimum (32-token chunks) is
+    linear in S."""
+    def sizes(S):
+        d = _lib.make_dims(1, S, 128, 8, 0, 512, 128, 64, 128, _lib.LAGA_BF16, 0)
+        return _lib.absorbed_bwd_workspace_bytes(d), _lib.absorbed_bwd_min_workspace_bytes(d)
+    full, least = sizes(16384)
+    assert 3.3e9 < full < 3.6e9
+    assert full - least > 0.9e9
+    m1, m2, m3 = (sizes(S)[1] for S in (4096, 8192, 12288))
+    assert abs((m3 - m2) - (m2 - m1)) < 1e6
 
 
 def test_noalloc_scratch_size_matches_header():

@@ -1,4 +1,4 @@
-"""Absorbed-form (B2) forward against the fp64 oracle (needs an MI355X).
+"""Absorbed-form (B2) forward and backward against the fp64 oracle (needs an MI355X).
 
 B2 is the pages' inference-side reformulation ported to training [LAGA §3.2
 (B2)]: the outputs (o, lse) equal the explicit form's, and the two
@@ -93,12 +93,15 @@ def test_absorbed_forward_is_deterministic():
 
 
 # ------------------------------------------------------------------ backward
-def _b2_step(d: li.Dims, seed: int):
+def _b2_step(d: li.Dims, seed: int, workspace: str = "default"):
     inp = li.make_inputs(d, seed, backward=True)
     x = device_inputs(inp)
     path = make_path(d, FP16)
     absf = path.absorbed_forward(x)
-    g = path.alloc_backward(workspace_bytes=_lib.absorbed_bwd_workspace_bytes(path.dims))
+    full = _lib.absorbed_bwd_workspace_bytes(path.dims)
+    least = _lib.absorbed_bwd_min_workspace_bytes(path.dims)
+    ws = {"default": full, "min": least, "mid": (full + least) // 2}[workspace]
+    g = path.alloc_backward(workspace_bytes=ws)
     for k in ("dq", "d_latent", "d_k_pe", "d_gamma"):
         g[k].fill_(float("nan"))
     g["d_w_kv_b"].fill_(-7.0)  # rows outside this rank's shard must stay untouched
@@ -107,14 +110,18 @@ def _b2_step(d: li.Dims, seed: int):
     return inp, path, x, absf, g
 
 
-@pytest.mark.parametrize("B,S,n_h,P,r", [(1, 300, 16, 8, 3), (2, 130, 64, 8, 7), (1, 1, 16, 8, 0),
-                                         (1, 257, 128, 32, 5), (1, 1000, 16, 8, 2)])
-def test_absorbed_backward_shapes(B, S, n_h, P, r):
-    """Every gradient against the oracle's B2 backward (itself equal to the explicit backward)."""
+@pytest.mark.parametrize("B,S,n_h,P,r,ws", [(1, 300, 16, 8, 3, "default"), (2, 130, 64, 8, 7, "default"),
+                                            (1, 1, 16, 8, 0, "default"), (1, 257, 128, 32, 5, "default"),
+                                            (1, 1000, 16, 8, 2, "default"), (1, 1000, 16, 8, 2, "min"),
+                                            (2, 300, 16, 8, 5, "min"), (1, 1000, 16, 8, 4, "mid")])
+def test_absorbed_backward_shapes(B, S, n_h, P, r, ws):
+    """Every gradient against the oracle's B2 backward (itself equal to the explicit
+    backward).  ws: the workspace passed; "min" runs 32-token chunks of query rows
+    (32 chunks at S=1000, 10 per sequence at S=300), "mid" a size in between."""
     d = li.Dims(B=B, S=S, n_h=n_h, sp_size=P, sp_rank=r, d_kv=512, d_nope=128, d_rope=64, d_v=128,
                 dtype=li.BF16)
-    announce(f"absorbed backward dims={d}")
-    inp, _, _, _, g = _b2_step(d, seed=S + 11 * r)
+    announce(f"absorbed backward dims={d} workspace={ws}")
+    inp, _, _, _, g = _b2_step(d, seed=S + 11 * r, workspace=ws)
     v = {k: t.value for k, t in inp.items()}
     ref = oracle.absorbed_backward(v["q"], v["latent"], v["k_pe"], v["w_kv_b"], v["gamma"], v["d_o"], n_h=d.n_h,
                                    sp_size=d.sp_size, sp_rank=d.sp_rank, d_nope=d.d_nope, eps=d.eps)
