@@ -155,7 +155,7 @@ PROFILE_KERNELS = {
 # Kernels of the forward-only path run once per forward-only workload; their grid
 # (work-items) tells the workloads apart.
 FWD_ONLY_GRIDS = {
-    "kv_up_fp16": {1048576: "S=16384 h=16", 262144: "S=4096 h=16", 2097152: "S=4096 h=128"},
+    "kv_up_fp16": {524288: "S=16384 h=16", 131072: "S=4096 h=16", 1048576: "S=4096 h=128"},
     "attn_fwd_fp16": {524288: "S=16384 h=16", 131072: "S=4096 h=16", 1048576: "S=4096 h=128"},
     "attn_fwd_fused": {1048576: "S=16384 h=16", 262144: "S=4096 h=16", 2097152: "S=4096 h=128"},
     "fused_prep": {2359552: "S=16384 h=16", 524544: "S=4096 h=16", 1310976: "S=4096 h=128"},
@@ -242,7 +242,7 @@ def summarize_profiles(out_root: str):
     line = [ln for ln in open(os.path.join(out_root, "kt.log")) if ln.startswith('{"metric"')]
     prun = json.loads(line[-1]) if line else None
     L = [f"# Kernel trace: LAGA training step, fp16-operand forward (unfused and fused) and absorbed-form (B2) "
-         f"forward, {title}", "", "Command (on the GPU box):", "", "```",
+         f"forward and backward, {title}", "", "Command (on the GPU box):", "", "```",
          PROFILE_CMD.format(opts="--kernel-trace --stats", d="kt", o="kt", args=KT_ARGS), "```", "",
          "Per launch, from the trace (`kt_kernel_trace.csv`), in us. For the step's kernels, 'timed' is the mean "
          "over the launches inside bench.py's timed region and 'bench' the HIP-event mean that the same run "
