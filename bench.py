@@ -148,7 +148,8 @@ PROFILE_KERNELS = {
     "b2_pds": ([["b2_pds_kernel"]], _N + "absorbed.hip"),
     "b2_rows_by_keys": ([["gemm_dma_kernel<", "DKC<2, unsigned short, 128, false>, laga::(anonymous namespace)::DRC<2"]],
                         _N + "gemm.hip"),
-    "b2_key_grads": ([["gemm_dma_kernel<", "DRC<2, 128>, laga::(anonymous namespace)::DRC<2, 128>", "EpiAccum"]],
+    "b2_key_grads": ([["gemm_dma_kernel<", "DRC<2, 128>, laga::(anonymous namespace)::DRC<2, 128>", "EpiAccum"],
+                      ["gemm_dma_kernel<", "DRC<2, 128>, laga::(anonymous namespace)::DRC<2, 128>", "EpiPart"]],
                      _N + "gemm.hip"),
     "b2_dw": ([["gemm_dma_kernel<", "DRC<1, 128>, laga::(anonymous namespace)::DRC<2, 128>"]], _N + "gemm.hip"),
 }

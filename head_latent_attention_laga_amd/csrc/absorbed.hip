@@ -32,6 +32,8 @@
 // pass and the 4 rows of a transposing read fall on different banks, and with
 // 128-byte aligned rows every read is a per-lane base XOR a constant plus an
 // immediate offset.
+#include <algorithm>
+
 #include "attn_common.hpp"
 #include "launch.hpp"
 
@@ -438,14 +440,29 @@ __global__ __launch_bounds__(256) void b2_pds_kernel(const float* __restrict__ S
   const float dl = delta[rr];
   const float sc2 = scale * 1.4426950408889634f;
   float p[8], ds[8];
+  const int64_t lim = st < nkeys - 1 ? st : nkeys - 1;  // last key of the row
+  if (u0 + 7 <= lim) {  // the whole group is valid: two 16-byte loads of each
+    const f32x4 s0 = *reinterpret_cast<const f32x4*>(S + rr * ldu + u0);
+    const f32x4 s1 = *reinterpret_cast<const f32x4*>(S + rr * ldu + u0 + 4);
+    const f32x4 d0 = *reinterpret_cast<const f32x4*>(dP + rr * ldu + u0);
+    const f32x4 d1 = *reinterpret_cast<const f32x4*>(dP + rr * ldu + u0 + 4);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int64_t u = u0 + k;
-    p[k] = 0.f;
-    ds[k] = 0.f;
-    if (u < nkeys && u <= st) {
-      p[k] = __builtin_amdgcn_exp2f(fmaf(S[rr * ldu + u], sc2, -lse2));
-      ds[k] = scale * p[k] * (dP[rr * ldu + u] - dl);
+    for (int k = 0; k < 4; ++k) {
+      p[k] = __builtin_amdgcn_exp2f(fmaf(s0[k], sc2, -lse2));
+      p[4 + k] = __builtin_amdgcn_exp2f(fmaf(s1[k], sc2, -lse2));
+      ds[k] = scale * p[k] * (d0[k] - dl);
+      ds[4 + k] = scale * p[4 + k] * (d1[k] - dl);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int64_t u = u0 + k;
+      p[k] = 0.f;
+      ds[k] = 0.f;
+      if (u <= lim) {
+        p[k] = __builtin_amdgcn_exp2f(fmaf(S[rr * ldu + u], sc2, -lse2));
+        ds[k] = scale * p[k] * (dP[rr * ldu + u] - dl);
+      }
     }
   }
   u16x8 h8, l8;
@@ -530,7 +547,7 @@ unsigned blocks_for(int64_t n) { return static_cast<unsigned>((n + 255) / 256); 
 // Workspace of laga_absorbed_bwd, regions 256-byte aligned.
 struct B2Layout {
   int64_t R, Tp, ldu, tc, rc_max;
-  size_t qx, dacc, kxp, accp, dqx, dL, sbuf, dpbuf, pp, dsp, rlse, rdelta, kpart, dw, dg, total;
+  size_t qx, dacc, kxp, accp, dqx, dL, sbuf, dpbuf, pp, dsp, rlse, rdelta, kpart, kgpart, dw, dg, total;
 };
 
 // tc: tokens per chunk of query rows (a multiple of 32); 0 picks the default,
@@ -567,6 +584,14 @@ B2Layout b2_layout(const Shape& s, int64_t tc = 0) {
   L.rlse = take(static_cast<size_t>(L.rc_max) * 4);
   L.rdelta = take(static_cast<size_t>(L.rc_max) * 4);
   L.kpart = take(static_cast<size_t>(B2_KSPLIT) * L.rc_max * DQ * 4);
+  // Key-side partials: the largest over the chunks that split their rows.
+  size_t kg = 0;
+  for (int64_t s0 = 0; s0 < s.S; s0 += L.tc) {
+    const int64_t s1 = s0 + L.tc < s.S ? s0 + L.tc : s.S;
+    const int nch = b2_keygrad_chunks(s1, (s1 - s0) * s.h);
+    if (nch > 1) kg = std::max(kg, static_cast<size_t>(2) * nch * s1 * DQ);
+  }
+  L.kgpart = take(kg * 4);
   L.dw = take(b2_dw_partial_floats(s) * 4);
   L.dg = take(norm_bwd_partial_floats(s) * 4);
   L.total = off;
@@ -611,6 +636,7 @@ hipError_t launch_absorbed_bwd(const Shape& s, const void* q, const void* latent
   float* rlse = reinterpret_cast<float*>(ws + L.rlse);
   float* rdelta = reinterpret_cast<float*>(ws + L.rdelta);
   float* kpart = reinterpret_cast<float*>(ws + L.kpart);
+  float* kgpart = reinterpret_cast<float*>(ws + L.kgpart);
   float* dqx = reinterpret_cast<float*>(ws + L.dqx);
   float* dL = reinterpret_cast<float*>(ws + L.dL);
   float* sbuf = reinterpret_cast<float*>(ws + L.sbuf);
@@ -657,7 +683,7 @@ hipError_t launch_absorbed_bwd(const Shape& s, const void* q, const void* latent
                          nrows, accp + r0 * DL, R * DL);
       B2_TRY(hipGetLastError());
       B2_TRY(launch_b2_key_grads(pp, dsp, pplane, L.ldu, nrows, nkeys, dacc + r0 * DL, dacc_plane, qx + r0 * DQ,
-                                 qx_plane, dL + b * s.S * DL, d_k_pe + b * s.S * DR, st));
+                                 qx_plane, dL + b * s.S * DL, d_k_pe + b * s.S * DR, kgpart, st));
       B2_TRY(launch_b2_rows_by_keys(dsp, pplane, L.ldu, nrows, kpad, keys, kxp_plane, DQ, kpart, st));
       const int ncq = b2_key_chunks(nrows, DQ, kpad);
       hipLaunchKernelGGL(b2_ksum_kernel, dim3(blocks_for(nrows * (DQ / 4))), dim3(256), 0, st, kpart, ncq,

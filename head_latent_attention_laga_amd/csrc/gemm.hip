@@ -245,6 +245,10 @@ struct EpiStore {  // out[z * chunk_stride + m * ld + n] (z: batch * chunks + K 
   }
 };
 
+// EpiStore into K-chunk partials (its own type, so that these launches are
+// told apart from other stores of the same operand shapes in a trace).
+struct EpiPart : EpiStore {};
+
 // out as bf16 hi + lo planes (x = hi + lo to about 2^-16), four consecutive n at
 // a time: hi at p[z * zstride + m * ld + n], lo at the same place + plane.
 struct EpiPlanes {
@@ -934,21 +938,70 @@ hipError_t launch_b2_rows_keys(const void* rows, int64_t rows_plane, int64_t row
                                                                              kdim, 1, st);
 }
 
+int b2_keygrad_chunks(int64_t nkeys, int64_t nrows) {
+  // K (= rows) chunks so that the dS product (576 columns) runs about 512
+  // workgroups; at most B2_KG_SPLIT, at least 256 rows each.
+  const int64_t tiles = ((nkeys + 127) / 128) * ((B2_DQ + 127) / 128);
+  int64_t c = (512 + tiles - 1) / tiles;
+  if (c > B2_KG_SPLIT) c = B2_KG_SPLIT;
+  if (c > nrows / 256) c = nrows / 256;
+  if (c < 1) c = 1;
+  const int64_t per = ((nrows + c - 1) / c + BK - 1) / BK * BK;  // as run_gemm_dma splits
+  return static_cast<int>((nrows + per - 1) / per);
+}
+
+namespace {
+// dL[u][c] += sum over k of part[k][u][c] (c < 512) and dk_pe[u][c - 512] +=
+// the same for c >= 512, where k runs over the nch partials of the P product
+// (columns < 512 only) and then the nch partials of the c.dS product, in that
+// order.  part[g][k][u][576], g = 0 (P) / 1 (c.dS).  One thread per 4 columns.
+__global__ __launch_bounds__(256) void b2_kg_sum_kernel(const float* __restrict__ part, int nch, int64_t nkeys,
+                                                        float* __restrict__ dL, float* __restrict__ dkpe) {
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (j >= nkeys * (B2_DQ / 4)) return;
+  const int64_t u = j / (B2_DQ / 4);
+  const int c = static_cast<int>(j % (B2_DQ / 4)) * 4;
+  const int64_t e = u * B2_DQ + c, gs = static_cast<int64_t>(nch) * nkeys * B2_DQ;
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+  if (c < B2_DL)
+    for (int k = 0; k < nch; ++k) v += *reinterpret_cast<const f32x4*>(part + k * nkeys * B2_DQ + e);
+  for (int k = 0; k < nch; ++k) v += *reinterpret_cast<const f32x4*>(part + gs + k * nkeys * B2_DQ + e);
+  float* o = c < B2_DL ? dL + u * B2_DL + c : dkpe + u * 64 + (c - B2_DL);
+  *reinterpret_cast<f32x4*>(o) += v;
+}
+}  // namespace
+
 hipError_t launch_b2_key_grads(const void* pp, const void* dsp, int64_t p_plane, int64_t ldu, int64_t nrows,
                                int64_t nkeys, const void* dacc_rows, int64_t dacc_plane, const void* qx_rows,
-                               int64_t qx_plane, float* dL, float* dkpe, hipStream_t st) {
+                               int64_t qx_plane, float* dL, float* dkpe, float* part, hipStream_t st) {
   // dL[u][c] += sum_r P[r][u] dacc[r][c]; (dL || dk_pe)[u][c] += sum_r cdS[r][u] qx[r][c].
+  // With few key tiles the rows (K) are split into chunks whose fp32 partials
+  // (part: 2 b2_keygrad_chunks(nkeys, nrows) nkeys 576 floats) are summed in
+  // a fixed order.
   typedef DRC<2, 128> OA;  // P / cdS [r][u] read as A(row = u, k = r)
   typedef DRC<2, 128> OB;  // dacc / qx [r][c] read as B(row = c, k = r)
   Operand<bf16_t> Ap{static_cast<const bf16_t*>(pp), ldu, p_plane, nkeys, nrows};
   Operand<bf16_t> Bd{static_cast<const bf16_t*>(dacc_rows), B2_DL, dacc_plane, B2_DL, nrows};
-  EpiAccum e1{dL, B2_DL, dkpe, 64, nkeys, B2_DL, B2_DL};
-  hipError_t err = run_gemm_dma<OA, OB, 2, 2, 2, 2>(Ap, Operand<float>{}, Bd, e1, nkeys, B2_DL, nrows, 1, st);
-  if (err != hipSuccess) return err;
   Operand<bf16_t> As{static_cast<const bf16_t*>(dsp), ldu, p_plane, nkeys, nrows};
   Operand<bf16_t> Bq{static_cast<const bf16_t*>(qx_rows), B2_DQ, qx_plane, B2_DQ, nrows};
-  EpiAccum e2{dL, B2_DL, dkpe, 64, nkeys, B2_DQ, B2_DL};
-  return run_gemm_dma<OA, OB, 2, 2, 2, 2>(As, Operand<float>{}, Bq, e2, nkeys, B2_DQ, nrows, 1, st);
+  const int nch = b2_keygrad_chunks(nkeys, nrows);
+  if (nch == 1) {
+    EpiAccum e1{dL, B2_DL, dkpe, 64, nkeys, B2_DL, B2_DL};
+    hipError_t err = run_gemm_dma<OA, OB, 2, 2, 2, 2>(Ap, Operand<float>{}, Bd, e1, nkeys, B2_DL, nrows, 1, st);
+    if (err != hipSuccess) return err;
+    EpiAccum e2{dL, B2_DL, dkpe, 64, nkeys, B2_DQ, B2_DL};
+    return run_gemm_dma<OA, OB, 2, 2, 2, 2>(As, Operand<float>{}, Bq, e2, nkeys, B2_DQ, nrows, 1, st);
+  }
+  const int64_t stride = nkeys * B2_DQ;
+  EpiPart e1{{part, nkeys, B2_DL, B2_DQ, stride}};
+  hipError_t err = run_gemm_dma<OA, OB, 2, 2, 2, 2>(Ap, Operand<float>{}, Bd, e1, nkeys, B2_DL, nrows, nch, st);
+  if (err != hipSuccess) return err;
+  EpiPart e2{{part + nch * stride, nkeys, B2_DQ, B2_DQ, stride}};
+  err = run_gemm_dma<OA, OB, 2, 2, 2, 2>(As, Operand<float>{}, Bq, e2, nkeys, B2_DQ, nrows, nch, st);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(b2_kg_sum_kernel, dim3(static_cast<unsigned>((nkeys * (B2_DQ / 4) + 255) / 256)), dim3(256),
+                     0, st, part, nch, nkeys, dL, dkpe);
+  return hipGetLastError();
 }
 
 int b2_key_chunks(int64_t nrows, int ncols, int64_t kpad) {

@@ -102,9 +102,13 @@ hipError_t launch_b2_planes(const Shape& s, const void* x, int64_t x_ld, int64_t
 hipError_t launch_b2_rows_keys(const void* rows, int64_t rows_plane, int64_t rows_ld, int64_t nrows, const void* keys,
                                int64_t keys_plane, int64_t nkeys, int64_t kdim, float* out, int64_t out_ld,
                                hipStream_t st);
+// Products over rows into the key-side gradients; with few key tiles their K
+// runs in up to B2_KG_SPLIT chunks into `part`, 2 b2_keygrad_chunks nkeys 576 floats.
+constexpr int B2_KG_SPLIT = 8;
+int b2_keygrad_chunks(int64_t nkeys, int64_t nrows);
 hipError_t launch_b2_key_grads(const void* pp, const void* dsp, int64_t p_plane, int64_t ldu, int64_t nrows,
                                int64_t nkeys, const void* dacc_rows, int64_t dacc_plane, const void* qx_rows,
-                               int64_t qx_plane, float* dL, float* dkpe, hipStream_t st);
+                               int64_t qx_plane, float* dL, float* dkpe, float* part, hipStream_t st);
 // Products that contract over a chunk's keys run in at most B2_KSPLIT K
 // chunks, each to its own fp32 partial, summed in a fixed order afterwards.
 constexpr int B2_KSPLIT = 4;

@@ -289,7 +289,7 @@ laga_status laga_attn_bwd_noalloc(const laga_dims* dims, const void* q, const vo
  * LAGA_ERR_UNSUPPORTED).  workspace (16-byte aligned, owned by the caller,
  * contents irrelevant): laga_absorbed_bwd_workspace_bytes(dims) bytes give the
  * default chunks, about 8.7 KB per token and local head, 4.4 KB per token, and
- * up to 1 GiB of chunk buffers (3.5 GB at S = 16384, h = 16).  A smaller
+ * up to 1 GiB of chunk buffers (3.6 GB at S = 16384, h = 16).  A smaller
  * workspace, down to laga_absorbed_bwd_min_workspace_bytes(dims) (chunks of 32
  * tokens), runs with the largest chunks that fit it: less memory, more
  * launches; below the minimum the call returns LAGA_ERR_WORKSPACE.  Results of

@@ -198,7 +198,7 @@ def test_absorbed_backward_workspace_sizes():
         d = _lib.make_dims(1, S, 128, 8, 0, 512, 128, 64, 128, _lib.LAGA_BF16, 0)
         return _lib.absorbed_bwd_workspace_bytes(d), _lib.absorbed_bwd_min_workspace_bytes(d)
     full, least = sizes(16384)
-    assert 3.3e9 < full < 3.6e9
+    assert 3.3e9 < full < 3.8e9
     assert full - least > 0.9e9
     m1, m2, m3 = (sizes(S)[1] for S in (4096, 8192, 12288))
     assert abs((m3 - m2) - (m2 - m1)) < 1e6
