@@ -32,6 +32,15 @@
 // pass and the 4 rows of a transposing read fall on different banks, and with
 // 128-byte aligned rows every read is a per-lane base XOR a constant plus an
 // immediate offset.
+//
+// Backward (launch_absorbed_bwd): B2's own steps in reverse, every product
+// on bf16 hi + lo planes (three MFMA terms, fp32 accumulation) so that dW_kv_b
+// and dgamma meet the same bars as LAGA's backward.  Query rows go in chunks
+// (tokens s0 .. s1 of one sequence, all heads): S and dP = d_acc . L over the
+// chunk's keys u < s1 are materialised in fp32, the rows' lse and delta are
+// recomputed from them, P and c.dS are written as planes, and the products
+// over keys (acc, d_q_abs || dq_rope) and over rows (dL || dk_pe) consume
+// them.  After the chunks: dq_nope, dW^k, dW^v and the norm's backward.
 #include <algorithm>
 
 #include "attn_common.hpp"
@@ -318,8 +327,8 @@ __device__ __forceinline__ void split8(const float* x, u16x8& hi, u16x8& lo) {
 // Row statistics of one chunk from its scores S and dP = d_acc . L (fp32,
 // row pitch ldu), over the row's keys u <= its token: lse = ln sum_u exp(S c)
 // and delta = sum_u P dP (= sum_j dO o for this P).  One wavefront per row,
-// each lane an online (max, sum, weighted dP sum) over a strided set of keys,
-// merged across the wavefront.
+// each lane an online (max, sum, weighted dP sum) over its 4-key groups (four
+// 16-byte loads of S and of dP in flight), merged across the wavefront.
 __global__ __launch_bounds__(256) void b2_rowstat_kernel(const float* __restrict__ S, const float* __restrict__ dP,
                                                          int64_t ldu, int64_t nrows, int64_t nkeys, int64_t s0, int h,
                                                          float scale, float* __restrict__ lse,
