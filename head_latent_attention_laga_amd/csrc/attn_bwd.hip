@@ -30,8 +30,9 @@
 // dW_kv_b, dLatent and dgamma use K, V, P and dS as hi + lo pairs (q and dO
 // are exact in fp16): S and dP add the low planes of K and V as e4m3 products
 // against e4m3 copies of q_nope and dO, each query row scaled by its own power
-// of two (the row's E8M0 byte is the A operand's scale), and dK, dV take P and
-// dS as fp16 hi + lo.  The float32 instantiation uses fp32 MFMAs.
+// of two (the row's E8M0 byte is the A operand's scale), and dK_nope, dV take P
+// and dS as fp16 hi + lo (dk_pe the hi term of dS).  The float32 instantiation
+// uses fp32 MFMAs.
 #include "attn_bwd_common.hpp"
 
 namespace laga {
@@ -347,7 +348,10 @@ struct Dkdv {
       for (int i = 0; i < 4; ++i) dsv[4 * g + i] = pv[4 * g + i] * (dp[4 * g + i] - d4[i]);
     }
     split16(dsv, dh);
-    // dK^T[d, key] += q^T dS   (k = queries)
+    // dK^T[d, key] += q^T dS   (k = queries).  The rope rows (d >= DN) give
+    // dk_pe, which reaches no other gradient (not dLatent, dW_kv_b or dgamma,
+    // whose bars need dS as a hi + lo pair): they take the hi term of dS only,
+    // as dq does.
 #pragma unroll
     for (int stp = 0; stp < STEPS; ++stp) {
       F qa[NKT];
@@ -356,7 +360,10 @@ struct Dkdv {
 #pragma unroll
       for (int q = 0; q < NS; ++q)
 #pragma unroll
-        for (int n = 0; n < NKT; ++n) acc.dk[n] = M::mma(qa[n], *reinterpret_cast<F*>(dh[stp][q]), acc.dk[n]);
+        for (int n = 0; n < NKT; ++n) {
+          if (q > 0 && n * 32 >= DN) continue;
+          acc.dk[n] = M::mma(qa[n], *reinterpret_cast<F*>(dh[stp][q]), acc.dk[n]);
+        }
     }
   }
 
