@@ -35,6 +35,7 @@
 // fp16 rounds independently from pair to pair and averages out in O and in
 // the backward's delta = sum dO o.
 // The float32 instantiation uses fp32 MFMAs throughout.
+#include <algorithm>
 #include "attn_common.hpp"
 #include "launch.hpp"
 
@@ -535,9 +536,16 @@ struct Fwd {
   }
 
   // Query tile qt of (b, head) against the images at img (that head's block 0),
-  // NBUF image buffers at lds.
+  // NBUF image buffers at lds.  part 0: every key block, o and lse written.
+  // part 1 / 2: the key blocks before / from split_block(), and the
+  // unnormalised partial (O, running max, sum; log2 units) written to `partial`
+  // ([BM rows][PART_ROW] floats) for fused_merge_kernel.
+  static constexpr int PART_ROW = DV + 4;  // 16-byte aligned rows: O, then the running max and sum
+  __device__ static int split_block(int64_t q0, int nkb) { return blocks_for_all(q0, nkb) / 2; }
+
   template <int NBUF>
-  __device__ static void run_images(const FwdArgs& a, const char* img, int b, int head, int qt, char* lds) {
+  __device__ static void run_images(const FwdArgs& a, const char* img, int b, int head, int qt, char* lds,
+                                    int part = 0, float* partial = nullptr) {
     static_assert(!LO8, "images hold single-plane K and V");
     static_assert(NBUF == 2 || NBUF == 3, "double or triple buffering");
     const int lane = threadIdx.x % kWave;
@@ -549,24 +557,43 @@ struct Fwd {
     int64_t kend = q0 + BM;
     if (kend > a.S) kend = a.S;
     const int nkb = static_cast<int>((kend + BN - 1) / BN);
+    const int kmid = split_block(q0, nkb);
+    const int kb0 = part == 2 ? kmid : 0, kb1 = part == 1 ? kmid : nkb;  // this task's key blocks
+    const int nall = blocks_for_all(q0, nkb) < kb1 ? blocks_for_all(q0, nkb) : kb1;
     State st_;
     begin(a, b, head, tq, qvalid, st_);  // q loads first: the block waits below count only image copies after them
 #pragma unroll
     for (int k = 0; k < NBUF - 1; ++k)
-      if (k < nkb) issue_image(img + static_cast<int64_t>(k) * BUF_BYTES, lds + k * BUF_BYTES, wv);
-    const int nall = blocks_for_all(q0, nkb);
-    int kb = 0;
-    // Unrolled by NBUF so that each step names its buffers as constant offsets.
+      if (kb0 + k < kb1) issue_image(img + static_cast<int64_t>(kb0 + k) * BUF_BYTES, lds + k * BUF_BYTES, wv);
+    int kb = kb0;
+    // Unrolled by NBUF so that each step names its buffers as constant offsets
+    // (block kb0 + j + NBUF i sits in buffer j).
     for (; kb + NBUF - 1 < nall; kb += NBUF) {
 #pragma unroll
       for (int j = 0; j < NBUF; ++j)
-        image_step<true, NBUF>(a, img, kb + j, nkb, wv, qw, tq, lds + j * BUF_BYTES,
+        image_step<true, NBUF>(a, img, kb + j, kb1, wv, qw, tq, lds + j * BUF_BYTES,
                                lds + ((j + NBUF - 1) % NBUF) * BUF_BYTES, st_);
     }
-    for (; kb < nkb; ++kb)
-      image_step<false, NBUF>(a, img, kb, nkb, wv, qw, tq, lds + (kb % NBUF) * BUF_BYTES,
-                              lds + ((kb + NBUF - 1) % NBUF) * BUF_BYTES, st_);
-    finish(a, b, head, tq, qvalid, st_);
+    for (; kb < kb1; ++kb)
+      image_step<false, NBUF>(a, img, kb, kb1, wv, qw, tq, lds + ((kb - kb0) % NBUF) * BUF_BYTES,
+                              lds + ((kb - kb0 + NBUF - 1) % NBUF) * BUF_BYTES, st_);
+    if (part == 0) {
+      finish(a, b, head, tq, qvalid, st_);
+      return;
+    }
+    if (!qvalid) return;
+    const int hf = lane / 32;
+    float* pr = partial + static_cast<int64_t>(wv * 32 + lane % 32) * PART_ROW;
+#pragma unroll
+    for (int n = 0; n < NO; ++n)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4*>(pr + n * 32 + 8 * g + 4 * hf) =
+            f32x4{st_.o[n][4 * g], st_.o[n][4 * g + 1], st_.o[n][4 * g + 2], st_.o[n][4 * g + 3]};
+    if (hf == 0) {
+      pr[DV] = st_.m_run;
+      pr[DV + 1] = st_.l_run;
+    }
   }
 };
 
@@ -622,6 +649,8 @@ hipError_t fwd_t(const Shape& s, const void* q, const void* kn, const void* kp, 
 // head's producers and consumers share an L2.
 typedef Fwd<bf16_t, MmaF16, MmaBf16, 1, 128, 64, 128, 8> FusedAttn;
 constexpr int kFusedKeys = 256;          // keys per producer task
+constexpr int kMaxTasks = 64;            // consumer tasks per head when query tiles are split
+constexpr int kCUs = 256;                // compute units the split rule balances over (MI355X)
 constexpr unsigned kSpinLimit = 1u << 20;  // polls (about 0.2 us apart) before a consumer gives up
 
 struct FusedArgs {
@@ -634,6 +663,12 @@ struct FusedArgs {
   int* err;            // set when a consumer gave up waiting
   int* done;           // [B*h] producer tasks finished per head
   int n_kt, nkb_img, parts, hpp, prod_pp;
+  // Consumer tasks per head in ticket order when some query tiles are split
+  // (n_task > 0): qt << 2 | part (0 whole, 1 / 2 the halves of its key blocks);
+  // with n_task == 0 tile n_qt - 1 - rank, whole.  Split tiles are qt >= q_split.
+  int n_task, q_split;
+  int task[kMaxTasks];
+  float* part;  // [(qt - q_split) * B * h + bh][2][BM][PART_ROW] partials of split tiles
 };
 
 template <int BKP, int NSTP>
@@ -809,7 +844,9 @@ __global__ __launch_bounds__(8 * kWave, 2) void attn_fwd_fused_kernel(FusedArgs 
     return;
   }
   const int c = t - a.prod_pp;
-  const int bh = bh0 + c % a.hpp, qt = a.f.n_qt - 1 - c / a.hpp;
+  const int bh = bh0 + c % a.hpp, rank = c / a.hpp;
+  const int e = a.n_task > 0 ? a.task[rank] : (a.f.n_qt - 1 - rank) << 2;
+  const int qt = e >> 2, half = e & 3;
   const int b = bh / a.f.h, head = bh % a.f.h;
   if (threadIdx.x == 0) {
     int ok = 1;
@@ -828,7 +865,15 @@ __global__ __launch_bounds__(8 * kWave, 2) void attn_fwd_fused_kernel(FusedArgs 
     sh[1] = ok;
   }
   __syncthreads();
+  float* partial = half == 0 ? nullptr
+                             : a.part + ((static_cast<int64_t>(qt - a.q_split) * a.f.B * a.f.h + bh) * 2 + (half - 1)) *
+                                            FusedAttn::BM * FusedAttn::PART_ROW;
   if (!sh[1]) {  // never expected: mark the tile's outputs instead of hanging
+    if (half != 0) {  // a split tile: its partials are merged into o and lse, so poison them
+      for (int i = threadIdx.x; i < FusedAttn::BM * FusedAttn::PART_ROW; i += 8 * kWave)
+        partial[i] = __builtin_nanf("");
+      return;
+    }
     const int64_t q0 = static_cast<int64_t>(qt) * FusedAttn::BM;
     for (int i = threadIdx.x; i < FusedAttn::BM * 128; i += 8 * kWave) {
       const int64_t tq = q0 + i / 128;
@@ -839,7 +884,36 @@ __global__ __launch_bounds__(8 * kWave, 2) void attn_fwd_fused_kernel(FusedArgs 
     return;
   }
   FusedAttn::run_images<kImageBufs>(a.f, a.img + static_cast<int64_t>(bh) * a.nkb_img * FusedAttn::BUF_BYTES, b, head, qt,
-                        lds);
+                                    lds, half, partial);
+}
+
+// o and lse of the split query tiles from their two partials: with m = max(m1,
+// m2) and a_i = 2^(m_i - m), o = (a1 O1 + a2 O2) / (a1 l1 + a2 l2) and lse =
+// (m + log2(a1 l1 + a2 l2)) ln 2.  One thread per (tile, head, row, 4 columns).
+__global__ __launch_bounds__(256) void fused_merge_kernel(const float* __restrict__ part, float* __restrict__ o,
+                                                          float* __restrict__ lse, int q_split, int n_split, int B,
+                                                          int h, int64_t S) {
+  constexpr int BM = FusedAttn::BM, PR = FusedAttn::PART_ROW, DV = 128;
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t per_tile = static_cast<int64_t>(BM) * (DV / 4);
+  if (j >= static_cast<int64_t>(n_split) * B * h * per_tile) return;
+  const int64_t tb = j / per_tile;  // (split tile, bh)
+  const int r = static_cast<int>((j % per_tile) / (DV / 4)), c4 = static_cast<int>(j % (DV / 4)) * 4;
+  const int bh = static_cast<int>(tb % (B * h)), qt = q_split + static_cast<int>(tb / (B * h));
+  const int64_t tq = static_cast<int64_t>(qt) * BM + r;
+  if (tq >= S) return;
+  const float* p1 = part + (tb * 2) * BM * PR + static_cast<int64_t>(r) * PR;
+  const float* p2 = p1 + static_cast<int64_t>(BM) * PR;
+  const float m1 = p1[DV], l1 = p1[DV + 1], m2 = p2[DV], l2 = p2[DV + 1];
+  const float m = fmaxf(m1, m2);
+  const float a1 = __builtin_amdgcn_exp2f(m1 - m), a2 = __builtin_amdgcn_exp2f(m2 - m);
+  const float l = a1 * l1 + a2 * l2, inv = 1.0f / l;
+  const f32x4 x = *reinterpret_cast<const f32x4*>(p1 + c4), y = *reinterpret_cast<const f32x4*>(p2 + c4);
+  const int b = bh / h, head = bh % h;
+  *reinterpret_cast<f32x4*>(o + ((b * S + tq) * h + head) * DV + c4) =
+      f32x4{(a1 * x[0] + a2 * y[0]) * inv, (a1 * x[1] + a2 * y[1]) * inv, (a1 * x[2] + a2 * y[2]) * inv,
+            (a1 * x[3] + a2 * y[3]) * inv};
+  if (c4 == 0) lse[(static_cast<int64_t>(b) * h + head) * S + tq] = (m + log2f(l)) * 0.69314718055994531f;
 }
 
 // The fused forward's prep: workgroups [0, nb_norm) normalise 4 latent rows
@@ -886,9 +960,58 @@ __global__ __launch_bounds__(256) void fused_prep_kernel(const bf16_t* __restric
 
 // Workspace of the fused forward: counters | L16 | W16 | images.
 struct FusedLayout {
-  size_t cnt, l16, w16, img, total;
+  size_t cnt, l16, w16, img, part, total;
   int n_cnt, n_kt, nkb_img;
+  int n_qt, q_split, n_task;  // q_split == n_qt: no tile is split
+  int task[kMaxTasks];
 };
+
+// Which query tiles run as two tasks, and the consumer task order.  Tile qt
+// has nkb(qt) key blocks; with the work spread evenly each CU gets W / kCUs
+// blocks (W: all tiles of all heads), and a tile larger than that would set
+// the time alone.  Such tiles (qt >= 1, so both halves have blocks) are split
+// at split_block() into two tasks, when the per-head task list fits kMaxTasks
+// (short sequences only: at S = 16384 with 16 heads, or S = 4096 with 128, no
+// tile is split).  Tasks run heaviest first.
+void fused_tasks(const Shape& s, FusedLayout& L) {
+  constexpr int BM = FusedAttn::BM;
+  L.n_qt = static_cast<int>((s.S + BM - 1) / BM);
+  L.q_split = L.n_qt;
+  L.n_task = 0;
+  if (2 * L.n_qt > kMaxTasks) return;
+  auto nkb = [&](int qt) {
+    const int64_t kend = std::min<int64_t>(static_cast<int64_t>(qt + 1) * BM, s.S);
+    return static_cast<int>((kend + BN - 1) / BN);
+  };
+  auto nall = [&](int qt) { return std::min(static_cast<int>((static_cast<int64_t>(qt) * BM + 31) / BN) + 1, nkb(qt)); };
+  int64_t W = 0;
+  for (int qt = 0; qt < L.n_qt; ++qt) W += nkb(qt);
+  W *= s.B * s.h;
+  const double avg = static_cast<double>(W) / kCUs;
+  int q = L.n_qt;
+  while (q > 1 && nkb(q - 1) > avg) --q;  // nkb grows with qt
+  if (q == L.n_qt) return;
+  L.q_split = q;
+  struct T { int w, qt, part; };
+  T t[kMaxTasks];
+  int n = 0;
+  for (int qt = 0; qt < L.n_qt; ++qt) {
+    if (qt < q) {
+      t[n++] = {nkb(qt), qt, 0};
+    } else {
+      const int mid = nall(qt) / 2;
+      t[n++] = {mid, qt, 1};
+      t[n++] = {nkb(qt) - mid, qt, 2};
+    }
+  }
+  std::sort(t, t + n, [](const T& x, const T& y) {
+    return x.w != y.w ? x.w > y.w : (x.qt != y.qt ? x.qt > y.qt : x.part < y.part);
+  });
+  for (int i = 0; i < n; ++i) L.task[i] = t[i].qt << 2 | t[i].part;
+  L.n_task = n;
+}
+
+FusedLayout fused_layout(const Shape& s);
 
 size_t r256(size_t b) { return (b + 255) & ~size_t(255); }
 
@@ -906,6 +1029,9 @@ FusedLayout fused_layout(const Shape& s) {
   off += r256(static_cast<size_t>(s.h) * 256 * 512 * 2);
   L.img = off;
   off += static_cast<size_t>(s.B) * s.h * L.nkb_img * FusedAttn::BUF_BYTES;
+  fused_tasks(s, L);
+  L.part = off;
+  off += static_cast<size_t>(L.n_qt - L.q_split) * s.B * s.h * 2 * FusedAttn::BM * FusedAttn::PART_ROW * 4;
   L.total = off;
   return L;
 }
@@ -969,9 +1095,20 @@ hipError_t launch_attn_fwd_fused(const Shape& s, const void* q, const void* late
   a.parts = nbh % 8 == 0 ? 8 : 1;
   a.hpp = nbh / a.parts;
   a.prod_pp = a.hpp * a.n_kt;
-  const int64_t grid = static_cast<int64_t>(a.parts) * a.hpp * (a.n_kt + a.f.n_qt);
+  a.n_task = L.n_task;
+  a.q_split = L.q_split;
+  for (int i = 0; i < kMaxTasks; ++i) a.task[i] = i < L.n_task ? L.task[i] : 0;
+  a.part = reinterpret_cast<float*>(ws + L.part);
+  const int tasks = L.n_task > 0 ? L.n_task : a.f.n_qt;  // consumer tasks per head
+  const int64_t grid = static_cast<int64_t>(a.parts) * a.hpp * (a.n_kt + tasks);
   if (grid >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(attn_fwd_fused_kernel, dim3(static_cast<unsigned>(grid)), dim3(8 * kWave), 0, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess || L.n_task == 0) return e;
+  const int n_split = L.n_qt - L.q_split;
+  const int64_t nthr = static_cast<int64_t>(n_split) * s.B * s.h * FusedAttn::BM * 32;
+  hipLaunchKernelGGL(fused_merge_kernel, dim3(static_cast<unsigned>((nthr + 255) / 256)), dim3(256), 0, st, a.part, o,
+                     lse, L.q_split, n_split, static_cast<int>(s.B), s.h, s.S);
   return hipGetLastError();
 }
 

@@ -159,12 +159,15 @@ def test_fused_forward_checks_on_the_host(lib):
     assert lib.laga_attn_fwd_fused(ctypes.byref(d), *args, MISALIGNED, ctypes.c_size_t(need), None) == ALIGN
 
 
-def test_fused_workspace_is_linear_in_the_sequence(lib):
+def test_fused_workspace_is_linear_in_the_sequence_beyond_split_tiles(lib):
     def ws(S, **kw):
         return lib.laga_attn_fwd_fused_workspace_bytes(ctypes.byref(v3(S=S, precision=_lib.LAGA_OPERANDS_FP16, **kw)))
-    a, b, c = ws(4096), ws(8192), ws(12288)
+    a, b, c = ws(8192), ws(12288), ws(16384)
     assert b - a == c - b > 0
-    assert ws(16384, n_h=128, sp_size=8) < 200e6
+    assert c < 200e6
+    # S=4096: half of its 16 query tiles run as two tasks each; their partials
+    # (2 x 256 rows x 132 floats per tile and head) come on top of the linear part.
+    assert ws(4096) - (a - (b - a)) == 8 * 16 * 2 * 256 * 132 * 4
 
 
 def test_absorbed_backward_checks_on_the_host(lib):

@@ -37,7 +37,8 @@ def _oracle_full(inp, d):
 
 @pytest.mark.parametrize("B,S,n_h,P,r", [
     (1, 300, 16, 8, 3), (2, 130, 64, 8, 7), (1, 1, 16, 8, 0), (1, 64, 128, 16, 2), (1, 1000, 16, 8, 2),
-    (1, 256, 16, 8, 1), (1, 257, 16, 8, 4), (3, 77, 24, 8, 1), (1, 513, 40, 8, 5), (2, 600, 128, 16, 9)])
+    (1, 256, 16, 8, 1), (1, 257, 16, 8, 4), (3, 77, 24, 8, 1), (1, 513, 40, 8, 5), (2, 600, 128, 16, 9),
+    (2, 2048, 16, 8, 6)])
 def test_fused_full_compare(B, S, n_h, P, r):
     d = _dims(B, S, n_h, P, r)
     announce(f"fused forward full compare dims={d}")
