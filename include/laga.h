@@ -157,8 +157,13 @@ laga_status laga_attn_fwd(const laga_dims* dims, const void* q, const void* k_no
  * the caller, whose contents need no initialisation and are overwritten:
  * 672 bytes per token and local head (K, V and rope rows, padded as the
  * attention's LDS tiles) with S rounded up to 256, 1 KB per token and 256 KB
- * per local head (197 MB at S = 16384, h = 16).  Two launches on `stream`; calls that share a
- * workspace must not overlap in time.
+ * per local head (197 MB at S = 16384, h = 16), plus 270 KB per split
+ * 256-query tile and local head (35 MB at S = 4096, h = 16): a query tile with
+ * more key blocks than the even share of all tiles' work per compute unit
+ * runs as two tasks over the halves of its keys, merged afterwards (short
+ * sequences only).  Two launches on
+ * `stream` (three when tiles are split); calls that share a workspace must not
+ * overlap in time.
  */
 size_t laga_attn_fwd_fused_workspace_bytes(const laga_dims* dims);
 laga_status laga_attn_fwd_fused(const laga_dims* dims, const void* q, const void* latent,
