@@ -164,8 +164,12 @@ FWD_ONLY_GRIDS = {
 }
 
 
+# $REPO: the repository root (absolute: the profiler runs from /tmp); $OUT: the directory
+# whose rocprofv3 output the summaries are made from (`--summarize-profiles $OUT`).
 PROFILE_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 {opts} --output-format csv "
-               "-d $GRAFT_REPO_ROOT/gpurun_out/{d} -o {o} -- python3 $GRAFT_REPO_ROOT/bench.py {args}")
+               "-d $OUT/{d} -o {o} -- python3 $REPO/bench.py {args}")
+PROFILE_VARS = ("`$REPO` is the repository root and `$OUT` the directory these summaries were made from "
+                "(`python bench.py --summarize-profiles $OUT`).")
 PMC_ARGS = "--steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy"
 KT_ARGS = "--steps 10 --warmup 5 --no-cpu-baseline"
 COUNTER_PASSES = {
@@ -244,7 +248,7 @@ def summarize_profiles(out_root: str):
     prun = json.loads(line[-1]) if line else None
     L = [f"# Kernel trace: LAGA training step, fp16-operand forward (unfused and fused) and absorbed-form (B2) "
          f"forward and backward, {title}", "", "Command (on the GPU box):", "", "```",
-         PROFILE_CMD.format(opts="--kernel-trace --stats", d="kt", o="kt", args=KT_ARGS), "```", "",
+         PROFILE_CMD.format(opts="--kernel-trace --stats", d="kt", o="kt", args=KT_ARGS), "```", "", PROFILE_VARS, "",
          "Per launch, from the trace (`kt_kernel_trace.csv`), in us. For the step's kernels, 'timed' is the mean "
          "over the launches inside bench.py's timed region and 'bench' the HIP-event mean that the same run "
          "printed in its JSON line.", "",
@@ -280,7 +284,7 @@ def summarize_profiles(out_root: str):
     L = [f"# HBM traffic per kernel launch: {title}", "",
          "Two counter passes (FETCH_SIZE, then WRITE_SIZE), each on its own run:", "", "```",
          PROFILE_CMD.format(opts="--pmc FETCH_SIZE", d="pmc_fetch", o="pmc", args=PMC_ARGS),
-         PROFILE_CMD.format(opts="--pmc WRITE_SIZE", d="pmc_write", o="pmc", args=PMC_ARGS), "```", "",
+         PROFILE_CMD.format(opts="--pmc WRITE_SIZE", d="pmc_write", o="pmc", args=PMC_ARGS), "```", "", PROFILE_VARS, "",
          f"Calibration: `--calibrate-copy` first runs three 256 MiB device copies (`__amd_rocclr_copyBuffer`); per "
          f"copy FETCH_SIZE read {copy_kib / sf:.1f} KiB and WRITE_SIZE {copy_kib / sw:.1f} KiB against {copy_kib} KiB "
          f"moved each way, so the scale factors are fetch x{sf:.4f}, write x{sw:.4f}. GB/s divides the scaled bytes "
@@ -311,7 +315,7 @@ def summarize_profiles(out_root: str):
          "Two passes, each on its own run:", "", "```"]
     for d, cs in COUNTER_PASSES.items():
         L.append(PROFILE_CMD.format(opts=f"--pmc {cs}", d=d, o="pmc", args=PMC_ARGS))
-    L += ["```", "",
+    L += ["```", "", PROFILE_VARS, "",
           "Columns (means over the launches): MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 "
           "SIMDs), the share of SIMD cycles the matrix cores were busy; clock = GRBM_GUI_ACTIVE / 8 / duration; "
           "VALU, LDS and any-instruction active and the wait shares are per wave cycle (SQ_ACTIVE_INST_*, "
