@@ -129,6 +129,7 @@ PROFILE_KERNELS = {
     "attn_fwd_fp16": ([["attn_fwd_kernel<", "MmaBf16, 1, 128"]], _N + "attn_fwd.hip"),
     "fused_prep": ([["fused_prep_kernel"]], _N + "attn_fwd.hip"),
     "attn_fwd_fused": ([["attn_fwd_fused_kernel"]], _N + "attn_fwd.hip"),
+    "fused_merge": ([["fused_merge_kernel"]], _N + "attn_fwd.hip"),
     "bwd_delta": ([["bwd_prep_kernel"]], _N + "attn_bwd.hip"),
     "do_convert": ([["do_convert_kernel"]], _N + "attn_bwd.hip"),
     "attn_bwd_dkdv": ([["dkdv_kernel<"], ["dkdv_kernelIDF16_NS_6MmaF16ELi2"]], _N + "attn_bwd.hip"),
@@ -158,7 +159,7 @@ PROFILE_KERNELS = {
 FWD_ONLY_GRIDS = {
     "kv_up_fp16": {524288: "S=16384 h=16", 131072: "S=4096 h=16", 1048576: "S=4096 h=128"},
     "attn_fwd_fp16": {524288: "S=16384 h=16", 131072: "S=4096 h=16", 1048576: "S=4096 h=128"},
-    "attn_fwd_fused": {1048576: "S=16384 h=16", 262144: "S=4096 h=16", 2097152: "S=4096 h=128"},
+    "attn_fwd_fused": {1048576: "S=16384 h=16", 327680: "S=4096 h=16", 2097152: "S=4096 h=128"},
     "fused_prep": {2359552: "S=16384 h=16", 524544: "S=4096 h=16", 1310976: "S=4096 h=128"},
     "rmsnorm_fwd": {1048576: "S=16384", 262144: "S=4096"},
 }
