@@ -521,16 +521,49 @@ struct Fwd {
     else wait_vmcnt<IMG_HI - 1>();
   }
 
+  // Readiness of the key tiles (kTileBlocks blocks each) when images are
+  // produced by other workgroups: flags[kt] is set (release) once tile kt's
+  // images are written.  Thread 0 checks a tile before the barrier of the step
+  // that copies its first block; the flag's load is issued one step earlier,
+  // so the step's wait for its copies also covers it and a ready tile costs no
+  // stall.  Waiting is bounded: past kSpinLimit polls *ok is cleared and the
+  // error word set, and the caller writes NaN instead of results.
+  struct Ready { const int* flags; int* err; int* ok; };
+  static constexpr int kTileBlocks = 4;                // 256 keys per produced tile
+  static constexpr unsigned kSpinLimit = 1u << 20;     // polls (about 0.2 us apart)
+  __device__ static int peek_tile(const Ready& rd, int blk, int nkb) {
+    return blk < nkb && blk % kTileBlocks == 0
+               ? __hip_atomic_load(rd.flags + blk / kTileBlocks, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+               : 1;
+  }
+  __device__ static void tile_ready(const Ready& rd, int kt, int fv) {
+    unsigned spins = 0;
+    while (fv == 0) {
+      if (++spins > kSpinLimit) {
+        *rd.ok = 0;
+        __hip_atomic_store(rd.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
+      fv = __hip_atomic_load(rd.flags + kt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the tile's images are visible to the copies below
+  }
+
   // One key block with NBUF buffers: block kb is in `cur`; block kb + NBUF - 1
   // goes into `ahead` (the buffer of block kb - 1, free once every wavefront
   // has passed this step's barrier).
   template <bool ALL, int NBUF>
   __device__ static void image_step(const FwdArgs& a, const char* img, int kb, int nkb, int wv, int64_t qw,
-                                    int64_t tq, char* cur, char* ahead, State& st_) {
+                                    int64_t tq, char* cur, char* ahead, State& st_, const Ready& rd, int& fv) {
     if constexpr (NBUF == 2) wait_vmcnt<0>();
     else wait_image(kb + 1 < nkb, wv);
+    const int nb = kb + NBUF - 1;  // the block this step copies
+    if (rd.flags != nullptr && threadIdx.x == 0 && nb < nkb && nb % kTileBlocks == 0)
+      tile_ready(rd, nb / kTileBlocks, fv);
     __syncthreads();
-    if (kb + NBUF - 1 < nkb) issue_image(img + static_cast<int64_t>(kb + NBUF - 1) * BUF_BYTES, ahead, wv);
+    if (nb < nkb) issue_image(img + static_cast<int64_t>(nb) * BUF_BYTES, ahead, wv);
+    if (rd.flags != nullptr && threadIdx.x == 0) fv = peek_tile(rd, nb + 1, nkb);
     const int64_t key0 = static_cast<int64_t>(kb) * BN;
     if (ALL || key0 <= qw + 31) compute_block(a, cur, key0, qw, tq, st_);
   }
@@ -544,8 +577,8 @@ struct Fwd {
   __device__ static int split_block(int64_t q0, int nkb) { return blocks_for_all(q0, nkb) / 2; }
 
   template <int NBUF>
-  __device__ static void run_images(const FwdArgs& a, const char* img, int b, int head, int qt, char* lds,
-                                    int part = 0, float* partial = nullptr) {
+  __device__ static bool run_images(const FwdArgs& a, const char* img, int b, int head, int qt, char* lds,
+                                    int part, float* partial, const Ready& rd) {
     static_assert(!LO8, "images hold single-plane K and V");
     static_assert(NBUF == 2 || NBUF == 3, "double or triple buffering");
     const int lane = threadIdx.x % kWave;
@@ -560,11 +593,16 @@ struct Fwd {
     const int kmid = split_block(q0, nkb);
     const int kb0 = part == 2 ? kmid : 0, kb1 = part == 1 ? kmid : nkb;  // this task's key blocks
     const int nall = blocks_for_all(q0, nkb) < kb1 ? blocks_for_all(q0, nkb) : kb1;
+    static_assert(NBUF == 2, "the tile flags are read one step ahead, under the step's vmcnt(0)");
     State st_;
     begin(a, b, head, tq, qvalid, st_);  // q loads first: the block waits below count only image copies after them
-#pragma unroll
-    for (int k = 0; k < NBUF - 1; ++k)
-      if (kb0 + k < kb1) issue_image(img + static_cast<int64_t>(kb0 + k) * BUF_BYTES, lds + k * BUF_BYTES, wv);
+    int fv = 1;
+    if (rd.flags != nullptr && threadIdx.x == 0)
+      tile_ready(rd, kb0 / kTileBlocks,
+                 __hip_atomic_load(rd.flags + kb0 / kTileBlocks, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    __syncthreads();
+    issue_image(img + static_cast<int64_t>(kb0) * BUF_BYTES, lds, wv);
+    if (rd.flags != nullptr && threadIdx.x == 0) fv = peek_tile(rd, kb0 + 1, kb1);
     int kb = kb0;
     // Unrolled by NBUF so that each step names its buffers as constant offsets
     // (block kb0 + j + NBUF i sits in buffer j).
@@ -572,16 +610,17 @@ struct Fwd {
 #pragma unroll
       for (int j = 0; j < NBUF; ++j)
         image_step<true, NBUF>(a, img, kb + j, kb1, wv, qw, tq, lds + j * BUF_BYTES,
-                               lds + ((j + NBUF - 1) % NBUF) * BUF_BYTES, st_);
+                               lds + ((j + NBUF - 1) % NBUF) * BUF_BYTES, st_, rd, fv);
     }
     for (; kb < kb1; ++kb)
       image_step<false, NBUF>(a, img, kb, kb1, wv, qw, tq, lds + ((kb - kb0) % NBUF) * BUF_BYTES,
-                              lds + ((kb - kb0 + NBUF - 1) % NBUF) * BUF_BYTES, st_);
+                              lds + ((kb - kb0 + NBUF - 1) % NBUF) * BUF_BYTES, st_, rd, fv);
+    if (rd.flags != nullptr && !*rd.ok) return false;  // set before the last step's barrier
     if (part == 0) {
       finish(a, b, head, tq, qvalid, st_);
-      return;
+      return true;
     }
-    if (!qvalid) return;
+    if (!qvalid) return true;
     const int hf = lane / 32;
     float* pr = partial + static_cast<int64_t>(wv * 32 + lane % 32) * PART_ROW;
 #pragma unroll
@@ -594,6 +633,7 @@ struct Fwd {
       pr[DV] = st_.m_run;
       pr[DV + 1] = st_.l_run;
     }
+    return true;
   }
 };
 
@@ -651,7 +691,6 @@ typedef Fwd<bf16_t, MmaF16, MmaBf16, 1, 128, 64, 128, 8> FusedAttn;
 constexpr int kFusedKeys = 256;          // keys per producer task
 constexpr int kMaxTasks = 64;            // consumer tasks per head when query tiles are split
 constexpr int kCUs = 256;                // compute units the split rule balances over (MI355X)
-constexpr unsigned kSpinLimit = 1u << 20;  // polls (about 0.2 us apart) before a consumer gives up
 
 struct FusedArgs {
   FwdArgs f;  // q, o, lse, sizes and the score scale of the attention
@@ -661,7 +700,7 @@ struct FusedArgs {
   char* img;           // [B*h][nkb_img][BUF_BYTES] key-block images
   int* tickets;        // [8]
   int* err;            // set when a consumer gave up waiting
-  int* done;           // [B*h] producer tasks finished per head
+  int* done;           // [B*h][n_kt] set when that key tile's images are written
   int n_kt, nkb_img, parts, hpp, prod_pp;
   // Consumer tasks per head in ticket order when some query tiles are split
   // (n_task > 0): qt << 2 | part (0 whole, 1 / 2 the halves of its key blocks);
@@ -809,11 +848,12 @@ struct KvProducerT {
         *reinterpret_cast<u32x4*>(gdst + c * 16) = *reinterpret_cast<const u32x4*>(lds + c * 16);
       __syncthreads();  // the LDS images are free again
     }
-    // Every store of this task is complete before the head's count goes up.
+    // Every store of this task is complete before the tile's flag is set.
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     __syncthreads();
     if (threadIdx.x == 0)
-      __hip_atomic_fetch_add(a.done + b * a.f.h + head, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.done + (static_cast<int64_t>(b) * a.f.h + head) * a.n_kt + kt, 1, __ATOMIC_RELEASE,
+                         __HIP_MEMORY_SCOPE_AGENT);
   }
 };
 
@@ -830,8 +870,10 @@ __global__ __launch_bounds__(8 * kWave, 2) void attn_fwd_fused_kernel(FusedArgs 
   __shared__ __attribute__((aligned(1024))) char lds[kFusedLds + 16];
   int* sh = reinterpret_cast<int*>(lds + kFusedLds);
   const int part = a.parts == 8 ? static_cast<int>(blockIdx.x % 8) : 0;
-  if (threadIdx.x == 0)
+  if (threadIdx.x == 0) {
     sh[0] = __hip_atomic_fetch_add(a.tickets + part, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh[1] = 1;  // cleared if a consumer gives up waiting for a key tile
+  }
   __syncthreads();
   const int t = __builtin_amdgcn_readfirstlane(sh[0]);
   const int bh0 = part * a.hpp;
@@ -848,43 +890,27 @@ __global__ __launch_bounds__(8 * kWave, 2) void attn_fwd_fused_kernel(FusedArgs 
   const int e = a.n_task > 0 ? a.task[rank] : (a.f.n_qt - 1 - rank) << 2;
   const int qt = e >> 2, half = e & 3;
   const int b = bh / a.f.h, head = bh % a.f.h;
-  if (threadIdx.x == 0) {
-    int ok = 1;
-    unsigned spins = 0;
-    // Relaxed polls, then one acquire fence: the caches are invalidated once,
-    // not on every poll.
-    while (__hip_atomic_load(a.done + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.n_kt) {
-      if (++spins > kSpinLimit) {
-        ok = 0;
-        __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(8);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    sh[1] = ok;
-  }
-  __syncthreads();
   float* partial = half == 0 ? nullptr
                              : a.part + ((static_cast<int64_t>(qt - a.q_split) * a.f.B * a.f.h + bh) * 2 + (half - 1)) *
                                             FusedAttn::BM * FusedAttn::PART_ROW;
-  if (!sh[1]) {  // never expected: mark the tile's outputs instead of hanging
-    if (half != 0) {  // a split tile: its partials are merged into o and lse, so poison them
-      for (int i = threadIdx.x; i < FusedAttn::BM * FusedAttn::PART_ROW; i += 8 * kWave)
-        partial[i] = __builtin_nanf("");
-      return;
-    }
-    const int64_t q0 = static_cast<int64_t>(qt) * FusedAttn::BM;
-    for (int i = threadIdx.x; i < FusedAttn::BM * 128; i += 8 * kWave) {
-      const int64_t tq = q0 + i / 128;
-      if (tq >= a.f.S) continue;
-      a.f.o[((b * a.f.S + tq) * a.f.h + head) * 128 + i % 128] = __builtin_nanf("");
-      if (i % 128 == 0) a.f.lse[(static_cast<int64_t>(b) * a.f.h + head) * a.f.S + tq] = __builtin_nanf("");
-    }
+  // Each key tile is waited for (its producer's flag) just before its first
+  // block is copied, so the attention starts once the first tile is written.
+  const FusedAttn::Ready rd{a.done + static_cast<int64_t>(bh) * a.n_kt, a.err, sh + 1};
+  if (FusedAttn::run_images<kImageBufs>(a.f, a.img + static_cast<int64_t>(bh) * a.nkb_img * FusedAttn::BUF_BYTES, b,
+                                        head, qt, lds, half, partial, rd))
+    return;
+  // Never expected (a producer did not finish): NaN outputs instead of a hang.
+  if (half != 0) {  // a split tile: its partials are merged into o and lse, so poison them
+    for (int i = threadIdx.x; i < FusedAttn::BM * FusedAttn::PART_ROW; i += 8 * kWave) partial[i] = __builtin_nanf("");
     return;
   }
-  FusedAttn::run_images<kImageBufs>(a.f, a.img + static_cast<int64_t>(bh) * a.nkb_img * FusedAttn::BUF_BYTES, b, head, qt,
-                                    lds, half, partial);
+  const int64_t q0 = static_cast<int64_t>(qt) * FusedAttn::BM;
+  for (int i = threadIdx.x; i < FusedAttn::BM * 128; i += 8 * kWave) {
+    const int64_t tq = q0 + i / 128;
+    if (tq >= a.f.S) continue;
+    a.f.o[((b * a.f.S + tq) * a.f.h + head) * 128 + i % 128] = __builtin_nanf("");
+    if (i % 128 == 0) a.f.lse[(static_cast<int64_t>(b) * a.f.h + head) * a.f.S + tq] = __builtin_nanf("");
+  }
 }
 
 // o and lse of the split query tiles from their two partials: with m = max(m1,
@@ -1019,7 +1045,7 @@ FusedLayout fused_layout(const Shape& s) {
   FusedLayout L;
   L.n_kt = static_cast<int>((s.S + kFusedKeys - 1) / kFusedKeys);
   L.nkb_img = L.n_kt * (kFusedKeys / BN);
-  L.n_cnt = 16 + static_cast<int>(s.B) * s.h;
+  L.n_cnt = 16 + static_cast<int>(s.B) * s.h * L.n_kt;
   size_t off = 0;
   L.cnt = off;
   off += r256(static_cast<size_t>(L.n_cnt) * 4);
