@@ -673,12 +673,13 @@ hipError_t fwd_t(const Shape& s, const void* q, const void* kn, const void* kp, 
 //  * producer (tickets first): K/V of 256 keys x one head, C^T = W_r[head] L^T
 //    (fp16 matrix-core products, both operands copied global -> LDS through a
 //    ring of three stages), written -- with the keys' k_pe rows -- as four
-//    images of the attention's LDS key-block buffer, then counted as done for
-//    that head (release at device scope);
+//    images of the attention's LDS key-block buffer, then flagged as written
+//    (one flag per head and key tile, release at device scope);
 //  * consumer (tickets after every producer ticket): the attention of one
-//    256-query tile of one head, heaviest tiles first, which waits until every
-//    producer of its head is done (acquire) and then streams the images with
-//    plain global -> LDS copies.
+//    256-query tile of one head (or of one half of its key blocks, for the
+//    heaviest tiles of short sequences), heaviest first, which streams the
+//    images with plain global -> LDS copies, waiting (acquire) for each key
+//    tile's flag before copying its first block.
 // A consumer waits only for producer tasks, and every producer ticket is
 // handed out before any consumer ticket, so each producer a consumer waits
 // for is already running on some CU, and producers wait for nothing: every
