@@ -48,7 +48,19 @@ struct Dkdv {
   static constexpr int BQ = 32, BK = 128;
   static constexpr bool TR = M::KPL == 8;  // 16-bit operands: separate transposed-read tiles
   // One q tile and one dO tile per block, read both as rows and transposed.
-  static constexpr int LQR = DQK + TilePad<M>::both, LOR = DV + TilePad<M>::both;
+  // 16-bit operands: row pitches of 16 (mod 32) dwords, the 16-byte chunks
+  // of row r XOR-swizzled by sw(r) = (r / 4) mod 4.  A 16-byte row read
+  // serves 16 rows at once: r mod 4 picks one of four 16-dword windows of the
+  // 64 banks and sw(r) one chunk inside it, so the 16 rows hit distinct
+  // banks; the four consecutive rows (one sw) of a transposing read fall in
+  // the four windows.  fp32: rows padded by 4 elements.
+  static constexpr int sw_pitch(int n) {
+    int d = n / 2;
+    while (d % 32 != 16) ++d;
+    return 2 * d;
+  }
+  static constexpr int LQR = TR ? sw_pitch(DQK) : DQK + 4, LOR = TR ? sw_pitch(DV) : DV + 4;
+  static_assert(!TR || (DQK % 32 == 0 && DV % 32 == 0), "whole groups of four chunks per row");
   static constexpr int QR_B = BQ * LQR * sizeof(E), OR_B = BQ * LOR * sizeof(E);
   // Split operands: the low terms S_lo = q8 K_lo^T and dP_lo = dO8 V_lo^T run
   // as e4m3 products; e4m3 q_nope / dO rows (16-byte row reads, 16-byte pad)
@@ -122,6 +134,9 @@ struct Dkdv {
     }
   }
 
+  // Offset in its row of row r's 16-byte chunk that starts at element el.
+  __device__ static int chunk_at(int r, int el) { return TR ? 8 * ((el / 8) ^ ((r / 4) % 4)) : el; }
+
   __device__ static void store(const Regs& R, char* buf) {
     E* Qr = reinterpret_cast<E*>(buf);
     E* Or = reinterpret_cast<E*>(buf + QR_B);
@@ -136,7 +151,7 @@ struct Dkdv {
       convert_chunk<E, InT>(R.q[i], tmp);
 #pragma unroll
       for (int j = 0; j < IPC; j += 16 / sizeof(E)) {
-        *reinterpret_cast<u32x4*>(Qr + r * LQR + col + j) = *reinterpret_cast<u32x4*>(tmp + j);
+        *reinterpret_cast<u32x4*>(Qr + r * LQR + chunk_at(r, col + j)) = *reinterpret_cast<u32x4*>(tmp + j);
       }
     }
 #pragma unroll
@@ -148,7 +163,7 @@ struct Dkdv {
       convert_chunk<E, InT>(R.o[i], tmp);
 #pragma unroll
       for (int j = 0; j < IPC; j += 16 / sizeof(E)) {
-        *reinterpret_cast<u32x4*>(Or + r * LOR + col + j) = *reinterpret_cast<u32x4*>(tmp + j);
+        *reinterpret_cast<u32x4*>(Or + r * LOR + chunk_at(r, col + j)) = *reinterpret_cast<u32x4*>(tmp + j);
       }
     }
     if (tid < BQ) {
@@ -181,7 +196,16 @@ struct Dkdv {
   // registers st*KPL .. (see acc_key_col).
   __device__ static F tr_frag(const E* T, int ld, int st, int n0) {
     if constexpr (TR) {
-      return tr_frag_acc(T, ld, st * 16, n0);
+      // tr_frag_acc's lanes on the swizzled rows: rows 16 st + 4 hf + s / 4
+      // (sw = hf) and the same + 8 (sw = hf ^ 2); n0 spans whole chunk groups.
+      const int lane = threadIdx.x % kWave;
+      const int g = lane / 16, s = lane % 16, hf = lane / 32;
+      const int row = st * 16 + 4 * hf + s / 4, blk = 2 * (g % 2) + (s % 4) / 2;
+      const s16x4 lo = ds_read_tr16(T + row * ld + n0 + 8 * (blk ^ hf) + 4 * (s % 2));
+      const s16x4 hi = ds_read_tr16(T + (row + 8) * ld + n0 + 8 * (blk ^ hf ^ 2) + 4 * (s % 2));
+      typedef short s16x8 __attribute__((ext_vector_type(8)));
+      const s16x8 r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      return __builtin_bit_cast(F, r);
     } else {
       const int lane = threadIdx.x % kWave;
       const int qi = 8 * (st / 4) + 4 * (lane / 32) + (st % 4);
@@ -245,8 +269,6 @@ struct Dkdv {
     // chains run one after the other so that the vector work on each result
     // (P from S, dS from dP) overlaps the next chain of products:
     //   S | dP + P | dV + dS | dK
-    const E* qrow = Qr + col * LQR + hf * M::KPL;
-    const E* orow = Or + col * LOR + hf * M::KPL;
     f32x16 sc, dp;
 #pragma unroll
     for (int r = 0; r < 16; ++r) { sc[r] = 0.f; dp[r] = 0.f; }
@@ -258,6 +280,12 @@ struct Dkdv {
       // per-query scale in the A operand (dP likewise).
       const int qs = reinterpret_cast<const int*>(st)[2 * BQ + col];
       const int os = reinterpret_cast<const int*>(st)[3 * BQ + col];
+      // Row reads of 16-byte chunk 2 i + hf (K step i): chunk x ^ 2 (i % 2) of
+      // group i / 2, x = hf ^ sw(col).
+      static_assert(TR && M::K == 16 && M::KPL == 8, "16-bit split operands");
+      const int x = hf ^ ((col / 4) % 4);
+      const E* qrow[2] = {Qr + col * LQR + 8 * x, Qr + col * LQR + 8 * (x ^ 2)};
+      const E* orow[2] = {Or + col * LOR + 8 * x, Or + col * LOR + 8 * (x ^ 2)};
       const char* q8row = buf + OFF_Q8 + col * (DN + P8) + 32 * hf;
       const char* o8row = buf + OFF_O8 + col * (DV + P8) + 32 * hf;
       constexpr int N8Q = 2 * KS8_N, N8O = 2 * KS8_V;
@@ -270,11 +298,11 @@ struct Dkdv {
           [&](int i) {
             if (i < N8Q) return *reinterpret_cast<const u32x4*>(q8row + 64 * (i / 2) + 16 * (i % 2));
             i -= N8Q;
-            if (i < KS_QK) return *reinterpret_cast<const u32x4*>(qrow + i * M::K);
+            if (i < KS_QK) return *reinterpret_cast<const u32x4*>(qrow[i % 2] + 32 * (i / 2));
             i -= KS_QK;
             if (i < N8O) return *reinterpret_cast<const u32x4*>(o8row + 64 * (i / 2) + 16 * (i % 2));
             i -= N8O;
-            return *reinterpret_cast<const u32x4*>(orow + i * M::K);
+            return *reinterpret_cast<const u32x4*>(orow[i % 2] + 32 * (i / 2));
           },
           [&](int i, const u32x4& f) {
             if (i < N8Q) {
@@ -297,6 +325,9 @@ struct Dkdv {
             dp = M::mma(__builtin_bit_cast(F, f), K.vf[i], dp);
           });
     } else {
+      static_assert(!TR, "16-bit operands are split");
+      const E* qrow = Qr + col * LQR + hf * M::KPL;
+      const E* orow = Or + col * LOR + hf * M::KPL;
 #pragma unroll
       for (int s = 0; s < KS_N; ++s) sc = M::mma(lds_frag<M>(qrow + s * M::K), K.kf[s], sc);
 #pragma unroll
@@ -532,10 +563,13 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(const float* __restrict__ 
 
 // bfloat16 inputs: delta as above, plus fp16 copies (exact) of the q and dO
 // rows and of the k_pe band, which the attention-backward kernels then stage
-// with plain 16-byte copies.  One wavefront per (b, t, i) row: the first DV/8
-// lanes take 8 elements of dO and o each, the next DQK/8 lanes 8 elements of
-// q, and on the i == 0 row the next DR/8 lanes 8 elements of k_pe.
-constexpr int kRowsPerWave = 4;  // rows of the delta / copy pass per wavefront
+// with plain 16-byte copies.  A wavefront takes the rows of kRowsPerWave
+// consecutive tokens (b, t) of one head i, so that their delta and scale
+// entries ([b, i, t] order) are consecutive and four lanes store each kind
+// at once.  Per row, the first DV/8 lanes take 8 elements of dO and o each,
+// the next DQK/8 lanes 8 elements of q, and on head 0 the next DR/8 lanes 8
+// elements of k_pe.
+constexpr int kRowsPerWave = 4;  // tokens of the delta / copy pass per wavefront
 
 template <int DN, int DR, int DV>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__ o, const bf16_t* __restrict__ q,
@@ -544,24 +578,25 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
                                                        half_t* __restrict__ q16, half_t* __restrict__ kpe16,
                                                        uint8_t* __restrict__ q8, uint8_t* __restrict__ do8,
                                                        int* __restrict__ qsc, int* __restrict__ osc,
-                                                       float* __restrict__ do_max, int64_t rows, int h, int64_t S) {
+                                                       float* __restrict__ do_max, int64_t T, int h, int64_t S) {
   constexpr int DQK = DN + DR, NO = DV / 8, NQ = DQK / 8, NR = DR / 8;
   static_assert(NO + NQ + NR <= kWave && DV % 8 == 0 && DQK % 8 == 0 && DR % 8 == 0, "one chunk per lane");
   static_assert(NO == 16 && DN / 8 == 16, "dO and q_nope fill one 16-lane group each");
   const int lane = threadIdx.x % kWave;
-  // kRowsPerWave consecutive rows (b, t, i) per wavefront, their loads issued
-  // together; rows past the end still reach the workgroup barrier below and
-  // touch no memory.
-  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave) * kRowsPerWave;
+  // Wavefront w: head i = w mod h, tokens bt0 .. bt0 + kRowsPerWave - 1; the
+  // loads of its rows are issued together.  Tokens past the end still reach
+  // the workgroup barrier below and touch no memory.
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
+  const int i = static_cast<int>(w % h);
+  const int64_t bt0 = (w / h) * kRowsPerWave;
   u16x8 raw[kRowsPerWave];
   f32x4 o0[kRowsPerWave], o1[kRowsPerWave];
 #pragma unroll
   for (int r = 0; r < kRowsPerWave; ++r) {
-    const int64_t row = row0 + r;
-    const int i = static_cast<int>(row % h);
+    const int64_t row = (bt0 + r) * h + i;
     raw[r] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
     o0[r] = o1[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (row >= rows) continue;
+    if (bt0 + r >= T) continue;
     if (lane < NO) {
       const int64_t at = row * DV + lane * 8;
       raw[r] = *reinterpret_cast<const u16x8*>(d_o + at);
@@ -570,16 +605,17 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
     } else if (lane < NO + NQ) {
       raw[r] = *reinterpret_cast<const u16x8*>(q + row * DQK + (lane - NO) * 8);
     } else if (lane < NO + NQ + NR && i == 0) {
-      raw[r] = *reinterpret_cast<const u16x8*>(k_pe + (row / h) * DR + (lane - NO - NQ) * 8);
+      raw[r] = *reinterpret_cast<const u16x8*>(k_pe + (bt0 + r) * DR + (lane - NO - NQ) * 8);
     }
   }
   float wave_amax = 0.f;  // largest |dO| of the wavefront's rows (dO lanes)
+  float dl[kRowsPerWave];  // delta of each row (every lane)
+  int esc[kRowsPerWave];   // E8M0 byte of each row: dO's in lanes 0..15, q_nope's in 16..31
 #pragma unroll
   for (int r = 0; r < kRowsPerWave; ++r) {
-    const int64_t row = row0 + r;
-    const bool live = row < rows;
-    const int64_t bt = (live ? row : 0) / h;
-    const int i = static_cast<int>((live ? row : 0) % h);
+    const int64_t bt = bt0 + r;
+    const bool live = bt < T;
+    const int64_t row = bt * h + i;
     float f[8];
     half8 hv;
 #pragma unroll
@@ -608,17 +644,30 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
     wave_amax = fmaxf(wave_amax, amax);
     const int sh = e4m3_row_shift(amax);
     const float sc = __uint_as_float(static_cast<uint32_t>(127 + sh) << 23);
-    const int64_t b = bt / S, t = bt % S;
-    const int64_t si = (b * h + i) * S + t;
     if (live && lane < NO + DN / 8) {
       uint8_t* dst = lane < NO ? do8 + row * DV + lane * 8 : q8 + row * DN + (lane - NO) * 8;
       *reinterpret_cast<uint2*>(dst) = make_uint2(pack_e4m3x4(f[0] * sc, f[1] * sc, f[2] * sc, f[3] * sc),
                                                   pack_e4m3x4(f[4] * sc, f[5] * sc, f[6] * sc, f[7] * sc));
-      if (lane == 0) osc[si] = 127 - sh;
-      if (lane == NO) qsc[si] = 127 - sh;
     }
-    acc = wave_sum(acc);
-    if (live && lane == 0) delta[si] = acc;
+    esc[r] = 127 - sh;
+    dl[r] = wave_sum(acc);
+  }
+  // Lane r (dO's group) stores row r's delta and dO scale, lane NO + r q_nope's scale.
+  const int r = lane % NO;
+  if (r < kRowsPerWave && lane < NO + DN / 8 && bt0 + r < T) {
+    float d = dl[0];
+    int e = esc[0];
+#pragma unroll
+    for (int k = 1; k < kRowsPerWave; ++k)
+      if (r == k) { d = dl[k]; e = esc[k]; }
+    const int64_t bt = bt0 + r;
+    const int64_t si = ((bt / S) * h + i) * S + bt % S;
+    if (lane < NO) {
+      delta[si] = d;
+      osc[si] = e;
+    } else {
+      qsc[si] = e;
+    }
   }
   // Largest |dO| of the workgroup's rows (lane 0's group holds dO), one value per workgroup.
   __shared__ float wmax[4];
@@ -679,12 +728,15 @@ hipError_t launch_bwd_prep(const Shape& s, const float* o, const void* q, const 
   const int64_t rows = s.T * s.h;
   const unsigned blocks = static_cast<unsigned>((rows + 3) / 4);
   if (s.bf16 && s.d_nope == 128 && s.d_rope == 64 && s.d_v == 128) {
-    const unsigned pblocks = static_cast<unsigned>((rows + 4 * kRowsPerWave - 1) / (4 * kRowsPerWave));
+    // One wavefront per kRowsPerWave tokens and head; one dO maximum per
+    // workgroup (the workspace holds (T h + 3) / 4 of them: more than enough).
+    const int64_t waves = (s.T + kRowsPerWave - 1) / kRowsPerWave * s.h;
+    const unsigned pblocks = static_cast<unsigned>((waves + 3) / 4);
     hipLaunchKernelGGL((bwd_prep_kernel<128, 64, 128>), dim3(pblocks), dim3(256), 0, st, o,
                        static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(d_o),
                        static_cast<const bf16_t*>(k_pe), delta, static_cast<half_t*>(c.q16),
                        static_cast<half_t*>(c.kpe16), static_cast<uint8_t*>(c.q8), static_cast<uint8_t*>(c.do8),
-                       c.qsc, c.osc, c.do_row_max, rows, s.h, s.S);
+                       c.qsc, c.osc, c.do_row_max, s.T, s.h, s.S);
     hipLaunchKernelGGL(do_shift_kernel, dim3(1), dim3(1024), 0, st, c.do_row_max, static_cast<int64_t>(pblocks),
                        c.do_shift);
     const int64_t n8 = rows * s.d_v / 8;

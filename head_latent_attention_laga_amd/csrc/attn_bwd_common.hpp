@@ -1,5 +1,5 @@
 // Pieces shared by the two attention-backward kernels (dK/dV and dq): the
-// argument block, LDS tile padding and staging helpers.
+// argument block and staging helpers.
 #pragma once
 
 #include <type_traits>
@@ -24,13 +24,6 @@ struct BwdArgs {
   const int* do_shift;
   int64_t S, plane_k, plane_v, plane_dkv; int B, h; float scale_log2, scale;
 };
-
-// Row padding (elements) of LDS tiles.  `row`: tiles read only with 16-byte
-// row fragments.  `both`: tiles also read with transposing reads; a pitch of
-// 8 (mod 16) dwords keeps the eight rows of a 16-byte read and the four rows
-// of a transposing read on distinct banks.
-template <class M> struct TilePad { static constexpr int row = 8, both = 16; };
-template <> struct TilePad<MmaF32> { static constexpr int row = 4, both = 4; };  // keeps 16-byte row alignment
 
 // 16-byte chunk of `E` converted from a 16-byte chunk of the input type.
 template <class E, class InT>
