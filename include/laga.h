@@ -14,7 +14,9 @@
  * Conventions shared by every entry point
  *  - All arrays are dense, row-major, contiguous device memory owned by the
  *    caller.  The library allocates nothing, keeps no state between calls and
- *    is reentrant; calls on one stream are ordered by that stream.
+ *    is reentrant; calls on one stream are ordered by that stream.  The one
+ *    exception is laga_attn_bwd_noalloc, whose workspace is a static device
+ *    array of the library, shared by all its calls on a GPU (see there).
  *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
  *    enqueued asynchronously; device faults surface at the caller's next
  *    synchronisation.  Argument checks run on the host before any launch and
