@@ -25,8 +25,11 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
           f"-I{INCLUDE}"] + DEVICE_FLAGS
-# Per-file extra compiler flags (none at present).
-FILE_FLAGS: dict = {}
+# Per-file extra compiler flags.  absorbed.hip: every matrix-core result in
+# vector registers (the latent attention's output accumulators are rescaled by
+# vector instructions; held in accumulator registers they were copied out on
+# every key block).
+FILE_FLAGS: dict = {"absorbed.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:

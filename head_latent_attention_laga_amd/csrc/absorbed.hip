@@ -22,7 +22,11 @@
 // reads of the same tile: the score and value sides share one copy of L in
 // LDS).  The two partial score tiles meet through LDS: each lane adds its
 // partner's same-lane values, so both wavefronts hold bitwise the same scores
-// and the same softmax.  One wavefront per SIMD.
+// and the same softmax.  One wavefront per SIMD.  This file is compiled with
+// every matrix-core result in vector registers (a build flag): the output
+// accumulators are rescaled by vector instructions whenever the running
+// maximum grows, and held in accumulator registers they were copied out and
+// back around that rare branch on every key block.
 //
 // Key blocks move HBM -> LDS with buffer loads straight into LDS (16 bytes per
 // lane, no staging registers) into two separate shared arrays, the next block
@@ -75,21 +79,38 @@ struct AbsArgs {
 __device__ __forceinline__ int swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 
 struct Abs {
+  // Source offsets (bytes into the key block) of the lane's 16-byte chunk in
+  // each pass: physical chunk P = (p NW + wavefront) 64 + lane of the tile
+  // holds row P / CPR, logical chunk (P mod CPR) ^ swz(row).  They do not
+  // depend on the block, so they are formed once, before the key loop, and
+  // kept: each is pinned to an accumulator register where it is formed,
+  // which stops the compiler from recomputing them (a division by CPR and
+  // the swizzle, per pass) on every block.
+  struct Src { uint32_t off[PASSES]; };
+
+  __device__ static Src src_offsets() {
+    const int lane = threadIdx.x % kWave;
+    const int wv = static_cast<int>(threadIdx.x) / kWave;
+    Src o;
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int P = (p * NW + wv) * kWave + lane;
+      const int r = P / CPR, pc = P % CPR;
+      o.off[p] = static_cast<uint32_t>(r * PITCH + (pc ^ swz(r)) * 16);
+      asm volatile("" : "+a"(o.off[p]));
+    }
+    return o;
+  }
+
   // Issue one key block (rows key0 ..) into `buf`; rows past the sequence read as zero.
-  __device__ static void issue(const AbsArgs& a, int b, int64_t key0, char* buf) {
+  __device__ static void issue(const AbsArgs& a, int b, int64_t key0, char* buf, const Src& so) {
     const int64_t left = a.S - key0;
     const int nk = static_cast<int>(left < BN ? (left > 0 ? left : 0) : BN);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<half_t*>(a.kx + (static_cast<int64_t>(b) * a.S + key0) * DQ), 0, nk * PITCH, 0x00020000);
-    const int lane = threadIdx.x % kWave;
     const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int w = p * NW + wv;
-      const int P = w * kWave + lane;  // physical chunk of the tile
-      const int r = P / CPR, pc = P % CPR;
-      load_lds16(rs, buf + w * 1024, r * PITCH + (pc ^ swz(r)) * 16);
-    }
+    for (int p = 0; p < PASSES; ++p) load_lds16(rs, buf + (p * NW + wv) * 1024, so.off[p]);
   }
 
   struct State {
@@ -184,12 +205,11 @@ struct Abs {
   // Blocks are computed by both wavefronts of a pair or by neither (skipped
   // when they lie wholly after the pair's last query token), but every
   // wavefront reaches both barriers of every step.
-  template <bool P>
   __device__ static void step(const AbsArgs& a, int kb, int b, int64_t t_lo, int64_t t_hi, int64_t tq, int hw,
-                              const char* cur, char* nxt, float* xch, const Offs& of, State& st) {
+                              const char* cur, char* nxt, float* xch, const Offs& of, const Src& so, State& st) {
     dma_barrier();  // block kb has landed in `cur`; `nxt` (block kb-1) and the exchange area are free
     const int64_t key0 = static_cast<int64_t>(kb) * BN;
-    issue(a, b, key0 + BN, nxt);  // on every step, so every path has the same loads in flight
+    issue(a, b, key0 + BN, nxt, so);  // on every step, so every path has the same loads in flight
     if (key0 <= t_hi) {
       compute(a, cur, xch, key0, t_lo, tq, hw, of, st);
     } else {
@@ -218,7 +238,8 @@ struct Abs {
     const int64_t tile_hi = (last < rows ? last : rows - 1) / a.h;
     const int nkb = static_cast<int>(tile_hi / BN) + 1;
 
-    issue(a, b, 0, lds0);
+    const Src so = src_offsets();
+    issue(a, b, 0, lds0, so);
 
     State st;
     {
@@ -256,10 +277,10 @@ struct Abs {
     // Unrolled by two so that each step names its buffers statically.
     int kb = 0;
     for (; kb + 1 < nkb; kb += 2) {
-      step<false>(a, kb, b, t_lo, t_hi, tq, hw, lds0, lds1, xch, of, st);
-      step<true>(a, kb + 1, b, t_lo, t_hi, tq, hw, lds1, lds0, xch, of, st);
+      step(a, kb, b, t_lo, t_hi, tq, hw, lds0, lds1, xch, of, so, st);
+      step(a, kb + 1, b, t_lo, t_hi, tq, hw, lds1, lds0, xch, of, so, st);
     }
-    if (kb < nkb) step<false>(a, kb, b, t_lo, t_hi, tq, hw, lds0, lds1, xch, of, st);
+    if (kb < nkb) step(a, kb, b, t_lo, t_hi, tq, hw, lds0, lds1, xch, of, so, st);
     // The last step's prefetch must land before the wave ends: the
     // workgroup's LDS is handed to another workgroup afterwards.
     __builtin_amdgcn_s_waitcnt(0);
