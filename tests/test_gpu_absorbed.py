@@ -42,7 +42,8 @@ def _compare(d: li.Dims, inp, out, rows):
 
 
 @pytest.mark.parametrize("B,S,n_h,P,r", [(1, 300, 16, 8, 3), (2, 130, 64, 8, 7), (1, 1, 16, 8, 0),
-                                         (1, 64, 128, 16, 2), (1, 97, 128, 1, 0), (1, 1000, 16, 8, 2)])
+                                         (1, 64, 128, 16, 2), (1, 97, 128, 1, 0), (1, 1000, 16, 8, 2),
+                                         (1, 150, 15, 5, 2), (2, 97, 5, 1, 0)])
 def test_absorbed_forward_shapes(B, S, n_h, P, r):
     d = li.Dims(B=B, S=S, n_h=n_h, sp_size=P, sp_rank=r, d_kv=512, d_nope=128, d_rope=64, d_v=128,
                 dtype=li.BF16)
@@ -113,7 +114,8 @@ def _b2_step(d: li.Dims, seed: int, workspace: str = "default"):
 @pytest.mark.parametrize("B,S,n_h,P,r,ws", [(1, 300, 16, 8, 3, "default"), (2, 130, 64, 8, 7, "default"),
                                             (1, 1, 16, 8, 0, "default"), (1, 257, 128, 32, 5, "default"),
                                             (1, 1000, 16, 8, 2, "default"), (1, 1000, 16, 8, 2, "min"),
-                                            (2, 300, 16, 8, 5, "min"), (1, 1000, 16, 8, 4, "mid")])
+                                            (2, 300, 16, 8, 5, "min"), (1, 1000, 16, 8, 4, "mid"),
+                                            (1, 150, 15, 5, 2, "default"), (2, 97, 5, 1, 0, "min")])
 def test_absorbed_backward_shapes(B, S, n_h, P, r, ws):
     """Every gradient against the oracle's B2 backward (itself equal to the explicit
     backward).  ws: the workspace passed; "min" runs 32-token chunks of query rows

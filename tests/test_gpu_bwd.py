@@ -45,7 +45,8 @@ def _run(d: li.Dims, seed: int):
 @pytest.mark.parametrize("B,S,n_h,P,r,dtype", [
     (1, 256, 2, 1, 0, li.F32), (2, 77, 4, 2, 1, li.F32), (1, 1, 2, 1, 0, li.F32), (1, 200, 16, 8, 7, li.F32),
     (1, 300, 16, 8, 3, li.BF16), (2, 130, 64, 8, 7, li.BF16), (1, 1, 16, 8, 0, li.BF16),
-    (1, 257, 128, 32, 5, li.BF16), (1, 1000, 16, 8, 2, li.BF16)])
+    (1, 257, 128, 32, 5, li.BF16), (1, 1000, 16, 8, 2, li.BF16), (1, 150, 15, 5, 2, li.BF16),
+    (2, 97, 5, 1, 0, li.BF16)])
 def test_backward_full_compare(B, S, n_h, P, r, dtype):
     d = _dims(B, S, n_h, P, r, dtype)
     announce(f"backward full compare dims={d}")

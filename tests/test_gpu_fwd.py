@@ -75,7 +75,8 @@ def test_f32_shapes(B, S, n_h, P, r):
 
 @pytest.mark.parametrize("precision", [FP16, SPLIT])
 @pytest.mark.parametrize("B,S,n_h,P,r", [(1, 300, 16, 8, 3), (2, 130, 64, 8, 7), (1, 1, 16, 8, 0),
-                                         (1, 64, 128, 16, 2), (1, 1000, 16, 8, 2)])
+                                         (1, 64, 128, 16, 2), (1, 1000, 16, 8, 2), (1, 150, 15, 5, 2),
+                                         (2, 97, 5, 1, 0)])
 def test_bf16_shapes(precision, B, S, n_h, P, r):
     _full_forward_check(_dims(B, S, n_h, P, r, li.BF16), precision, seed=S + P)
 
