@@ -158,16 +158,28 @@ struct Dq {
 #pragma unroll
       for (int r = 0; r < 16; ++r) { sc[u][r] = 0.f; dp[u][r] = 0.f; }
     // S^T and dP^T: one chain of row reads, kAhead ahead of the products,
-    // each read feeding every query group.
+    // each K / V read feeding every query group; the dP^T steps also read
+    // the groups' dO fragments (B operands, the wavefront's LDS area) ahead.
     const E* krow = Kr + (k0 + col) * LKR + hf * M::KPL;
     const E* vrow = Vr + (k0 + col) * LV + hf * M::KPL;
-    pipelined<KS_QK + KS_V, kAhead, F>(
-        [&](int i) { return i < KS_QK ? lds_frag<M>(krow + i * M::K) : lds_frag<M>(vrow + (i - KS_QK) * M::K); },
-        [&](int i, const F& f) {
+    struct Ops { F a; F o[QH]; };
+    pipelined<KS_QK + KS_V, kAhead, Ops>(
+        [&](int i) {
+          Ops r;
+          if (i < KS_QK) {
+            r.a = lds_frag<M>(krow + i * M::K);
+          } else {
+            r.a = lds_frag<M>(vrow + (i - KS_QK) * M::K);
+#pragma unroll
+            for (int u = 0; u < QH; ++u) r.o[u] = lds_frag<M>(st_.dorow + 32 * u * LDO + (i - KS_QK) * M::K);
+          }
+          return r;
+        },
+        [&](int i, const Ops& f) {
 #pragma unroll
           for (int u = 0; u < QH; ++u) {
-            if (i < KS_QK) sc[u] = M::mma(f, st_.qf[u][i], sc[u]);
-            else dp[u] = M::mma(f, lds_frag<M>(st_.dorow + 32 * u * LDO + (i - KS_QK) * M::K), dp[u]);
+            if (i < KS_QK) sc[u] = M::mma(f.a, st_.qf[u][i], sc[u]);
+            else dp[u] = M::mma(f.a, f.o[u], dp[u]);
           }
         });
     // P and dS = P (dP - delta) in the key order of the accumulator
