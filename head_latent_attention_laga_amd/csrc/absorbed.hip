@@ -133,12 +133,14 @@ struct Abs {
     f32x16 sc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[r] = 0.f;
-#pragma unroll
-    for (int j = 0; j < KSH; ++j) {
-      const int s = hw * KSH + j;  // score step over the 576 dims
-      const half8 kf = lds_at<half8>(buf, (of.rb ^ (32u * (s % 4))) + 128 * (s / 4));
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, st.qf[j], sc, 0, 0, 0);
-    }
+    // The key fragments read kAhead products ahead of their use.
+    constexpr int kAhead = 3;
+    pipelined<KSH, kAhead, half8>(
+        [&](int j) {
+          const int s = hw * KSH + j;  // score step over the 576 dims
+          return lds_at<half8>(buf, (of.rb ^ (32u * (s % 4))) + 128 * (s / 4));
+        },
+        [&](int j, const half8& kf) { sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, st.qf[j], sc, 0, 0, 0); });
     // Partial scores meet the partner's: same lane, same (key, query) elements.
     f32x4* mine = reinterpret_cast<f32x4*>(xch) + (threadIdx.x / kWave) * kWave * 4 + lane;
     const f32x4* theirs = reinterpret_cast<const f32x4*>(xch) + ((threadIdx.x / kWave) ^ 1) * kWave * 4 + lane;
