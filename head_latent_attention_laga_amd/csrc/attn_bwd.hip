@@ -264,6 +264,14 @@ struct Dkdv {
     const E* Qr = reinterpret_cast<const E*>(buf);
     const E* Or = reinterpret_cast<const E*>(buf + QR_B);
     const float* st = reinterpret_cast<const float*>(buf + OFF_ST);
+    // The rows' lse and delta, read before the products: issued next to their
+    // use they were waited for in the middle of the dP chain.
+    f32x4 l4[4], d4[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      l4[g] = *reinterpret_cast<const f32x4*>(st + 8 * g + 4 * hf);
+      d4[g] = *reinterpret_cast<const f32x4*>(st + BQ + 8 * g + 4 * hf);
+    }
 
     // S[q, key], dP[q, key]: rows = queries 8g + 4hf + i, column = key.  The
     // chains run one after the other so that the vector work on each result
@@ -344,11 +352,10 @@ struct Dkdv {
     E ph[STEPS][NS][M::KPL];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(st + 8 * g + 4 * hf);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * g + i;
-        float p = __builtin_amdgcn_exp2f(fmaf(sc[r], a.scale_log2, -l4[i]));
+        float p = __builtin_amdgcn_exp2f(fmaf(sc[r], a.scale_log2, -l4[g][i]));
         if constexpr (MASK) {
           const int qi = 8 * g + 4 * hf + i;
           if (rel > qi || qi >= nq) p = 0.f;
@@ -374,9 +381,8 @@ struct Dkdv {
     float dsv[16];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(st + BQ + 8 * g + 4 * hf);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dsv[4 * g + i] = pv[4 * g + i] * (dp[4 * g + i] - d4[i]);
+      for (int i = 0; i < 4; ++i) dsv[4 * g + i] = pv[4 * g + i] * (dp[4 * g + i] - d4[g][i]);
     }
     split16(dsv, dh);
     // dK^T[d, key] += q^T dS   (k = queries).  The rope rows (d >= DN) give
