@@ -147,12 +147,13 @@ struct Abs {
 #pragma unroll
     for (int g = 0; g < 4; ++g) mine[g * kWave] = f32x4{sc[4 * g], sc[4 * g + 1], sc[4 * g + 2], sc[4 * g + 3]};
     lds_barrier();
+    f32x4 o4[4];  // the partner's values, all four reads in flight together
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x4 o4 = theirs[g * kWave];
+    for (int g = 0; g < 4; ++g) o4[g] = theirs[g * kWave];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) sc[4 * g + k] += o4[k];
-    }
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) sc[4 * g + k] += o4[g][k];
     // Causal mask on blocks that reach past the pair's first query token:
     // key key0 + 8(r/4) + 4hf + r%4 is masked above the lane's token.
     if (key0 + BN - 1 > t_lo) {
@@ -184,24 +185,26 @@ struct Abs {
     }
     st.l_run += pair_sum(lsum);
 
-    // O^T += V^T P^T over the block's 32 keys for this wavefront's 256 columns.
+    // O^T += V^T P^T over the block's 32 keys for this wavefront's 256 columns,
+    // the V^T fragments (transposing reads) kAhead products ahead.
+    half8 pf[2];
 #pragma unroll
-    for (int sp = 0; sp < 2; ++sp) {
-      half8 pf;
+    for (int sp = 0; sp < 2; ++sp)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pf[j] = static_cast<half_t>(sc[sp * 8 + j]);
-#pragma unroll
-      for (int nl = 0; nl < NOH; ++nl) {
-        const int n = hw * NOH + nl;
-        const uint32_t row0 = sp * 16 * PITCH + 128 * (n >> 1);
-        const uint32_t x0 = (of.tb ^ (64u * (n & 1))) + row0;
-        const uint32_t x1 = (of.tb ^ (64u * (n & 1) + 32u)) + row0 + 8 * PITCH;
-        const s16x4 lo = ds_read_tr16(buf + x0), hi = ds_read_tr16(buf + x1);
-        typedef short s16x8 __attribute__((ext_vector_type(8)));
-        const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        st.o[nl] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, v), pf, st.o[nl], 0, 0, 0);
-      }
-    }
+      for (int j = 0; j < 8; ++j) pf[sp][j] = static_cast<half_t>(sc[sp * 8 + j]);
+    pipelined<2 * NOH, kAhead, half8>(
+        [&](int i) {
+          const int sp = i / NOH, n = hw * NOH + i % NOH;
+          const uint32_t row0 = sp * 16 * PITCH + 128 * (n >> 1);
+          const uint32_t x0 = (of.tb ^ (64u * (n & 1))) + row0;
+          const uint32_t x1 = (of.tb ^ (64u * (n & 1) + 32u)) + row0 + 8 * PITCH;
+          const s16x4 lo = ds_read_tr16(buf + x0), hi = ds_read_tr16(buf + x1);
+          typedef short s16x8 __attribute__((ext_vector_type(8)));
+          return __builtin_bit_cast(half8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        },
+        [&](int i, const half8& v) {
+          st.o[i % NOH] = __builtin_amdgcn_mfma_f32_32x32x16_f16(v, pf[i / NOH], st.o[i % NOH], 0, 0, 0);
+        });
   }
 
   // Blocks are computed by both wavefronts of a pair or by neither (skipped
