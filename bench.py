@@ -707,14 +707,21 @@ def main():
 
 
 def gpu_sclk():
-    """The GPU's current shader clock as rocm-smi reports it (None if unavailable)."""
-    import subprocess
-    try:
-        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30).stdout
-    except (OSError, subprocess.SubprocessError):
-        return None
-    lines = [ln.strip() for ln in out.splitlines() if "sclk" in ln.lower()]
-    return lines[0] if lines else None
+    """The shader clock level the driver marks as current in sysfs (None if unavailable).
+
+    Read from the file directly rather than through rocm-smi: a child process
+    started under a profiler that preloads its GPU library would initialise the
+    GPU before its own exec."""
+    import glob
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                lines = [ln.strip() for ln in f if ln.strip().endswith("*")]
+        except OSError:
+            continue
+        if lines:
+            return lines[0]
+    return None
 
 
 if __name__ == "__main__":
