@@ -248,7 +248,7 @@ def summarize_profiles(out_root: str):
     line = [ln for ln in open(os.path.join(out_root, "kt.log")) if ln.startswith('{"metric"')]
     prun = json.loads(line[-1]) if line else None
     L = [f"# Kernel trace: LAGA training step, fp16-operand forward (unfused and fused) and absorbed-form (B2) "
-         f"forward and backward, {title}", "", "Command (on the GPU box):", "", "```",
+         f"forward and backward, {title}", "", "Command (on the MI355X):", "", "```",
          PROFILE_CMD.format(opts="--kernel-trace --stats", d="kt", o="kt", args=KT_ARGS), "```", "", PROFILE_VARS, "",
          "Per launch, from the trace (`kt_kernel_trace.csv`), in us. For the step's kernels, 'timed' is the mean "
          "over the launches inside bench.py's timed region and 'bench' the HIP-event mean that the same run "
